@@ -1,0 +1,165 @@
+"""Pins of the oracle's scaled GEMM, low-rank residual and whole-layer formula.
+
+The model card "nunchaku-z-image-turbo-svdq" (section "What's stored on disk")
+gives y = scaled_mma(quant(x*smooth), qweight, ascales, wscales) * wtscale *
+wcscales + (x @ proj_down) @ proj_up^T + bias. Pins: the int64-exact form of
+the main term, a pure-Python integer brute force on tiny shapes, and the
+formula's closed-form special cases (R = 0: a plain quantised GEMM;
+qweight = 0: a pure low-rank product; lossless inputs: an exact GEMM).
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import formats as F
+from oracle import svdq as S
+
+
+def _tiny(seed=None, **over):
+    cfg = dict(workloads.TINY)
+    if seed is not None:
+        cfg["seed"] = seed
+    cfg.update(over)
+    d = workloads.make_linear(**cfg)
+    d["qweight"], d["wscales"] = S.quantize_weight(d["W"], d["wcscales"], d["wtscale"])
+    return d
+
+
+def test_main_term_fp64_equals_int64_exact():
+    d = _tiny()
+    qact, ascales = S.quantize_act(d["x"], d["smooth"])
+    main = S.main_term(qact, ascales, d["qweight"], d["wscales"])
+    exact = S.main_term_int64(qact, ascales, d["qweight"], d["wscales"])
+    assert np.abs(exact).max() < 2 ** 53
+    assert np.array_equal(main, exact.astype(np.float64) * 2.0 ** -20)
+
+
+def test_main_term_dit_int64_exact():
+    d = workloads.make_linear(M=32, K=1024, N=64, R=0, kind="dit", seed=77)
+    qw, ws = S.quantize_weight(d["W"], d["wcscales"], d["wtscale"])
+    qact, ascales = S.quantize_act(d["x"], d["smooth"])
+    main = S.main_term(qact, ascales, qw, ws)
+    exact = S.main_term_int64(qact, ascales, qw, ws)
+    assert np.array_equal(main, exact.astype(np.float64) * 2.0 ** -20)
+
+
+def test_main_term_pure_python_brute_force():
+    """Sum over k of (E2M1 * e4m3) products with Python Fractions, element by element."""
+    d = _tiny()
+    qact, ascales = S.quantize_act(d["x"], d["smooth"])
+    main = S.main_term(qact, ascales, d["qweight"], d["wscales"])
+    grid = [0, Fraction(1, 2), 1, Fraction(3, 2), 2, 3, 4, 6]
+
+    def e2m1(c):
+        return -grid[c & 7] if c & 8 else grid[c & 7]
+
+    def e4m3(b):
+        e, f = (b >> 3) & 15, b & 7
+        return Fraction(f, 512) if e == 0 else (1 + Fraction(f, 8)) * Fraction(2) ** (e - 7)
+
+    K = d["K"]
+    for m, n in [(0, 0), (5, 17), (63, 127), (31, 64), (10, 99)]:
+        acc = Fraction(0)
+        for k in range(K):
+            ab = int(qact[m, k // 2])
+            wb = int(d["qweight"][n, k // 2])
+            a = e2m1(ab & 15 if k % 2 == 0 else ab >> 4) * e4m3(int(ascales[k // 16, m]))
+            w = e2m1(wb & 15 if k % 2 == 0 else wb >> 4) * e4m3(int(d["wscales"][k // 16, n]))
+            acc += a * w
+        assert Fraction(main[m, n]) == acc
+
+
+def test_r0_is_plain_quantised_gemm():
+    d = _tiny(R=0)
+    y64, y, qact, ascales = S.linear_w4a4(d["x"], d["smooth"], d["qweight"], d["wscales"],
+                                          d["wcscales"], d["wtscale"], d["proj_down"],
+                                          d["proj_up"], d["bias"])
+    A = S.dequant(qact, ascales)
+    W = S.dequant(d["qweight"], d["wscales"])
+    alpha = F.bf16_to_f64(d["wtscale"])[0] * F.bf16_to_f64(d["wcscales"])
+    ref = torch.from_numpy(A) @ torch.from_numpy(W).T * torch.from_numpy(alpha) + \
+        torch.from_numpy(F.bf16_to_f64(d["bias"]))
+    assert np.allclose(y64, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_zero_weight_is_pure_lowrank_product():
+    d = _tiny()
+    qw0 = np.zeros_like(d["qweight"])
+    y64, y, _, _ = S.linear_w4a4(d["x"], d["smooth"], qw0, d["wscales"], d["wcscales"],
+                                 d["wtscale"], d["proj_down"], d["proj_up"], d["bias"])
+    x = torch.from_numpy(F.bf16_to_f64(d["x"]))
+    pd = torch.from_numpy(F.bf16_to_f64(d["proj_down"]))
+    pu = torch.from_numpy(F.bf16_to_f64(d["proj_up"]))
+    b = torch.from_numpy(F.bf16_to_f64(d["bias"]))
+    ref = torch.matmul(torch.matmul(x, pd), pu.T) + b
+    assert np.allclose(y64, ref.numpy(), rtol=1e-12, atol=1e-14)
+    # output rounding: the bf16 result is RNE of the float64 result
+    assert np.array_equal(y, F.f64_to_bf16(ref.numpy())) or \
+        np.mean(y != F.f64_to_bf16(ref.numpy())) < 1e-3
+
+
+def test_lossless_inputs_give_exact_gemm():
+    """smooth = 1 and x built from NVFP4 values: quantisation is lossless, so the
+    main term is x @ W_eff^T exactly."""
+    rng = np.random.default_rng(4)
+    M, K, N = 16, 128, 32
+    codes = rng.integers(0, 16, size=(M, K), dtype=np.uint8)
+    codes[:, ::16] = 7
+    sc = rng.integers(0x10, 0x60, size=(M, K // 16), dtype=np.uint8)
+    xv = F.e2m1_decode(codes) * np.repeat(F.e4m3_decode(sc), 16, axis=1)
+    x_bits = F.f64_to_bf16(xv)
+    ones = F.f64_to_bf16(np.ones(K))
+    d = workloads.make_linear(M=M, K=K, N=N, R=0, kind="tiny", seed=8)
+    qw, ws = S.quantize_weight(d["W"], d["wcscales"], d["wtscale"])
+    qact, ascales = S.quantize_act(x_bits, ones)
+    main = S.main_term(qact, ascales, qw, ws)
+    assert np.array_equal(main, xv @ S.dequant(qw, ws).T)
+
+
+def test_epilogue_scales_only_the_main_term():
+    d = _tiny()
+    qact, ascales = S.quantize_act(d["x"], d["smooth"])
+    main = S.main_term(qact, ascales, d["qweight"], d["wscales"])
+    lr = S.lowrank(d["x"], d["proj_down"], d["proj_up"])
+    wc2 = F.f64_to_bf16(2 * F.bf16_to_f64(d["wcscales"]))
+    y1 = S.epilogue(main, d["wcscales"], d["wtscale"], lr, None)
+    y2 = S.epilogue(main, wc2, d["wtscale"], lr, None)
+    assert np.allclose(y2 - y1, main * F.bf16_to_f64(d["wcscales"])[None, :], rtol=1e-12, atol=1e-15)
+
+
+def test_lowrank_uses_raw_x():
+    d = _tiny()
+    x = F.bf16_to_f64(d["x"])
+    ref = (x @ F.bf16_to_f64(d["proj_down"])) @ F.bf16_to_f64(d["proj_up"]).T
+    assert np.allclose(S.lowrank(d["x"], d["proj_down"], d["proj_up"]), ref, rtol=1e-13, atol=1e-16)
+
+
+def test_w4a4_is_close_to_unquantised_product_when_self_consistent():
+    """Sanity of the whole formula (not a parity gate): for W = W_q + proj_up proj_down^T
+    quantised faithfully, y approximates x @ W^T."""
+    rng = np.random.default_rng(12)
+    M, K, N, R = 32, 256, 64, 16
+    x = rng.standard_normal((M, K))
+    x_bits = F.f64_to_bf16(x)
+    pd = F.f64_to_bf16(rng.standard_normal((K, R)) * 0.02)
+    pu = F.f64_to_bf16(rng.standard_normal((N, R)) * 0.02)
+    Wr = rng.standard_normal((N, K)) * 0.02
+    ones = F.f64_to_bf16(np.ones(K))
+    wc = F.f64_to_bf16(np.abs(Wr).max(axis=1) / (6 * 448))
+    wt = F.f64_to_bf16(np.ones(1))
+    qw, ws = S.quantize_weight(Wr, wc, wt)
+    y64, _, _, _ = S.linear_w4a4(x_bits, ones, qw, ws, wc, wt, pd, pu, None)
+    W_full = Wr + F.bf16_to_f64(pu) @ F.bf16_to_f64(pd).T
+    ref = F.bf16_to_f64(x_bits) @ W_full.T
+    cos = np.sum(y64 * ref) / np.linalg.norm(y64) / np.linalg.norm(ref)
+    assert cos > 0.98
+
+
+def test_normwise_metric():
+    a = np.array([[3.0, 4.0]])
+    assert S.normwise_rel_err(a, a) == 0.0
+    assert S.normwise_rel_err(np.array([[3.0, 0.0]]), a) == pytest.approx(4.0 / 5.0)
