@@ -1,0 +1,404 @@
+// C ABI of the library (declared in include/svdq.h): argument validation on
+// the host, workspace layout, and the launch sequence of each entry point.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kernels.h"
+#include "svdq.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SVDQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;
+};
+Range range(const char* name, const void* p, size_t bytes) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  return Range{name, b, b + bytes};
+}
+bool overlaps(const Range& a, const Range& b) {
+  return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// every output against every input and every other output
+int check_alias(const Range* in, int n_in, const Range* out, int n_out) {
+  for (int o = 0; o < n_out; ++o) {
+    if (out[o].lo == 0) continue;
+    for (int i = 0; i < n_in; ++i)
+      if (in[i].lo != 0 && overlaps(out[o], in[i]))
+        return fail(SVDQ_ERR_ALIAS, "output %s overlaps input %s", out[o].name, in[i].name);
+    for (int p = o + 1; p < n_out; ++p)
+      if (out[p].lo != 0 && overlaps(out[o], out[p]))
+        return fail(SVDQ_ERR_ALIAS, "output %s overlaps output %s", out[o].name, out[p].name);
+  }
+  return SVDQ_OK;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int check_mk(int64_t M, int64_t K, int64_t R) {
+  if (M < 0) return fail(SVDQ_ERR_SHAPE, "M = %lld is negative", (long long)M);
+  if (K <= 0 || K % 16 != 0)
+    return fail(SVDQ_ERR_SHAPE, "K = %lld must be a positive multiple of 16", (long long)K);
+  if (R < 0) return fail(SVDQ_ERR_SHAPE, "R = %lld is negative", (long long)R);
+  if (R % 16 != 0)
+    return fail(SVDQ_ERR_UNSUPPORTED, "R = %lld: the kernels need R to be a multiple of 16", (long long)R);
+  if (M > kMaxDim || K > kMaxDim || R > kMaxDim)
+    return fail(SVDQ_ERR_UNSUPPORTED, "dimension above 2^24 (M=%lld K=%lld R=%lld)", (long long)M,
+                (long long)K, (long long)R);
+  return SVDQ_OK;
+}
+
+int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (ptrs[i] == nullptr) return fail(SVDQ_ERR_NULL, "%s is NULL", names[i]);
+  for (int i = 0; i < n; ++i)
+    if (!aligned16(ptrs[i])) return fail(SVDQ_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  return SVDQ_OK;
+}
+
+size_t quant_ws_bytes(int64_t M, int64_t K, int64_t R) {
+  return R > 0 ? svdq::lora_down_workspace_bytes(M, K, R) : 0;
+}
+
+struct LinearWs {
+  size_t qact, ascales, lora, down, total;
+};
+LinearWs linear_ws(int64_t M, int64_t K, int64_t R) {
+  LinearWs w;
+  w.qact = 0;
+  w.ascales = align256(w.qact + (size_t)M * (size_t)(K / 2));
+  w.lora = align256(w.ascales + (size_t)(K / 16) * (size_t)M);
+  w.down = align256(w.lora + (size_t)M * (size_t)R * 2);
+  w.total = w.down + quant_ws_bytes(M, K, R);
+  return w;
+}
+
+// enqueue a1 (+ a2): pointers already validated
+int run_quantize(const void* x, const void* smooth, int64_t M, int64_t K, const void* proj_down,
+                 int64_t R, void* qact, void* ascales, void* lora_act, void* workspace,
+                 hipStream_t s) {
+  unsigned* counters = nullptr;
+  int n_counters = 0;
+  if (R > 0 && svdq::lora_down_splits(M, K, R) > 1) {
+    counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
+                                           svdq::lora_down_counter_offset(M, K, R));
+    n_counters = svdq::lora_down_counters(M);
+  }
+  hipError_t e = svdq::launch_quant_act(static_cast<const uint16_t*>(x),
+                                        static_cast<const uint16_t*>(smooth),
+                                        static_cast<uint8_t*>(qact), static_cast<uint8_t*>(ascales),
+                                        M, K, counters, n_counters, s);
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
+  if (R > 0) {
+    e = svdq::launch_lora_down(static_cast<const uint16_t*>(x),
+                               static_cast<const uint16_t*>(proj_down),
+                               static_cast<uint16_t*>(lora_act), workspace, M, K, R, s);
+    if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "down-projection launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+int check_gemm_weight(int weight_layout, const void* wscales) {
+  if (weight_layout != SVDQ_WEIGHT_CANONICAL && weight_layout != SVDQ_WEIGHT_PACKED)
+    return fail(SVDQ_ERR_INVALID, "weight_layout %d is not a known layout", weight_layout);
+  if (weight_layout == SVDQ_WEIGHT_PACKED && wscales != nullptr)
+    return fail(SVDQ_ERR_INVALID, "wscales must be NULL with the packed layout (the buffer holds them)");
+  if (weight_layout == SVDQ_WEIGHT_CANONICAL && wscales == nullptr)
+    return fail(SVDQ_ERR_NULL, "wscales is NULL");
+  return SVDQ_OK;
+}
+
+size_t weight_bytes(int weight_layout, int64_t N, int64_t K) {
+  return weight_layout == SVDQ_WEIGHT_PACKED ? svdq::packed_weight_bytes(N, K)
+                                             : (size_t)N * (size_t)(K / 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+int svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
+
+const char* svdq_status_string(int status) {
+  switch (status) {
+    case SVDQ_OK: return "ok";
+    case SVDQ_ERR_NULL: return "null pointer";
+    case SVDQ_ERR_SHAPE: return "invalid shape";
+    case SVDQ_ERR_UNSUPPORTED: return "unsupported by these kernels";
+    case SVDQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SVDQ_ERR_WORKSPACE: return "workspace too small";
+    case SVDQ_ERR_ALIAS: return "output overlaps another buffer";
+    case SVDQ_ERR_HIP: return "HIP error";
+    case SVDQ_ERR_INVALID: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* svdq_last_error(void) { return g_last_error.c_str(); }
+
+size_t svdq_quantize_act_workspace_bytes(int64_t M, int64_t K, int64_t R) {
+  if (M <= 0 || K <= 0 || R <= 0) return 0;
+  return quant_ws_bytes(M, K, R);
+}
+
+int svdq_quantize_act(const void* x, const void* smooth, int64_t M, int64_t K,
+                      const void* proj_down, int64_t R, void* qact, void* ascales,
+                      void* lora_act, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_mk(M, K, R);
+  if (st) return st;
+  if (M == 0) return ok();
+  {
+    const char* names[] = {"x", "smooth", "qact", "ascales"};
+    const void* ptrs[] = {x, smooth, qact, ascales};
+    if ((st = check_ptrs(names, ptrs, 4))) return st;
+  }
+  const size_t need = quant_ws_bytes(M, K, R);
+  if (R > 0) {
+    const char* names[] = {"proj_down", "lora_act"};
+    const void* ptrs[] = {proj_down, lora_act};
+    if ((st = check_ptrs(names, ptrs, 2))) return st;
+  }
+  if (need > 0) {
+    if (workspace == nullptr) return fail(SVDQ_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned16(workspace)) return fail(SVDQ_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(SVDQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  const Range in[] = {range("x", x, (size_t)M * K * 2), range("smooth", smooth, (size_t)K * 2),
+                      range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2)};
+  const Range out[] = {range("qact", qact, (size_t)M * (K / 2)),
+                       range("ascales", ascales, (size_t)(K / 16) * M),
+                       range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
+                       range("workspace", need > 0 ? workspace : nullptr, need)};
+  if ((st = check_alias(in, 3, out, 4))) return st;
+  return run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora_act, workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
+size_t svdq_repack_weight_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % 16 != 0) return 0;
+  return svdq::packed_weight_bytes(N, K);
+}
+
+static int check_nk(int64_t N, int64_t K) {
+  if (N < 0) return fail(SVDQ_ERR_SHAPE, "N = %lld is negative", (long long)N);
+  if (K <= 0 || K % 16 != 0)
+    return fail(SVDQ_ERR_SHAPE, "K = %lld must be a positive multiple of 16", (long long)K);
+  if (N > kMaxDim || K > kMaxDim)
+    return fail(SVDQ_ERR_UNSUPPORTED, "dimension above 2^24 (N=%lld K=%lld)", (long long)N, (long long)K);
+  return SVDQ_OK;
+}
+
+int svdq_repack_weight(const void* qweight, const void* wscales, int64_t N, int64_t K,
+                       void* packed, size_t packed_bytes, void* stream) {
+  int st = check_nk(N, K);
+  if (st) return st;
+  if (N == 0) return ok();
+  const char* names[] = {"qweight", "wscales", "packed"};
+  const void* ptrs[] = {qweight, wscales, packed};
+  if ((st = check_ptrs(names, ptrs, 3))) return st;
+  const size_t need = svdq::packed_weight_bytes(N, K);
+  if (packed_bytes < need)
+    return fail(SVDQ_ERR_WORKSPACE, "packed buffer has %zu bytes, %zu needed", packed_bytes, need);
+  const Range in[] = {range("qweight", qweight, (size_t)N * (K / 2)),
+                      range("wscales", wscales, (size_t)(K / 16) * N)};
+  const Range out[] = {range("packed", packed, need)};
+  if ((st = check_alias(in, 2, out, 1))) return st;
+  hipError_t e = svdq::launch_repack(static_cast<const uint8_t*>(qweight),
+                                     static_cast<const uint8_t*>(wscales),
+                                     static_cast<uint8_t*>(packed), N, K,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "repack launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int svdq_unpack_weight(const void* packed, size_t packed_bytes, int64_t N, int64_t K,
+                       void* qweight_out, void* wscales_out, void* stream) {
+  int st = check_nk(N, K);
+  if (st) return st;
+  if (N == 0) return ok();
+  const char* names[] = {"packed", "qweight_out", "wscales_out"};
+  const void* ptrs[] = {packed, qweight_out, wscales_out};
+  if ((st = check_ptrs(names, ptrs, 3))) return st;
+  const size_t need = svdq::packed_weight_bytes(N, K);
+  if (packed_bytes < need)
+    return fail(SVDQ_ERR_WORKSPACE, "packed buffer has %zu bytes, %zu needed", packed_bytes, need);
+  const Range in[] = {range("packed", packed, need)};
+  const Range out[] = {range("qweight_out", qweight_out, (size_t)N * (K / 2)),
+                       range("wscales_out", wscales_out, (size_t)(K / 16) * N)};
+  if ((st = check_alias(in, 1, out, 2))) return st;
+  hipError_t e = svdq::launch_unpack(static_cast<const uint8_t*>(packed),
+                                     static_cast<uint8_t*>(qweight_out),
+                                     static_cast<uint8_t*>(wscales_out), N, K,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "unpack launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static int validate_gemm(const void* qact, const void* ascales, const void* lora_act,
+                         const void* weight, const void* wscales, int weight_layout,
+                         const void* wcscales, const void* wtscale, const void* proj_up,
+                         const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                         const void* y, bool check_act) {
+  int st;
+  if ((st = check_gemm_weight(weight_layout, wscales))) return st;
+  {
+    const char* names[] = {"weight", "wcscales", "wtscale", "y"};
+    const void* ptrs[] = {weight, wcscales, wtscale, y};
+    if ((st = check_ptrs(names, ptrs, 4))) return st;
+  }
+  if (check_act) {
+    const char* names[] = {"qact", "ascales"};
+    const void* ptrs[] = {qact, ascales};
+    if ((st = check_ptrs(names, ptrs, 2))) return st;
+  }
+  if (weight_layout == SVDQ_WEIGHT_CANONICAL && !aligned16(wscales))
+    return fail(SVDQ_ERR_ALIGN, "wscales is not 16-byte aligned");
+  if (R > 0) {
+    if (check_act) {
+      const char* names[] = {"lora_act"};
+      const void* ptrs[] = {lora_act};
+      if ((st = check_ptrs(names, ptrs, 1))) return st;
+    }
+    const char* names[] = {"proj_up"};
+    const void* ptrs[] = {proj_up};
+    if ((st = check_ptrs(names, ptrs, 1))) return st;
+  }
+  if (bias != nullptr && !aligned16(bias)) return fail(SVDQ_ERR_ALIGN, "bias is not 16-byte aligned");
+  return SVDQ_OK;
+}
+
+int svdq_gemm_w4a4(const void* qact, const void* ascales, const void* lora_act,
+                   const void* weight, const void* wscales, int weight_layout,
+                   const void* wcscales, const void* wtscale, const void* proj_up,
+                   const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y,
+                   void* stream) {
+  int st = check_mk(M, K, R);
+  if (st) return st;
+  if ((st = check_nk(N, K))) return st;
+  if (M == 0 || N == 0) return ok();
+  if ((st = validate_gemm(qact, ascales, lora_act, weight, wscales, weight_layout, wcscales, wtscale,
+                          proj_up, bias, M, N, K, R, y, true)))
+    return st;
+  const Range in[] = {range("qact", qact, (size_t)M * (K / 2)),
+                      range("ascales", ascales, (size_t)(K / 16) * M),
+                      range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
+                      range("weight", weight, weight_bytes(weight_layout, N, K)),
+                      range("wscales", wscales, (size_t)(K / 16) * N),
+                      range("wcscales", wcscales, (size_t)N * 2),
+                      range("wtscale", wtscale, 2),
+                      range("proj_up", R > 0 ? proj_up : nullptr, (size_t)N * R * 2),
+                      range("bias", bias, (size_t)N * 2)};
+  const Range out[] = {range("y", y, (size_t)M * N * 2)};
+  if ((st = check_alias(in, 9, out, 1))) return st;
+  svdq::GemmArgs a;
+  a.qact = static_cast<const uint8_t*>(qact);
+  a.ascales = static_cast<const uint8_t*>(ascales);
+  a.lora_act = static_cast<const uint16_t*>(lora_act);
+  a.weight = static_cast<const uint8_t*>(weight);
+  a.wscales = static_cast<const uint8_t*>(wscales);
+  a.wcscales = static_cast<const uint16_t*>(wcscales);
+  a.wtscale = static_cast<const uint16_t*>(wtscale);
+  a.proj_up = static_cast<const uint16_t*>(proj_up);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.y = static_cast<uint16_t*>(y);
+  a.M = M; a.N = N; a.K = K; a.R = R;
+  a.packed = weight_layout == SVDQ_WEIGHT_PACKED;
+  hipError_t e = svdq::launch_gemm_w4a4(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t svdq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t R) {
+  (void)N;
+  if (M <= 0 || K <= 0 || K % 16 != 0 || R < 0) return 0;
+  return linear_ws(M, K, R).total;
+}
+
+int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, const void* wscales,
+                     int weight_layout, const void* wcscales, const void* wtscale,
+                     const void* proj_down, const void* proj_up, const void* bias, int64_t M,
+                     int64_t N, int64_t K, int64_t R, void* y, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_mk(M, K, R);
+  if (st) return st;
+  if ((st = check_nk(N, K))) return st;
+  if (M == 0 || N == 0) return ok();
+  {
+    const char* names[] = {"x", "smooth", "workspace"};
+    const void* ptrs[] = {x, smooth, workspace};
+    if ((st = check_ptrs(names, ptrs, 3))) return st;
+  }
+  if (R > 0) {
+    const char* names[] = {"proj_down"};
+    const void* ptrs[] = {proj_down};
+    if ((st = check_ptrs(names, ptrs, 1))) return st;
+  }
+  if ((st = validate_gemm(nullptr, nullptr, nullptr, weight, wscales, weight_layout, wcscales,
+                          wtscale, proj_up, bias, M, N, K, R, y, false)))
+    return st;
+  const LinearWs ws = linear_ws(M, K, R);
+  if (workspace_bytes < ws.total)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws.total);
+  const Range in[] = {range("x", x, (size_t)M * K * 2),
+                      range("smooth", smooth, (size_t)K * 2),
+                      range("weight", weight, weight_bytes(weight_layout, N, K)),
+                      range("wscales", wscales, (size_t)(K / 16) * N),
+                      range("wcscales", wcscales, (size_t)N * 2),
+                      range("wtscale", wtscale, 2),
+                      range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2),
+                      range("proj_up", R > 0 ? proj_up : nullptr, (size_t)N * R * 2),
+                      range("bias", bias, (size_t)N * 2)};
+  const Range out[] = {range("y", y, (size_t)M * N * 2), range("workspace", workspace, ws.total)};
+  if ((st = check_alias(in, 9, out, 2))) return st;
+
+  char* w = static_cast<char*>(workspace);
+  void* qact = w + ws.qact;
+  void* ascales = w + ws.ascales;
+  void* lora = R > 0 ? (void*)(w + ws.lora) : nullptr;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora, w + ws.down, s)))
+    return st;
+  svdq::GemmArgs a;
+  a.qact = static_cast<const uint8_t*>(qact);
+  a.ascales = static_cast<const uint8_t*>(ascales);
+  a.lora_act = static_cast<const uint16_t*>(lora);
+  a.weight = static_cast<const uint8_t*>(weight);
+  a.wscales = static_cast<const uint8_t*>(wscales);
+  a.wcscales = static_cast<const uint16_t*>(wcscales);
+  a.wtscale = static_cast<const uint16_t*>(wtscale);
+  a.proj_up = static_cast<const uint16_t*>(proj_up);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.y = static_cast<uint16_t*>(y);
+  a.M = M; a.N = N; a.K = K; a.R = R;
+  a.packed = weight_layout == SVDQ_WEIGHT_PACKED;
+  hipError_t e = svdq::launch_gemm_w4a4(a, s);
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Device-side helpers shared by the library's gfx950 kernels.
+//
+// NVFP4 = E2M1 codes with one float8_e4m3fn scale per 16 consecutive K
+// elements (model card "nunchaku-z-image-turbo-svdq", header). The helpers
+// below use gfx950 conversion instructions whose behaviour this library
+// relies on (each checked exhaustively against exact arithmetic on the device):
+//  * v_cvt_f32_fp8 decodes OCP e4m3fn exactly (all 256 codes, any byte select);
+//  * v_cvt_pk_fp8_f32 rounds to nearest even but returns NaN above 464, so
+//    inputs are clamped to 448 first (saturating encode);
+//  * v_cvt_scalef32_pk_fp4_f32 with scale 1.0 is round-to-nearest-even onto
+//    the E2M1 grid, saturating at 6, keeping the sign of zero; its scale
+//    operand only contributes its power-of-two exponent;
+//  * v_cvt_scalef32_pk_f16_fp4 with scale 1.0 decodes E2M1 exactly; an E2M1
+//    value times any e4m3 value has at most 6 significant bits and lies in
+//    [2^-10, 2688], so one f16 multiply by the decoded scale is exact.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svdq {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// e4m3fn byte (in the low byte of `b`) -> fp32, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)b, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)b, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)b, 3);
+  }
+}
+
+// s >= 0 -> e4m3fn code, round to nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float s) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false) & 0xFFu;
+}
+
+// Dequantise one dword of 8 E2M1 codes (low nibble first = lower k) times the
+// block scale `s` (an exactly representable f16) into 8 f16 values, exactly.
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t codes, _Float16 s) {
+  const f16x2 ss = {s, s};
+  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
+  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
+  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
+  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
+  f16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ u32x4 zero4() { u32x4 z = {0u, 0u, 0u, 0u}; return z; }
+
+}  // namespace svdq

@@ -1,0 +1,133 @@
+// Activation quantisation quant(x * smooth) for the SVDQuant W4A4 layer
+// (model card "nunchaku-z-image-turbo-svdq", section "What's stored on disk":
+// the activation operand of scaled_mma, with per-16-K e4m3 block scales).
+//
+// Per row m and 16-block b: v = x * smooth (fp32, exact for bf16 x bf16),
+// s = max|v| / 6 -> e4m3 (nearest even, saturating at 448) = ascales[b, m],
+// codes = E2M1 nearest even of v / s_d (saturating, sign kept), packed two per
+// byte with the even k in the low nibble.
+//
+// Exactness of the code decision without a division per element: v has at
+// most 16 significant bits and s_d at most 4, so v / s_d is either exactly an
+// E2M1 rounding midpoint (at most 5 significant bits) or at least 2^-16
+// (relative) away from every midpoint. q = v * RN(1/s_d) is within 2 units in
+// the last place of v / s_d. Rounding q to 21 significant bits (adding 4 to
+// its bit pattern and clearing the low 3 bits) therefore puts an exact
+// midpoint back exactly on it and leaves every other quotient on its side of
+// every midpoint; the hardware E2M1 conversion then rounds ties to even.
+//
+// HBM-bound: one workgroup covers 32 rows x 256 columns; each lane loads 8
+// consecutive bf16 (16 bytes) per row, a wave reads two 512-byte row
+// segments, and the pair of lanes holding one 16-block exchanges its maximum
+// with a lane swap. Codes leave as one dword per lane (contiguous per row);
+// scales are staged in LDS and leave as 32-byte runs of the [K/16, M] layout.
+#include "common.h"
+#include "kernels.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int kRows = 32;     // rows per workgroup
+constexpr int kChunk = 256;   // K elements per workgroup (16 blocks)
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float snap21(float q) {
+  return __uint_as_float((__float_as_uint(q) + 4u) & ~7u);
+}
+
+__global__ __launch_bounds__(kThreads) void quant_act_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ smooth,
+    uint8_t* __restrict__ qact, uint8_t* __restrict__ ascales, int M, int K,
+    unsigned* __restrict__ counters, int n_counters) {
+  __shared__ uint8_t s_scale[kChunk / 16][kRows];
+
+  const int tid = threadIdx.x;
+  const int kk = tid & 31;        // 8-element group within the chunk
+  const int rsub = tid >> 5;      // 0..7
+  const int m_base = blockIdx.x * kRows;
+  const int k0 = blockIdx.y * kChunk + kk * 8;
+  const bool k_in = k0 < K;       // both halves of a block agree (K % 16 == 0)
+
+  if (counters != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = tid; i < n_counters; i += kThreads) counters[i] = 0u;
+  }
+
+  float sm[8];
+  if (k_in) {
+    const u32x4 s = *reinterpret_cast<const u32x4*>(smooth + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sm[2 * j] = bf16lo_to_f32(s[j]);
+      sm[2 * j + 1] = bf16hi_to_f32(s[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm[j] = 0.0f;
+  }
+
+#pragma unroll
+  for (int i = 0; i < kRows / 8; ++i) {
+    const int mr = rsub + 8 * i;
+    const int m = m_base + mr;
+    const bool ok = k_in && m < M;
+    float v[8];
+    float amax = 0.0f;
+    if (ok) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + k0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf16lo_to_f32(w[j]) * sm[2 * j];
+        v[2 * j + 1] = bf16hi_to_f32(w[j]) * sm[2 * j + 1];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+    // the other half of this 16-block sits in the neighbouring lane
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+
+    const uint32_t sc = f32_to_e4m3_sat(__fdiv_rn(amax, 6.0f));
+    const float sd = e4m3_to_f32(sc, 0);
+    const float inv = sd > 0.0f ? __fdiv_rn(1.0f, sd) : 0.0f;
+
+    uint32_t packed = 0u;
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[0] * inv), snap21(v[1] * inv), 1.0f, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[2] * inv), snap21(v[3] * inv), 1.0f, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[4] * inv), snap21(v[5] * inv), 1.0f, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[6] * inv), snap21(v[7] * inv), 1.0f, 3);
+
+    if (ok) {
+      *reinterpret_cast<uint32_t*>(qact + (size_t)m * (K / 2) + k0 / 2) = packed;
+      if ((kk & 1) == 0) s_scale[kk >> 1][mr] = (uint8_t)sc;
+    }
+  }
+  __syncthreads();
+
+  // scales: [K/16, M] layout, 32 consecutive bytes per block row
+  const int kb0 = blockIdx.y * (kChunk / 16);
+#pragma unroll
+  for (int u = 0; u < (kChunk / 16) * kRows / kThreads; ++u) {
+    const int idx = tid + u * kThreads;
+    const int kbl = idx / kRows;
+    const int mr = idx % kRows;
+    const int m = m_base + mr;
+    const int kb = kb0 + kbl;
+    if (m < M && kb * 16 < K) ascales[(size_t)kb * M + m] = s_scale[kbl][mr];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const uint16_t* x, const uint16_t* smooth, uint8_t* qact,
+                            uint8_t* ascales, int64_t M, int64_t K, unsigned* counters,
+                            int n_counters, hipStream_t stream) {
+  dim3 grid((unsigned)((M + kRows - 1) / kRows), (unsigned)((K + kChunk - 1) / kChunk));
+  hipLaunchKernelGGL(quant_act_kernel, grid, dim3(kThreads), 0, stream, x, smooth, qact,
+                     ascales, (int)M, (int)K, counters, n_counters);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

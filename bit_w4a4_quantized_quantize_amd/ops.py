@@ -1,0 +1,193 @@
+"""PyTorch-facing binding of the HIP library: argument marshalling only.
+
+Every function checks dtype/device/contiguity, allocates outputs with torch
+(device memory and the current stream are the only things torch provides),
+and calls the C ABI with raw pointers. All arithmetic happens in the HIP
+kernels; there is no CPU or PyTorch fallback.
+
+Tensors (bf16 unless stated): x [M, K]; smooth [K]; qweight uint8 [N, K/2]
+(low nibble = even k); wscales uint8 [K/16, N] (e4m3fn bytes; a
+torch.float8_e4m3fn tensor is accepted and viewed as bytes); wcscales [N];
+wtscale [1]; proj_down [K, R]; proj_up [N, R]; bias [N] or None.
+"""
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import WEIGHT_CANONICAL, WEIGHT_PACKED, SvdqError  # noqa: F401
+
+
+def _bytes(t):
+    if t.dtype == torch.float8_e4m3fn or t.dtype == torch.int8:
+        return t.view(torch.uint8)
+    return t
+
+
+def _need(t, name, dtype, ndim=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device=None):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=None):
+    """quant(x * smooth) and, with proj_down, lora_act = x @ proj_down.
+
+    Returns (qact uint8 [M, K/2], ascales uint8 [K/16, M], lora_act bf16 [M, R] or None).
+    """
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    _need(smooth, "smooth", torch.bfloat16, 1)
+    R = 0
+    if proj_down is not None:
+        _need(proj_down, "proj_down", torch.bfloat16, 2)
+        R = proj_down.shape[1]
+    dev = x.device
+    if qact is None:
+        qact = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if ascales is None:
+        ascales = torch.empty((K // 16, M), dtype=torch.uint8, device=dev)
+    if R > 0 and lora_act is None:
+        lora_act = torch.empty((M, R), dtype=torch.bfloat16, device=dev)
+    L = _lib.lib()
+    ws_bytes = L.svdq_quantize_act_workspace_bytes(M, K, R)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    _lib.check("svdq_quantize_act", L.svdq_quantize_act(
+        _p(x), _p(smooth), M, K, _p(proj_down), R, _p(qact), _p(ascales),
+        _p(lora_act) if R > 0 else None, _p(ws), ws_bytes, _stream(dev)))
+    return qact, ascales, (lora_act if R > 0 else None)
+
+
+def repack_weight(qweight, wscales):
+    """qweight [N, K/2] + wscales [K/16, N] -> packed uint8 buffer (MFMA order)."""
+    qweight = _need(_bytes(qweight), "qweight", torch.uint8, 2)
+    wscales = _need(_bytes(wscales), "wscales", torch.uint8, 2)
+    N, Kh = qweight.shape
+    K = 2 * Kh
+    L = _lib.lib()
+    nbytes = L.svdq_repack_weight_bytes(N, K)
+    packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qweight.device)
+    _lib.check("svdq_repack_weight", L.svdq_repack_weight(
+        _p(qweight), _p(wscales), N, K, _p(packed), nbytes, _stream(qweight.device)))
+    return packed
+
+
+def unpack_weight(packed, N, K):
+    """Inverse of repack_weight: -> (qweight uint8 [N, K/2], wscales uint8 [K/16, N])."""
+    _need(packed, "packed", torch.uint8, 1)
+    qweight = torch.empty((N, K // 2), dtype=torch.uint8, device=packed.device)
+    wscales = torch.empty((K // 16, N), dtype=torch.uint8, device=packed.device)
+    L = _lib.lib()
+    _lib.check("svdq_unpack_weight", L.svdq_unpack_weight(
+        _p(packed), packed.numel(), N, K, _p(qweight), _p(wscales), _stream(packed.device)))
+    return qweight, wscales
+
+
+@dataclass
+class SVDQLinearWeights:
+    """One quantised linear layer's tensors, on the GPU.
+
+    weight is qweight [N, K/2] (layout WEIGHT_CANONICAL, wscales given) or a
+    buffer from repack_weight (layout WEIGHT_PACKED, wscales None).
+    """
+    N: int
+    K: int
+    weight: torch.Tensor
+    wscales: Optional[torch.Tensor]
+    wcscales: torch.Tensor
+    wtscale: torch.Tensor
+    smooth: torch.Tensor
+    proj_down: Optional[torch.Tensor]
+    proj_up: Optional[torch.Tensor]
+    bias: Optional[torch.Tensor] = None
+    layout: int = WEIGHT_CANONICAL
+
+    @property
+    def R(self):
+        return 0 if self.proj_down is None else int(self.proj_down.shape[1])
+
+    def packed(self):
+        """A copy of this layer with the weight repacked (load-time step)."""
+        if self.layout == WEIGHT_PACKED:
+            return self
+        buf = repack_weight(self.weight, self.wscales)
+        return SVDQLinearWeights(self.N, self.K, buf, None, self.wcscales, self.wtscale, self.smooth,
+                                 self.proj_down, self.proj_up, self.bias, WEIGHT_PACKED)
+
+
+def _check_layer(w: SVDQLinearWeights):
+    if w.layout == WEIGHT_CANONICAL:
+        _need(_bytes(w.weight), "qweight", torch.uint8, 2)
+        _need(_bytes(w.wscales), "wscales", torch.uint8, 2)
+    else:
+        _need(w.weight, "packed weight", torch.uint8, 1)
+    _need(w.wcscales, "wcscales", torch.bfloat16, 1)
+    _need(w.wtscale, "wtscale", torch.bfloat16, 1)
+    if w.R > 0:
+        _need(w.proj_down, "proj_down", torch.bfloat16, 2)
+        _need(w.proj_up, "proj_up", torch.bfloat16, 2)
+    if w.bias is not None:
+        _need(w.bias, "bias", torch.bfloat16, 1)
+
+
+def gemm_w4a4(qact, ascales, lora_act, w: SVDQLinearWeights, y=None):
+    """The scaled GEMM + low-rank up-projection + epilogue from quantised activations."""
+    _check_layer(w)
+    _need(qact, "qact", torch.uint8, 2)
+    _need(ascales, "ascales", torch.uint8, 2)
+    M = qact.shape[0]
+    if w.R > 0:
+        _need(lora_act, "lora_act", torch.bfloat16, 2)
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.bfloat16, device=qact.device)
+    L = _lib.lib()
+    _lib.check("svdq_gemm_w4a4", L.svdq_gemm_w4a4(
+        _p(qact), _p(ascales), _p(lora_act) if w.R > 0 else None,
+        _p(_bytes(w.weight)), _p(_bytes(w.wscales)) if w.wscales is not None else None, w.layout,
+        _p(w.wcscales), _p(w.wtscale), _p(w.proj_up) if w.R > 0 else None, _p(w.bias),
+        M, w.N, w.K, w.R, _p(y), _stream(qact.device)))
+    return y
+
+
+def linear_workspace_bytes(M, N, K, R):
+    return _lib.lib().svdq_linear_workspace_bytes(M, N, K, R)
+
+
+def linear_w4a4(x, w: SVDQLinearWeights, y=None, workspace=None):
+    """The whole layer: y [M, N] bf16."""
+    _check_layer(w)
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"x has K={K}, the layer K={w.K}")
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device)
+    L = _lib.lib()
+    nbytes = L.svdq_linear_workspace_bytes(M, w.N, K, w.R)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _lib.check("svdq_linear_w4a4", L.svdq_linear_w4a4(
+        _p(x), _p(w.smooth), _p(_bytes(w.weight)),
+        _p(_bytes(w.wscales)) if w.wscales is not None else None, w.layout,
+        _p(w.wcscales), _p(w.wtscale), _p(w.proj_down) if w.R > 0 else None,
+        _p(w.proj_up) if w.R > 0 else None, _p(w.bias), M, w.N, K, w.R,
+        _p(y), _p(workspace), workspace.numel(), _stream(x.device)))
+    return y

@@ -1,0 +1,170 @@
+/*
+ * svdq.h - C ABI of the MI355X (gfx950) SVDQuant W4A4 NVFP4 linear layer.
+ *
+ * The layer (model card "nunchaku-z-image-turbo-svdq", section "What's stored
+ * on disk", runtime reconstruction formula):
+ *
+ *   y = scaled_mma(quant(x * smooth), qweight, ascales, wscales) * wtscale * wcscales
+ *       + (x @ proj_down) @ proj_up^T + bias
+ *
+ * NVFP4 = E2M1 values with one float8_e4m3fn scale per 16 consecutive K
+ * elements (same card, header). On-disk tensors, all canonical row-major
+ * (same section, tensor table):
+ *   qweight   [N, K/2] int8   two E2M1 codes per byte, low nibble = even k
+ *   wscales   [K/16, N] e4m3fn
+ *   wcscales  [N] bf16        per output channel
+ *   wtscale   [1] bf16        global alpha (read on the device)
+ *   smooth    [K] bf16        smooth_factor
+ *   proj_down [K, R] bf16     SVD residual, down
+ *   proj_up   [N, R] bf16     SVD residual, up
+ * Runtime tensors the card leaves unspecified, fixed by this library:
+ *   x         [M, K] bf16     activations
+ *   qact      [M, K/2] u8     activation codes, low nibble = even k
+ *   ascales   [K/16, M] e4m3fn activation block scales (mirrors wscales)
+ *   lora_act  [M, R] bf16     x @ proj_down (raw x, not smoothed)
+ *   bias      [N] bf16        optional (NULL = no bias)
+ *   y         [M, N] bf16     output, round to nearest even
+ *
+ * Activation quantisation rule (the pages only name "quant"): per row and
+ * 16-block, v = x * smooth in fp32 (exact), s = max|v| / 6 rounded to e4m3
+ * (nearest-even, saturating at 448), codes = E2M1 nearest-even of |v| / s
+ * (saturating at 6) with the sign bit of v; a zero scale gives zero codes.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers on the current HIP device, except where a
+ *    comment says otherwise; sizes are element counts. `stream` is a
+ *    hipStream_t (NULL = the null stream). Work is enqueued on `stream` in
+ *    order; no entry point synchronises the host or allocates device memory,
+ *    and none keeps a pointer after it returns. The caller owns every buffer
+ *    and keeps it alive until the stream has passed the enqueued work.
+ *  - Every argument is checked on the host before any HIP call. On error
+ *    nothing is enqueued and outputs are untouched; svdq_last_error() then
+ *    returns a message for the calling thread. No C++ exception crosses
+ *    the ABI. Entry points are thread-safe and reentrant.
+ *  - M == 0 or N == 0 is a valid empty problem: nothing is enqueued.
+ *  - K must be a positive multiple of 16 (the NVFP4 block). R must be 0 or a
+ *    multiple of 16 (SVDQ_ERR_UNSUPPORTED otherwise). Every pointer must be
+ *    16-byte aligned (SVDQ_ERR_ALIGN).
+ *  - NaN or Inf inputs are not checked; results are then unspecified.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_NULL = 1,         /* a required pointer is NULL                      */
+  SVDQ_ERR_SHAPE = 2,        /* negative size, K not a positive multiple of 16  */
+  SVDQ_ERR_UNSUPPORTED = 3,  /* valid for the format, outside these kernels      */
+  SVDQ_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned                */
+  SVDQ_ERR_WORKSPACE = 5,    /* workspace (or packed buffer) too small          */
+  SVDQ_ERR_ALIAS = 6,        /* an output overlaps an input or another output   */
+  SVDQ_ERR_HIP = 7,          /* a HIP launch reported an error                  */
+  SVDQ_ERR_INVALID = 8       /* bad enum value or argument combination          */
+} svdq_status;
+
+/* Weight layouts accepted by the GEMM entry points. */
+enum {
+  SVDQ_WEIGHT_CANONICAL = 0, /* qweight [N, K/2] + wscales [K/16, N] as on disk            */
+  SVDQ_WEIGHT_PACKED = 1     /* one buffer from svdq_repack_weight; wscales must be NULL    */
+};
+
+#define SVDQ_ABI_VERSION 1
+
+int svdq_abi_version(void);
+const char* svdq_status_string(int status);
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* svdq_last_error(void);
+
+/*
+ * Activation quantisation quant(x * smooth), and the down-projection of the
+ * low-rank branch x @ proj_down (model card, section "What's stored on disk":
+ * the activation operand of scaled_mma and the (x @ proj_down) factor).
+ *
+ *   x [M, K] bf16, smooth [K] bf16          inputs
+ *   qact [M, K/2] u8, ascales [K/16, M] u8  outputs (rule in the file header)
+ *   proj_down [K, R] bf16, lora_act [M, R] bf16: used when R > 0 (both
+ *     required then); lora_act = bf16(x @ proj_down) with fp32 accumulation.
+ *   workspace: device scratch of at least svdq_quantize_act_workspace_bytes(M, K, R)
+ *     bytes (may be NULL when that size is 0); its contents need no
+ *     initialisation and are garbage afterwards.
+ * qact and ascales are bit-exact functions of x and smooth.
+ */
+size_t svdq_quantize_act_workspace_bytes(int64_t M, int64_t K, int64_t R);
+int svdq_quantize_act(const void* x, const void* smooth, int64_t M, int64_t K,
+                      const void* proj_down, int64_t R,
+                      void* qact, void* ascales, void* lora_act,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Load-time weight repack into the library's MFMA-order layout, and its
+ * inverse (model card, section "Why row-major": a one-shot pack at load time
+ * forming a bit-exact pair with its unpack; section "Conversion source":
+ * round trip verified bit-exact).
+ *
+ * Layout: n-panels of 32 channels, k-panels of 64 (four 16-blocks);
+ * NP = ceil(N/32), KP = ceil(K/64). Code region: chunk (p, q) of 1024 bytes
+ * at offset 1024*(p*NP+q); dword (h*32+c)*4+t holds the 4 canonical qweight
+ * bytes of channel 32q+c at k = 64p+16t+8h .. +7. Scale region after it:
+ * chunk (p, q) of 128 bytes at 1024*KP*NP + 128*(p*NP+q); byte c*4+t holds
+ * wscales[4p+t, 32q+c]. Positions outside N or K are zero.
+ *
+ * svdq_repack_weight: qweight [N, K/2] u8 + wscales [K/16, N] u8 -> packed
+ *   (packed_bytes >= svdq_repack_weight_bytes(N, K), else SVDQ_ERR_WORKSPACE).
+ * svdq_unpack_weight: packed -> qweight_out, wscales_out (canonical), exact inverse.
+ */
+size_t svdq_repack_weight_bytes(int64_t N, int64_t K);
+int svdq_repack_weight(const void* qweight, const void* wscales, int64_t N, int64_t K,
+                       void* packed, size_t packed_bytes, void* stream);
+int svdq_unpack_weight(const void* packed, size_t packed_bytes, int64_t N, int64_t K,
+                       void* qweight_out, void* wscales_out, void* stream);
+
+/*
+ * The scaled GEMM with the low-rank up-projection and the epilogue, from
+ * already quantised activations (model card, section "What's stored on disk",
+ * runtime formula without the quant step):
+ *
+ *   y = bf16( scaled_mma(qact, weight, ascales, wscales) * wtscale * wcscales[n]
+ *             + lora_act @ proj_up^T + bias[n] )
+ *
+ *   qact [M, K/2] u8, ascales [K/16, M] u8, lora_act [M, R] bf16 (R > 0)
+ *   weight: qweight [N, K/2] (SVDQ_WEIGHT_CANONICAL, wscales [K/16, N] given)
+ *           or a packed buffer (SVDQ_WEIGHT_PACKED, wscales NULL)
+ *   wcscales [N] bf16, wtscale [1] bf16, proj_up [N, R] bf16 (R > 0), bias [N] bf16 or NULL
+ *   y [M, N] bf16 output; must not overlap any input.
+ * The main term is exact per 16-block (operands are dequantised exactly to
+ * f16 and multiplied on the matrix cores with fp32 accumulation); the sum
+ * over blocks and the epilogue round in fp32.
+ */
+int svdq_gemm_w4a4(const void* qact, const void* ascales, const void* lora_act,
+                   const void* weight, const void* wscales, int weight_layout,
+                   const void* wcscales, const void* wtscale, const void* proj_up,
+                   const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                   void* y, void* stream);
+
+/*
+ * The whole layer: svdq_quantize_act into the workspace, then svdq_gemm_w4a4.
+ *   x [M, K] bf16, smooth [K] bf16, weight/wscales/weight_layout as above,
+ *   wcscales, wtscale, proj_down [K, R], proj_up [N, R], bias (or NULL),
+ *   y [M, N] bf16; workspace of at least svdq_linear_workspace_bytes(M, N, K, R)
+ *   bytes (no initialisation needed).
+ */
+size_t svdq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t R);
+int svdq_linear_w4a4(const void* x, const void* smooth,
+                     const void* weight, const void* wscales, int weight_layout,
+                     const void* wcscales, const void* wtscale,
+                     const void* proj_down, const void* proj_up, const void* bias,
+                     int64_t M, int64_t N, int64_t K, int64_t R,
+                     void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

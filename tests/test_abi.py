@@ -1,0 +1,173 @@
+"""C ABI host tests: the library loads without a GPU, exports every entry point
+include/svdq.h declares, and rejects bad arguments on the host before any HIP call.
+
+The error-path cases use fake device addresses that are never dereferenced; each
+case is built to fail validation, so nothing is ever launched. They are skipped
+where a GPU is visible, so a validation regression can never turn one of them
+into a launch with fake pointers.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from bit_w4a4_quantized_quantize_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+no_gpu_only = pytest.mark.skipif(torch.cuda.is_available(),
+                                 reason="fake-pointer validation cases run on CPU-only hosts")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svdq_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported_and_bound():
+    L = _lib.lib()
+    names = header_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(L, name), name
+        assert name in _lib.SIGNATURES, name
+    assert L.svdq_abi_version() == 1
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code in range(9):
+        assert L.svdq_status_string(code).decode()
+    assert L.svdq_status_string(99).decode() == "unknown status"
+
+
+def test_size_queries():
+    L = _lib.lib()
+    assert L.svdq_repack_weight_bytes(10240, 3840) == 10240 * 3840 // 2 + 10240 * 3840 // 16
+    assert L.svdq_repack_weight_bytes(33, 80) == 2 * 2 * 1152
+    assert L.svdq_repack_weight_bytes(10, 15) == 0
+    ws = L.svdq_linear_workspace_bytes(4096, 10240, 3840, 128)
+    assert ws >= 4096 * 1920 + 240 * 4096 + 4096 * 128 * 2
+    assert L.svdq_quantize_act_workspace_bytes(4096, 3840, 0) == 0
+    assert L.svdq_quantize_act_workspace_bytes(0, 3840, 128) == 0
+
+
+A = 0x7F0000000000  # fake, 16-byte aligned device addresses, never dereferenced
+
+
+def fake(i):
+    return A + i * 0x10000000
+
+
+def q(**kw):
+    args = dict(x=fake(1), smooth=fake(2), M=64, K=256, proj_down=fake(3), R=16,
+                qact=fake(4), ascales=fake(5), lora_act=fake(6), ws=fake(7), ws_bytes=1 << 30,
+                stream=None)
+    args.update(kw)
+    L = _lib.lib()
+    return L.svdq_quantize_act(args["x"], args["smooth"], args["M"], args["K"], args["proj_down"],
+                               args["R"], args["qact"], args["ascales"], args["lora_act"],
+                               args["ws"], args["ws_bytes"], args["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), 2), (dict(K=0), 2), (dict(K=24), 2), (dict(R=-16), 2),
+    (dict(R=8), 3), (dict(K=1 << 25), 3),
+    (dict(x=None), 1), (dict(smooth=None), 1), (dict(qact=None), 1), (dict(ascales=None), 1),
+    (dict(proj_down=None), 1), (dict(lora_act=None), 1),
+    (dict(x=fake(1) + 8), 4), (dict(ascales=fake(5) + 4), 4),
+    (dict(qact=fake(1) + 64), 6), (dict(lora_act=fake(3)), 6), (dict(ascales=fake(4)), 6),
+])
+def test_quantize_act_rejections(kw, code):
+    assert q(**kw) == code
+    assert _lib.lib().svdq_last_error().decode() != ""
+
+
+@no_gpu_only
+def test_quantize_act_workspace_checks():
+    L = _lib.lib()
+    need = L.svdq_quantize_act_workspace_bytes(4096, 3840, 128)
+    assert need > 0
+    assert q(M=4096, K=3840, R=128, ws_bytes=need - 1) == 5
+    assert q(M=4096, K=3840, R=128, ws=None) == 1
+    assert q(M=4096, K=3840, R=128, ws=fake(7) + 8) == 4
+
+
+@no_gpu_only
+def test_empty_problem_is_ok_without_pointers():
+    assert q(M=0, x=None, smooth=None, qact=None, ascales=None) == 0
+
+
+def gemm(**kw):
+    args = dict(qact=fake(1), ascales=fake(2), lora=fake(3), weight=fake(4), wscales=fake(5), layout=0,
+                wcscales=fake(6), wtscale=fake(7), proj_up=fake(8), bias=fake(9),
+                M=64, N=128, K=256, R=16, y=fake(10), stream=None)
+    args.update(kw)
+    L = _lib.lib()
+    return L.svdq_gemm_w4a4(args["qact"], args["ascales"], args["lora"], args["weight"], args["wscales"],
+                            args["layout"], args["wcscales"], args["wtscale"], args["proj_up"],
+                            args["bias"], args["M"], args["N"], args["K"], args["R"], args["y"],
+                            args["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-3), 2), (dict(K=40), 2), (dict(R=24), 3),
+    (dict(layout=5), 8), (dict(layout=1), 8), (dict(wscales=None), 1),
+    (dict(qact=None), 1), (dict(y=None), 1), (dict(wtscale=None), 1), (dict(proj_up=None), 1),
+    (dict(lora=None), 1), (dict(bias=fake(9) + 2), 4), (dict(weight=fake(4) + 1), 4),
+    (dict(y=fake(1)), 6), (dict(y=fake(6) - 64), 6),
+])
+def test_gemm_rejections(kw, code):
+    assert gemm(**kw) == code
+
+
+@no_gpu_only
+def test_gemm_empty_and_optional_bias_and_r0():
+    assert gemm(M=0) == 0
+    assert gemm(N=0) == 0
+    # R = 0 needs neither lora_act nor proj_up; these calls still fail later only on y=None
+    assert gemm(R=0, lora=None, proj_up=None, y=None) == 1
+
+
+def lin(**kw):
+    args = dict(x=fake(1), smooth=fake(2), weight=fake(3), wscales=fake(4), layout=0,
+                wcscales=fake(5), wtscale=fake(6), proj_down=fake(7), proj_up=fake(8), bias=None,
+                M=64, N=128, K=256, R=16, y=fake(9), ws=fake(10), ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    L = _lib.lib()
+    return L.svdq_linear_w4a4(args["x"], args["smooth"], args["weight"], args["wscales"], args["layout"],
+                              args["wcscales"], args["wtscale"], args["proj_down"], args["proj_up"],
+                              args["bias"], args["M"], args["N"], args["K"], args["R"], args["y"],
+                              args["ws"], args["ws_bytes"], args["stream"])
+
+
+@no_gpu_only
+def test_linear_rejections():
+    L = _lib.lib()
+    need = L.svdq_linear_workspace_bytes(64, 128, 256, 16)
+    assert lin(ws_bytes=need - 1) == 5
+    assert lin(ws=None) == 1
+    assert lin(proj_down=None) == 1
+    assert lin(y=fake(10)) == 6          # y overlaps the workspace
+    assert lin(K=17) == 2
+    assert lin(M=0) == 0
+
+
+@no_gpu_only
+def test_repack_rejections():
+    L = _lib.lib()
+    need = L.svdq_repack_weight_bytes(128, 256)
+    assert L.svdq_repack_weight(fake(1), fake(2), 128, 256, fake(3), need - 1, None) == 5
+    assert L.svdq_repack_weight(None, fake(2), 128, 256, fake(3), need, None) == 1
+    assert L.svdq_repack_weight(fake(1), fake(2), 128, 250, fake(3), need, None) == 2
+    assert L.svdq_repack_weight(fake(1), fake(2), 128, 256, fake(1) + 16, need, None) == 6
+    assert L.svdq_unpack_weight(fake(1), need, 128, 256, fake(1), fake(2), None) == 6
+    assert L.svdq_unpack_weight(fake(1), need, 0, 256, None, None, None) == 0

@@ -1,0 +1,105 @@
+"""GPU parity of the scaled GEMM + low-rank up-projection + epilogue (svdq_gemm_w4a4).
+
+Inputs: the oracle's own quantised activations and weights and a bf16 lora_act,
+so the GPU and the oracle see identical operands; the oracle then evaluates the
+formula in float64. Gate: normwise relative error <= 5e-3 on the bf16 output.
+Diagnostic bound (also asserted): nearly every element is within one bf16 ulp of
+the float64 result, since only fp32 accumulation and the final cast round.
+
+Cases: canonical and packed weight layouts (bit-identical outputs), R = 0,
+qweight = 0 (pure low-rank product), no bias, ragged M and N, K of one block and
+K not a multiple of the 64-wide stage, the 1024^2 FFN shape sampled by rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import formats as F
+from oracle import svdq as S
+from tests.gpu_util import dev_bf16, dev_u8, host_bits, make_layer, within_ulps
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+
+
+_CACHE = {}
+
+
+def _oracle_inputs(cfg, with_bias, zero_weight):
+    key = (tuple(sorted(cfg.items())), with_bias, zero_weight)
+    if key not in _CACHE:
+        d, layer = make_layer(cfg, with_bias=with_bias, zero_weight=zero_weight)
+        qact, ascales = S.quantize_act(d["x"], d["smooth"])
+        lora_bits = F.f64_to_bf16(S.lowrank_down(d["x"], d["proj_down"])) if d["R"] > 0 else None
+        _CACHE.clear()
+        _CACHE[key] = (d, layer, qact, ascales, lora_bits)
+    return _CACHE[key]
+
+
+def gemm_case(ops, cfg, packed=False, with_bias=True, zero_weight=False, rows=None):
+    d, layer, qact, ascales, lora_bits = _oracle_inputs(cfg, with_bias, zero_weight)
+    R = d["R"]
+    if packed:
+        layer = layer.packed()
+    y = ops.gemm_w4a4(dev_u8(qact), dev_u8(ascales), dev_bf16(lora_bits) if R > 0 else None, layer)
+    torch.cuda.synchronize()
+    y_bits = host_bits(y)
+    sel = slice(None) if rows is None else rows
+    y64 = S.gemm_w4a4(qact[sel], ascales[:, sel], F.bf16_to_f64(lora_bits)[sel] if R > 0 else None,
+                      d["qweight"], d["wscales"], d["wcscales"], d["wtscale"],
+                      d["proj_up"] if R > 0 else None, d["bias"])
+    got = y_bits[sel]
+    err = S.normwise_rel_err(F.bf16_to_f64(got), y64)
+    assert err <= TOL, err
+    frac = within_ulps(got, y64, 1).mean()
+    assert frac >= 0.999, frac
+    return y_bits, err
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(M=64, K=256, N=128, R=16, kind="tiny", seed=1001),
+    dict(M=200, K=3840, N=384, R=128, kind="dit", seed=21),
+    dict(M=1, K=256, N=16, R=16, kind="dit", seed=22),
+    dict(M=63, K=16, N=100, R=16, kind="tiny", seed=23),
+    dict(M=130, K=336, N=4100, R=32, kind="dit", seed=24),     # K % 64 != 0, ragged N
+    dict(M=257, K=1024, N=257, R=0, kind="dit", seed=25),      # R = 0
+    dict(M=96, K=10240, N=256, R=128, kind="swiglu", seed=26),
+])
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_parity(gpu_lib, cfg, packed):
+    gemm_case(gpu_lib, cfg, packed=packed)
+
+
+def test_gemm_layouts_bit_identical(gpu_lib):
+    cfg = dict(M=300, K=768, N=520, R=64, kind="dit", seed=31)
+    a, _ = gemm_case(gpu_lib, cfg, packed=False)
+    b, _ = gemm_case(gpu_lib, cfg, packed=True)
+    assert np.array_equal(a, b)
+
+
+def test_gemm_zero_weight_is_lowrank_plus_bias(gpu_lib):
+    gemm_case(gpu_lib, dict(M=128, K=512, N=192, R=128, kind="dit", seed=32), zero_weight=True)
+
+
+def test_gemm_no_bias(gpu_lib):
+    gemm_case(gpu_lib, dict(M=128, K=512, N=192, R=16, kind="dit", seed=33), with_bias=False)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_full_ffn_shape_sampled_rows(gpu_lib, packed):
+    """M=4096, K=3840, N=10240, R=128 (FFN w1 at 1024^2): the whole output on the GPU,
+    checked against the oracle on 48 sampled rows (all columns)."""
+    cfg = workloads.FFN_W1_1024
+    rows = np.sort(np.random.default_rng(5).choice(cfg["M"], size=48, replace=False))
+    rows[0], rows[-1] = 0, cfg["M"] - 1
+    gemm_case(gpu_lib, cfg, packed=packed, rows=rows)
+
+
+def test_gemm_deterministic(gpu_lib):
+    cfg = dict(M=256, K=1024, N=512, R=128, kind="dit", seed=34)
+    a, _ = gemm_case(gpu_lib, cfg)
+    b, _ = gemm_case(gpu_lib, cfg)
+    assert np.array_equal(a, b)

@@ -1,0 +1,132 @@
+"""GPU parity of the activation quantisation (qact, ascales): bit-exact against the oracle.
+
+Cases: the tiny and DiT-shaped workloads (outlier channels, SwiGLU-like inputs),
+the full 1024^2 activation shape, ragged M and K, exact E2M1 midpoints, signed
+zeros, all-zero and underflowing blocks, saturating blocks, and sentinel-filled
+outputs (every byte written, none beyond).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import formats as F
+from oracle import svdq as S
+from tests.gpu_util import dev_bf16, host_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def run_quant(ops, x_bits, sm_bits, sentinel=True):
+    M, K = x_bits.shape
+    x = dev_bf16(x_bits)
+    sm = dev_bf16(sm_bits)
+    qbuf = torch.full((M * (K // 2) + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full(((K // 16) * M + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    qact = qbuf[: M * (K // 2)].view(M, K // 2)
+    ascales = sbuf[: (K // 16) * M].view(K // 16, M)
+    ops.quantize_act(x, sm, qact=qact, ascales=ascales)
+    torch.cuda.synchronize()
+    if sentinel:
+        assert np.all(host_u8(qbuf[M * (K // 2):]) == 0xA5), "qact written past its end"
+        assert np.all(host_u8(sbuf[(K // 16) * M:]) == 0x5A), "ascales written past its end"
+    return host_u8(qact), host_u8(ascales)
+
+
+def assert_exact(ops, x_bits, sm_bits):
+    q_gpu, s_gpu = run_quant(ops, x_bits, sm_bits)
+    q_ref, s_ref = S.quantize_act(x_bits, sm_bits)
+    bad_s = np.argwhere(s_gpu != s_ref)
+    assert bad_s.size == 0, f"ascales mismatch at {bad_s[:5].tolist()}"
+    bad_q = np.argwhere(q_gpu != q_ref)
+    assert bad_q.size == 0, f"qact mismatch at {bad_q[:5].tolist()}: gpu {q_gpu[tuple(bad_q[0])]:#x} ref {q_ref[tuple(bad_q[0])]:#x}"
+
+
+@pytest.mark.parametrize("M,K,kind,seed", [
+    (64, 256, "tiny", 1001),
+    (256, 3840, "dit", 1002),
+    (96, 10240, "swiglu", 1023),
+    (1, 3840, "dit", 3),
+    (63, 272, "dit", 4),       # K not a multiple of the 256-wide chunk
+    (33, 48, "tiny", 5),       # K = 3 blocks
+    (4097, 256, "dit", 6),     # ragged M beyond a tile
+])
+def test_quant_bit_exact(gpu_lib, M, K, kind, seed):
+    x, sm = workloads.make_activation(M, K, kind=kind, seed=seed)
+    assert_exact(gpu_lib, x, sm)
+
+
+def test_quant_full_1024_shape(gpu_lib):
+    """The 1024^2 activation (M=4096, K=3840) with outlier channels, every element."""
+    cfg = workloads.FFN_W1_1024
+    x, sm = workloads.make_activation(cfg["M"], cfg["K"], kind=cfg["kind"], seed=cfg["seed"])
+    assert_exact(gpu_lib, x, sm)
+
+
+def test_quant_exact_ties_signed_zeros_and_special_blocks(gpu_lib):
+    rng = np.random.default_rng(17)
+    M, K = 64, 512
+    vals = np.zeros((M, K))
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for m in range(M):
+        for b in range(K // 16):
+            kind = (m + b) % 6
+            sc = F.e4m3_decode(np.array([rng.integers(0x08, 0x70)]))[0]
+            blk = np.zeros(16)
+            if kind == 0:      # exact midpoints times a normal scale, amax = 6 s
+                blk[0] = 6 * sc
+                blk[1:8] = mids * sc * np.where(rng.random(7) < 0.5, 1, -1)
+                blk[8:15] = mids[::-1] * sc
+            elif kind == 1:    # all zero with some negative zeros
+                blk[:] = 0.0
+            elif kind == 2:    # underflowing block: scale rounds to 0, signs kept
+                blk[:] = rng.standard_normal(16) * 2.0 ** -24
+            elif kind == 3:    # subnormal e4m3 scales
+                blk[:] = rng.standard_normal(16) * 2.0 ** -7
+            elif kind == 4:    # saturating: amax/6 > 448
+                blk[:] = rng.standard_normal(16) * 5000
+            else:              # ordinary
+                blk[:] = rng.standard_normal(16)
+            vals[m, 16 * b:16 * b + 16] = blk
+    x = F.f64_to_bf16(vals)
+    # negative zeros in the all-zero blocks
+    zero_blocks = np.zeros_like(x, dtype=bool)
+    for m in range(M):
+        for b in range(K // 16):
+            if (m + b) % 6 == 1:
+                zero_blocks[m, 16 * b:16 * b + 16:3] = True
+    x[zero_blocks] = 0x8000
+    ones = F.f64_to_bf16(np.ones(K))
+    # the tie cases must really be exact midpoints after bf16 rounding
+    xv = F.bf16_to_f64(x)
+    assert np.array_equal(np.abs(xv[vals != 0]), np.abs(F.bf16_to_f64(F.f64_to_bf16(vals[vals != 0]))))
+    assert_exact(gpu_lib, x, ones)
+    # also with a non-trivial smooth (bf16 x bf16 products, exact in fp32)
+    sm = F.f64_to_bf16(np.where(np.arange(K) % 2 == 0, 0.5, 2.0))
+    assert_exact(gpu_lib, x, sm)
+
+
+def test_quant_random_bit_patterns(gpu_lib):
+    """Arbitrary finite bf16 bit patterns (wide exponent range) times a random smooth."""
+    rng = np.random.default_rng(23)
+    M, K = 128, 1024
+    x = rng.integers(0, 1 << 16, size=(M, K), dtype=np.uint64).astype(np.uint16)
+    exp = (x >> 7) & 0xFF
+    x = np.where((exp > 100) & (exp < 150), x, x & 0x807F | (127 << 7)).astype(np.uint16)
+    sm = workloads.f32_to_bf16_bits(rng.uniform(0.25, 4.0, size=K))
+    assert_exact(gpu_lib, x, sm)
+
+
+def test_quant_deterministic(gpu_lib):
+    x, sm = workloads.make_activation(512, 3840, kind="dit", seed=8)
+    a = run_quant(gpu_lib, x, sm)
+    b = run_quant(gpu_lib, x, sm)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_quant_empty(gpu_lib):
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    sm = torch.ones(256, dtype=torch.bfloat16, device="cuda")
+    qact, ascales, lora = gpu_lib.quantize_act(x, sm)
+    assert qact.shape == (0, 128) and ascales.shape == (16, 0) and lora is None
