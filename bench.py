@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 SVDQuant linear TFLOP/s and % MFMA peak at M=4096,K=3840,N=10240, 1 GPU"
 PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense f16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
-GEMM_KERNEL_SOURCE = os.path.join(ROOT, "bit_w4a4_quantized_quantize_amd", "csrc", "gemm_w4a4.hip")
+GEMM_KERNEL_SOURCE = os.path.join(ROOT, "bit_w4a4_quantized_quantize_amd", "csrc", "gemm_packed.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_ffn_w1_1024_traffic.txt")
 
 
@@ -115,6 +115,7 @@ def make_sets(cfg, n_sets, layout, dev):
             ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
             qact=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
             ascales=torch.empty((K // 16, M), dtype=torch.uint8, device=dev),
+            qpk=torch.empty(ops._lib.lib().svdq_packed_act_bytes(M, K), dtype=torch.uint8, device=dev),
             lora=torch.empty((M, R), dtype=torch.bfloat16, device=dev)))
     return d, sets
 
@@ -188,7 +189,6 @@ def main():
 
     flops_linear = 2 * M * N * K + 2 * M * R * (K + N)
     flops_gemm = 2 * M * N * K + 2 * M * N * R
-    quant_bytes = M * K * 2 + K * 2 + M * K // 2 + (K // 16) * M + K * R * 2 + M * R * 2
 
     def step(i):
         s = sets[i]
@@ -212,24 +212,32 @@ def main():
     print(f"[bench] linear: {ms_per_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s "
           f"(wall {wall * 1e3 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
 
-    # ---- per-kernel timings on the same stream and rotation ----
-    for s in sets:
-        ops.quantize_act(s["x"], s["layer"].smooth, s["layer"].proj_down,
-                         qact=s["qact"], ascales=s["ascales"], lora_act=s["lora"])
+    # ---- per-kernel timings, same stream and rotation, the kernels the step runs ----
+    packed = args.layout == "packed"
+
+    def quant_down(i):
+        s = sets[i]
+        if packed:
+            ops.quantize_act(s["x"], s["layer"].smooth, s["layer"].proj_down, qact=s["qpk"],
+                             lora_act=s["lora"], packed=True)
+        else:
+            ops.quantize_act(s["x"], s["layer"].smooth, s["layer"].proj_down,
+                             qact=s["qact"], ascales=s["ascales"], lora_act=s["lora"])
+
+    for i in range(n_sets):
+        quant_down(i)
     torch.cuda.synchronize()
 
     def gemm(i):
         s = sets[i]
-        ops.gemm_w4a4(s["qact"], s["ascales"], s["lora"], s["layer"], y=s["y"])
+        if packed:
+            ops.gemm_w4a4(s["qpk"], None, s["lora"], s["layer"], y=s["y"], M=M)
+        else:
+            ops.gemm_w4a4(s["qact"], s["ascales"], s["lora"], s["layer"], y=s["y"])
 
     def quant(i):
         s = sets[i]
         ops.quantize_act(s["x"], s["layer"].smooth, None, qact=s["qact"], ascales=s["ascales"])
-
-    def quant_down(i):
-        s = sets[i]
-        ops.quantize_act(s["x"], s["layer"].smooth, s["layer"].proj_down,
-                         qact=s["qact"], ascales=s["ascales"], lora_act=s["lora"])
 
     gemm_ms = time_loop(gemm, n_sets, args.kernel_iters, 3, stream)
     quant_ms = time_loop(quant, n_sets, args.kernel_iters, 3, stream)
@@ -264,7 +272,9 @@ def main():
         },
         "pct_mfma_peak": round(100.0 * tflops / PEAK_F16_MFMA_TFLOPS, 2),
         "roofline": {
-            "kernel": "gemm_w4a4_kernel (a4 scaled GEMM + a5 low-rank up-projection + epilogue)",
+            "kernel": "gemm_packed_kernel (scaled GEMM + low-rank up-projection + epilogue)"
+                      if args.layout == "packed" else
+                      "gemm_w4a4_kernel (scaled GEMM + low-rank up-projection + epilogue)",
             "bound": "mfma",
             "achieved": round(gemm_tflops, 2),
             "peak": PEAK_F16_MFMA_TFLOPS,
@@ -279,7 +289,8 @@ def main():
             "hbm_bytes_per_launch": quant_bytes_a1,
             "achieved_GBps": round(quant_gbs, 1),
             "frac_of_hbm_peak": round(quant_gbs / PEAK_HBM_GBS, 4),
-            "with_down_projection_us": round(qd_ms * 1e3, 3),
+            "kernel": "quant_act_kernel (activation quantisation alone, canonical output)",
+            "fused_with_down_projection_us": round(qd_ms * 1e3, 3),
         },
     }
     if not args.no_cpu_baseline:

@@ -21,12 +21,13 @@ SIGNATURES = {
     "svdq_status_string": (ctypes.c_char_p, [_int]),
     "svdq_last_error": (ctypes.c_char_p, []),
     "svdq_quantize_act_workspace_bytes": (_size, [_i64, _i64, _i64]),
-    "svdq_quantize_act": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64,
+    "svdq_packed_act_bytes": (_size, [_i64, _i64]),
+    "svdq_quantize_act": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64, _int,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
     "svdq_repack_weight_bytes": (_size, [_i64, _i64]),
     "svdq_repack_weight": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _size, _c_void_p]),
     "svdq_unpack_weight": (_int, [_c_void_p, _size, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
-    "svdq_gemm_w4a4": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _int,
+    "svdq_gemm_w4a4": (_int, [_c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _c_void_p, _int,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
     "svdq_linear_workspace_bytes": (_size, [_i64, _i64, _i64, _i64]),
@@ -42,6 +43,8 @@ STATUS = {
 }
 WEIGHT_CANONICAL = 0
 WEIGHT_PACKED = 1
+ACT_CANONICAL = 0
+ACT_PACKED = 1
 
 _lib = None
 

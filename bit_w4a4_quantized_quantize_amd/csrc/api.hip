@@ -81,44 +81,41 @@ int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
 }
 
 size_t quant_ws_bytes(int64_t M, int64_t K, int64_t R) {
-  return R > 0 ? svdq::lora_down_workspace_bytes(M, K, R) : 0;
+  (void)M; (void)K; (void)R;
+  return 0;   // the fused quantisation / down-projection needs no scratch
 }
 
+// Whole-layer workspace: the quantised activations (canonical, or packed when
+// the weight is packed: the packed form is never smaller) and lora_act.
 struct LinearWs {
-  size_t qact, ascales, lora, down, total;
+  size_t act, ascales, lora, total;
 };
 LinearWs linear_ws(int64_t M, int64_t K, int64_t R) {
   LinearWs w;
-  w.qact = 0;
-  w.ascales = align256(w.qact + (size_t)M * (size_t)(K / 2));
-  w.lora = align256(w.ascales + (size_t)(K / 16) * (size_t)M);
-  w.down = align256(w.lora + (size_t)M * (size_t)R * 2);
-  w.total = w.down + quant_ws_bytes(M, K, R);
+  w.act = 0;
+  w.ascales = align256((size_t)M * (size_t)(K / 2));
+  const size_t canonical_end = align256(w.ascales + (size_t)(K / 16) * (size_t)M);
+  const size_t packed_end = align256(svdq::packed_weight_bytes(M, K));
+  w.lora = canonical_end > packed_end ? canonical_end : packed_end;
+  w.total = w.lora + (size_t)M * (size_t)R * 2;
   return w;
 }
 
 // enqueue a1 (+ a2): pointers already validated
 int run_quantize(const void* x, const void* smooth, int64_t M, int64_t K, const void* proj_down,
-                 int64_t R, void* qact, void* ascales, void* lora_act, void* workspace,
+                 int64_t R, void* qact, void* ascales, void* lora_act, bool packed_out,
                  hipStream_t s) {
-  unsigned* counters = nullptr;
-  int n_counters = 0;
-  if (R > 0 && svdq::lora_down_splits(M, K, R) > 1) {
-    counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
-                                           svdq::lora_down_counter_offset(M, K, R));
-    n_counters = svdq::lora_down_counters(M);
+  hipError_t e;
+  if (R == 0 && !packed_out) {
+    e = svdq::launch_quant_act(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
+                               static_cast<uint8_t*>(qact), static_cast<uint8_t*>(ascales), M, K, s);
+  } else {
+    e = svdq::launch_quant_lora(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
+                                static_cast<const uint16_t*>(proj_down), static_cast<uint8_t*>(qact),
+                                static_cast<uint8_t*>(ascales), static_cast<uint16_t*>(lora_act), M, K,
+                                R, packed_out, s);
   }
-  hipError_t e = svdq::launch_quant_act(static_cast<const uint16_t*>(x),
-                                        static_cast<const uint16_t*>(smooth),
-                                        static_cast<uint8_t*>(qact), static_cast<uint8_t*>(ascales),
-                                        M, K, counters, n_counters, s);
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
-  if (R > 0) {
-    e = svdq::launch_lora_down(static_cast<const uint16_t*>(x),
-                               static_cast<const uint16_t*>(proj_down),
-                               static_cast<uint16_t*>(lora_act), workspace, M, K, R, s);
-    if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "down-projection launch: %s", hipGetErrorString(e));
-  }
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "quantisation launch: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -165,37 +162,48 @@ size_t svdq_quantize_act_workspace_bytes(int64_t M, int64_t K, int64_t R) {
   return quant_ws_bytes(M, K, R);
 }
 
+size_t svdq_packed_act_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % 16 != 0) return 0;
+  return svdq::packed_weight_bytes(M, K);
+}
+
 int svdq_quantize_act(const void* x, const void* smooth, int64_t M, int64_t K,
-                      const void* proj_down, int64_t R, void* qact, void* ascales,
-                      void* lora_act, void* workspace, size_t workspace_bytes, void* stream) {
+                      const void* proj_down, int64_t R, int act_layout, void* qact,
+                      void* ascales, void* lora_act, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;   // no scratch is needed (size query returns 0)
   int st = check_mk(M, K, R);
   if (st) return st;
+  if (act_layout != SVDQ_ACT_CANONICAL && act_layout != SVDQ_ACT_PACKED)
+    return fail(SVDQ_ERR_INVALID, "act_layout %d is not a known layout", act_layout);
+  const bool packed = act_layout == SVDQ_ACT_PACKED;
+  if (packed && ascales != nullptr)
+    return fail(SVDQ_ERR_INVALID, "ascales must be NULL with the packed layout (the buffer holds them)");
   if (M == 0) return ok();
   {
-    const char* names[] = {"x", "smooth", "qact", "ascales"};
-    const void* ptrs[] = {x, smooth, qact, ascales};
-    if ((st = check_ptrs(names, ptrs, 4))) return st;
+    const char* names[] = {"x", "smooth", "qact"};
+    const void* ptrs[] = {x, smooth, qact};
+    if ((st = check_ptrs(names, ptrs, 3))) return st;
   }
-  const size_t need = quant_ws_bytes(M, K, R);
+  if (!packed) {
+    const char* names[] = {"ascales"};
+    const void* ptrs[] = {ascales};
+    if ((st = check_ptrs(names, ptrs, 1))) return st;
+  }
   if (R > 0) {
     const char* names[] = {"proj_down", "lora_act"};
     const void* ptrs[] = {proj_down, lora_act};
     if ((st = check_ptrs(names, ptrs, 2))) return st;
   }
-  if (need > 0) {
-    if (workspace == nullptr) return fail(SVDQ_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
-    if (!aligned16(workspace)) return fail(SVDQ_ERR_ALIGN, "workspace is not 16-byte aligned");
-    if (workspace_bytes < need)
-      return fail(SVDQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-  }
+  const size_t qbytes = packed ? svdq::packed_weight_bytes(M, K) : (size_t)M * (K / 2);
   const Range in[] = {range("x", x, (size_t)M * K * 2), range("smooth", smooth, (size_t)K * 2),
                       range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2)};
-  const Range out[] = {range("qact", qact, (size_t)M * (K / 2)),
-                       range("ascales", ascales, (size_t)(K / 16) * M),
-                       range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
-                       range("workspace", need > 0 ? workspace : nullptr, need)};
-  if ((st = check_alias(in, 3, out, 4))) return st;
-  return run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora_act, workspace,
+  const Range out[] = {range("qact", qact, qbytes),
+                       range("ascales", packed ? nullptr : ascales, (size_t)(K / 16) * M),
+                       range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2)};
+  if ((st = check_alias(in, 3, out, 3))) return st;
+  return run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora_act, packed,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -259,7 +267,7 @@ int svdq_unpack_weight(const void* packed, size_t packed_bytes, int64_t N, int64
   return ok();
 }
 
-static int validate_gemm(const void* qact, const void* ascales, const void* lora_act,
+static int validate_gemm(const void* qact, const void* ascales, int act_layout, const void* lora_act,
                          const void* weight, const void* wscales, int weight_layout,
                          const void* wcscales, const void* wtscale, const void* proj_up,
                          const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
@@ -272,9 +280,21 @@ static int validate_gemm(const void* qact, const void* ascales, const void* lora
     if ((st = check_ptrs(names, ptrs, 4))) return st;
   }
   if (check_act) {
-    const char* names[] = {"qact", "ascales"};
-    const void* ptrs[] = {qact, ascales};
-    if ((st = check_ptrs(names, ptrs, 2))) return st;
+    if (act_layout != SVDQ_ACT_CANONICAL && act_layout != SVDQ_ACT_PACKED)
+      return fail(SVDQ_ERR_INVALID, "act_layout %d is not a known layout", act_layout);
+    if (act_layout == SVDQ_ACT_PACKED) {
+      if (ascales != nullptr)
+        return fail(SVDQ_ERR_INVALID, "ascales must be NULL with packed activations");
+      if (weight_layout != SVDQ_WEIGHT_PACKED)
+        return fail(SVDQ_ERR_INVALID, "packed activations need the packed weight layout");
+      const char* names[] = {"qact"};
+      const void* ptrs[] = {qact};
+      if ((st = check_ptrs(names, ptrs, 1))) return st;
+    } else {
+      const char* names[] = {"qact", "ascales"};
+      const void* ptrs[] = {qact, ascales};
+      if ((st = check_ptrs(names, ptrs, 2))) return st;
+    }
   }
   if (weight_layout == SVDQ_WEIGHT_CANONICAL && !aligned16(wscales))
     return fail(SVDQ_ERR_ALIGN, "wscales is not 16-byte aligned");
@@ -292,7 +312,7 @@ static int validate_gemm(const void* qact, const void* ascales, const void* lora
   return SVDQ_OK;
 }
 
-int svdq_gemm_w4a4(const void* qact, const void* ascales, const void* lora_act,
+int svdq_gemm_w4a4(const void* qact, const void* ascales, int act_layout, const void* lora_act,
                    const void* weight, const void* wscales, int weight_layout,
                    const void* wcscales, const void* wtscale, const void* proj_up,
                    const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y,
@@ -301,11 +321,12 @@ int svdq_gemm_w4a4(const void* qact, const void* ascales, const void* lora_act,
   if (st) return st;
   if ((st = check_nk(N, K))) return st;
   if (M == 0 || N == 0) return ok();
-  if ((st = validate_gemm(qact, ascales, lora_act, weight, wscales, weight_layout, wcscales, wtscale,
-                          proj_up, bias, M, N, K, R, y, true)))
+  if ((st = validate_gemm(qact, ascales, act_layout, lora_act, weight, wscales, weight_layout, wcscales,
+                          wtscale, proj_up, bias, M, N, K, R, y, true)))
     return st;
-  const Range in[] = {range("qact", qact, (size_t)M * (K / 2)),
-                      range("ascales", ascales, (size_t)(K / 16) * M),
+  const bool act_packed = act_layout == SVDQ_ACT_PACKED;
+  const Range in[] = {range("qact", qact, act_packed ? svdq::packed_weight_bytes(M, K) : (size_t)M * (K / 2)),
+                      range("ascales", act_packed ? nullptr : ascales, (size_t)(K / 16) * M),
                       range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
                       range("weight", weight, weight_bytes(weight_layout, N, K)),
                       range("wscales", wscales, (size_t)(K / 16) * N),
@@ -328,7 +349,8 @@ int svdq_gemm_w4a4(const void* qact, const void* ascales, const void* lora_act,
   a.y = static_cast<uint16_t*>(y);
   a.M = M; a.N = N; a.K = K; a.R = R;
   a.packed = weight_layout == SVDQ_WEIGHT_PACKED;
-  hipError_t e = svdq::launch_gemm_w4a4(a, static_cast<hipStream_t>(stream));
+  hipError_t e = act_packed ? svdq::launch_gemm_packed(a, static_cast<hipStream_t>(stream))
+                            : svdq::launch_gemm_w4a4(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -358,8 +380,8 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
     const void* ptrs[] = {proj_down};
     if ((st = check_ptrs(names, ptrs, 1))) return st;
   }
-  if ((st = validate_gemm(nullptr, nullptr, nullptr, weight, wscales, weight_layout, wcscales,
-                          wtscale, proj_up, bias, M, N, K, R, y, false)))
+  if ((st = validate_gemm(nullptr, nullptr, SVDQ_ACT_CANONICAL, nullptr, weight, wscales,
+                          weight_layout, wcscales, wtscale, proj_up, bias, M, N, K, R, y, false)))
     return st;
   const LinearWs ws = linear_ws(M, K, R);
   if (workspace_bytes < ws.total)
@@ -377,12 +399,12 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   if ((st = check_alias(in, 9, out, 2))) return st;
 
   char* w = static_cast<char*>(workspace);
-  void* qact = w + ws.qact;
-  void* ascales = w + ws.ascales;
+  const bool packed = weight_layout == SVDQ_WEIGHT_PACKED;
+  void* qact = w + ws.act;
+  void* ascales = packed ? nullptr : (void*)(w + ws.ascales);
   void* lora = R > 0 ? (void*)(w + ws.lora) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora, w + ws.down, s)))
-    return st;
+  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora, packed, s))) return st;
   svdq::GemmArgs a;
   a.qact = static_cast<const uint8_t*>(qact);
   a.ascales = static_cast<const uint8_t*>(ascales);
@@ -395,8 +417,8 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   a.bias = static_cast<const uint16_t*>(bias);
   a.y = static_cast<uint16_t*>(y);
   a.M = M; a.N = N; a.K = K; a.R = R;
-  a.packed = weight_layout == SVDQ_WEIGHT_PACKED;
-  hipError_t e = svdq::launch_gemm_w4a4(a, s);
+  a.packed = packed;
+  hipError_t e = packed ? svdq::launch_gemm_packed(a, s) : svdq::launch_gemm_w4a4(a, s);
   if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -7,24 +7,18 @@
 
 namespace svdq {
 
-// a1: quant(x * smooth) -> qact [M, K/2], ascales [K/16, M]. When `counters`
-// is non-null the first workgroup also zeroes counters[0 .. n_counters) for
-// the down-projection launched after it on the same stream.
+// a1: quant(x * smooth) -> qact [M, K/2], ascales [K/16, M] (canonical layout;
+// the work is laid out for HBM streaming).
 hipError_t launch_quant_act(const uint16_t* x, const uint16_t* smooth, uint8_t* qact,
-                            uint8_t* ascales, int64_t M, int64_t K, unsigned* counters,
-                            int n_counters, hipStream_t stream);
+                            uint8_t* ascales, int64_t M, int64_t K, hipStream_t stream);
 
-// a2: lora_act [M, R] = bf16(x @ proj_down). Split over K across workgroups
-// when M is small; then the workspace holds fp32 partial sums and one
-// arrival counter per 32-row tile (zeroed by launch_quant_act).
-int lora_down_splits(int64_t M, int64_t K, int64_t R);
-int lora_down_counters(int64_t M);
-size_t lora_down_workspace_bytes(int64_t M, int64_t K, int64_t R);
-hipError_t launch_lora_down(const uint16_t* x, const uint16_t* proj_down, uint16_t* lora_act,
-                            void* workspace, int64_t M, int64_t K, int64_t R,
-                            hipStream_t stream);
-// Offset of the counter array inside the down-projection workspace.
-size_t lora_down_counter_offset(int64_t M, int64_t K, int64_t R);
+// a1 + a2 fused: one pass over x gives quant(x * smooth) and
+// lora_act [M, R] = bf16(x @ proj_down) (R may be 0). Output codes/scales in the
+// canonical layout or in the packed fragment layout read by gemm_packed.
+int quant_lora_row_tiles(int64_t M);
+hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down,
+                             uint8_t* qact, uint8_t* ascales, uint16_t* lora_act, int64_t M,
+                             int64_t K, int64_t R, bool packed_out, hipStream_t stream);
 
 // a4 + a5: scaled GEMM, low-rank up-projection and epilogue.
 struct GemmArgs {
@@ -41,9 +35,13 @@ struct GemmArgs {
   int64_t M, N, K, R;
   int packed;
 };
+// canonical activations (LDS-staged), canonical or packed weights
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
+// packed activations (qact holds the packed buffer, ascales unused) and packed weights
+hipError_t launch_gemm_packed(const GemmArgs& a, hipStream_t stream);
 
 // a3: load-time repack of qweight/wscales into the MFMA-order layout, and back.
+// The same chunk layout holds packed activations (rows = tokens).
 size_t packed_weight_bytes(int64_t N, int64_t K);
 hipError_t launch_repack(const uint8_t* qweight, const uint8_t* wscales, uint8_t* packed,
                          int64_t N, int64_t K, hipStream_t stream);

@@ -38,8 +38,7 @@ __device__ __forceinline__ float snap21(float q) {
 
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ smooth,
-    uint8_t* __restrict__ qact, uint8_t* __restrict__ ascales, int M, int K,
-    unsigned* __restrict__ counters, int n_counters) {
+    uint8_t* __restrict__ qact, uint8_t* __restrict__ ascales, int M, int K) {
   __shared__ uint8_t s_scale[kChunk / 16][kRows];
 
   const int tid = threadIdx.x;
@@ -48,10 +47,6 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
   const int m_base = blockIdx.x * kRows;
   const int k0 = blockIdx.y * kChunk + kk * 8;
   const bool k_in = k0 < K;       // both halves of a block agree (K % 16 == 0)
-
-  if (counters != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
-    for (int i = tid; i < n_counters; i += kThreads) counters[i] = 0u;
-  }
 
   float sm[8];
   if (k_in) {
@@ -122,11 +117,10 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 }  // namespace
 
 hipError_t launch_quant_act(const uint16_t* x, const uint16_t* smooth, uint8_t* qact,
-                            uint8_t* ascales, int64_t M, int64_t K, unsigned* counters,
-                            int n_counters, hipStream_t stream) {
+                            uint8_t* ascales, int64_t M, int64_t K, hipStream_t stream) {
   dim3 grid((unsigned)((M + kRows - 1) / kRows), (unsigned)((K + kChunk - 1) / kChunk));
   hipLaunchKernelGGL(quant_act_kernel, grid, dim3(kThreads), 0, stream, x, smooth, qact,
-                     ascales, (int)M, (int)K, counters, n_counters);
+                     ascales, (int)M, (int)K);
   return hipGetLastError();
 }
 

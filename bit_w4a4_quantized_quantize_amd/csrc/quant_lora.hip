@@ -1,0 +1,231 @@
+// Fused activation quantisation and low-rank down-projection: one pass over x
+// produces quant(x * smooth) (codes + e4m3 block scales) and
+// lora_act = bf16(x @ proj_down) (model card "nunchaku-z-image-turbo-svdq",
+// section "What's stored on disk": the activation operand of scaled_mma and
+// the (x @ proj_down) factor of the SVD residual; raw x feeds the residual).
+//
+// A workgroup owns 16*RT rows and the whole K range, so the down-projection
+// needs no cross-workgroup reduction: its 8 waves take interleaved 32-wide K
+// steps and their partial sums are added in a fixed order through LDS at the
+// end (deterministic). Each lane holds 8 consecutive k of one row (a 16-byte
+// load), which is at once the A fragment of v_mfma_f32_16x16x32_bf16 and half
+// of an NVFP4 block; the other half sits in lane ^ 16.
+//
+// proj_down [K, R] is R-contiguous; each lane loads an 8 (k) x 8 (r) block
+// with 16-byte loads and transposes it with byte permutes into 8 B fragments
+// whose column sets are {8c + i}; the output lane layout then gives each lane
+// 8 consecutive r of one row (a 16-byte bf16 store).
+//
+// The code decision follows the same exact scheme as the standalone
+// quantisation kernel (see quant_act.hip): q = v * RN(1/s_d), rounded to 21
+// significant bits, then the hardware E2M1 round-to-nearest-even.
+//
+// Output layouts: canonical (qact [M, K/2], ascales [K/16, M]) or the packed
+// MFMA-fragment layout used by the GEMM (the same chunk order as the packed
+// weights, with rows = tokens): code chunk (p, q) of 1024 bytes at
+// 1024*(p*MP + q), dword (h*32 + c)*4 + t = row 32q + c, k = 64p + 16t + 8h;
+// scale chunk at 1024*KP*MP + 128*(p*MP + q), byte c*4 + t.
+#include "common.h"
+#include "kernels.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRChunk = 128;
+
+__device__ __forceinline__ float snap21(float q) {
+  return __uint_as_float((__float_as_uint(q) + 4u) & ~7u);
+}
+__device__ __forceinline__ uint32_t perm_lo(uint32_t lo_src, uint32_t hi_src) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t perm_hi(uint32_t lo_src, uint32_t hi_src) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, 0x07060302u);
+}
+
+struct QLArgs {
+  const uint16_t* x;
+  const uint16_t* smooth;
+  const uint16_t* proj_down;
+  uint8_t* qact;       // canonical [M, K/2] or the packed buffer
+  uint8_t* ascales;    // canonical [K/16, M] (unused when packed)
+  uint16_t* lora_act;  // [M, R]
+  int M, K, R;
+};
+
+template <int RT, bool PACKED>
+__global__ __launch_bounds__(kThreads) void quant_lora_kernel(QLArgs a) {
+  constexpr int ROWS = 16 * RT;
+  __shared__ f32x4 s_red[kWaves / 2][RT][8][64];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 15;   // row within a 16-row tile; column group of proj_down
+  const int g = lane >> 4;   // k group of 8 within a 32-wide step
+  const int m0 = blockIdx.x * ROWS;
+  const int M = a.M, K = a.K, R = a.R;
+  const int MP = (M + 31) / 32;
+  const int KP = (K + 63) / 64;
+  // packed output covers whole 64-wide panels: positions beyond K get zero codes
+  // and zero scales (the GEMM multiplies them by the weight's zero padding)
+  const int steps = PACKED ? 2 * KP : (K + 31) / 32;
+  const size_t code_bytes = (size_t)MP * KP * 1024;
+
+  const int n_chunks = R > 0 ? (R + kRChunk - 1) / kRChunk : 1;
+  for (int rc_i = 0; rc_i < n_chunks; ++rc_i) {
+    const bool do_quant = rc_i == 0;
+    const int r_base = rc_i * kRChunk;
+    const int rcol = r_base + 8 * c;
+    const bool r_in = rcol < R;
+
+    f32x4 acc[RT][8];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int st = wave; st < steps; st += kWaves) {
+      const int kg = st * 32 + 8 * g;
+      const bool k_in = kg < K;
+      u32x4 xw[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int m = m0 + 16 * t + c;
+        xw[t] = zero4();
+        if (k_in && m < M) xw[t] = *reinterpret_cast<const u32x4*>(a.x + (size_t)m * K + kg);
+      }
+      u32x4 p[8];
+      if (R > 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = zero4();
+          if (r_in && kg + j < K)
+            p[j] = *reinterpret_cast<const u32x4*>(a.proj_down + (size_t)(kg + j) * R + rcol);
+        }
+      }
+
+      if (do_quant) {
+        float sm[8];
+        u32x4 s4 = zero4();
+        if (k_in) s4 = *reinterpret_cast<const u32x4*>(a.smooth + kg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sm[2 * j] = bf16lo_to_f32(s4[j]);
+          sm[2 * j + 1] = bf16hi_to_f32(s4[j]);
+        }
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const int m = m0 + 16 * t + c;
+          float v[8];
+          float amax = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bf16lo_to_f32(xw[t][j]) * sm[2 * j];
+            v[2 * j + 1] = bf16hi_to_f32(xw[t][j]) * sm[2 * j + 1];
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16));   // other half of the block
+          const uint32_t sc = f32_to_e4m3_sat(__fdiv_rn(amax, 6.0f));
+          const float sd = e4m3_to_f32(sc, 0);
+          const float inv = sd > 0.0f ? __fdiv_rn(1.0f, sd) : 0.0f;
+          uint32_t packed = 0u;
+          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[0] * inv), snap21(v[1] * inv), 1.0f, 0);
+          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[2] * inv), snap21(v[3] * inv), 1.0f, 1);
+          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[4] * inv), snap21(v[5] * inv), 1.0f, 2);
+          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[6] * inv), snap21(v[7] * inv), 1.0f, 3);
+          if (m < M && (PACKED || k_in)) {
+            if (PACKED) {
+              const int pp = kg >> 6, tt = (kg >> 4) & 3, hh = (kg >> 3) & 1;
+              const int q = m >> 5, cc = m & 31;
+              const size_t chunk = (size_t)pp * MP + q;
+              *reinterpret_cast<uint32_t*>(a.qact + chunk * 1024 + ((hh * 32 + cc) * 4 + tt) * 4) = packed;
+              if (hh == 0) a.qact[code_bytes + chunk * 128 + cc * 4 + tt] = (uint8_t)sc;
+            } else {
+              *reinterpret_cast<uint32_t*>(a.qact + (size_t)m * (K / 2) + kg / 2) = packed;
+              if ((g & 1) == 0) a.ascales[(size_t)(kg >> 4) * M + m] = (uint8_t)sc;
+            }
+          }
+        }
+      }
+
+      if (R > 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          u32x4 f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            f[q] = (i & 1) ? perm_hi(p[2 * q][i >> 1], p[2 * q + 1][i >> 1])
+                           : perm_lo(p[2 * q][i >> 1], p[2 * q + 1][i >> 1]);
+          const bf16x8 b = __builtin_bit_cast(bf16x8, f);
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xw[t]), b,
+                                                                acc[t][i], 0, 0, 0);
+        }
+      }
+    }
+
+    if (R > 0) {
+      // fixed-order tree over the 8 waves: 4+..→0..3, 2,3→0,1, 1→0
+#pragma unroll
+      for (int half = kWaves / 2; half >= 1; half >>= 1) {
+        __syncthreads();
+        if (wave >= half && wave < 2 * half) {
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s_red[wave - half][t][i][lane] = acc[t][i];
+        }
+        __syncthreads();
+        if (wave < half) {
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[t][i] += s_red[wave][t][i][lane];
+        }
+      }
+      if (wave == 0 && r_in) {
+        // lane holds rows 16t + 4g + q and columns rcol .. rcol+7
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int m = m0 + 16 * t + 4 * g + q;
+            if (m < M) {
+              u32x4 o;
+#pragma unroll
+              for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(acc[t][2 * w][q], acc[t][2 * w + 1][q]);
+              *reinterpret_cast<u32x4*>(a.lora_act + (size_t)m * R + rcol) = o;
+            }
+          }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int quant_lora_row_tiles(int64_t M) { return (M + 31) / 32 >= 256 ? 2 : 1; }
+
+hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down,
+                             uint8_t* qact, uint8_t* ascales, uint16_t* lora_act, int64_t M,
+                             int64_t K, int64_t R, bool packed_out, hipStream_t stream) {
+  QLArgs a{x, smooth, proj_down, qact, ascales, lora_act, (int)M, (int)K, (int)R};
+  const int rt = quant_lora_row_tiles(M);
+  dim3 grid((unsigned)((M + 16 * rt - 1) / (16 * rt)));
+  if (rt == 2) {
+    if (packed_out) hipLaunchKernelGGL((quant_lora_kernel<2, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((quant_lora_kernel<2, false>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (packed_out) hipLaunchKernelGGL((quant_lora_kernel<1, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((quant_lora_kernel<1, false>), grid, dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svdq

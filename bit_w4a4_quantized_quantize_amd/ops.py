@@ -17,7 +17,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import WEIGHT_CANONICAL, WEIGHT_PACKED, SvdqError  # noqa: F401
+from ._lib import ACT_CANONICAL, ACT_PACKED, WEIGHT_CANONICAL, WEIGHT_PACKED, SvdqError  # noqa: F401
 
 
 def _bytes(t):
@@ -48,10 +48,12 @@ def _stream(device=None):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=None):
+def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=None, packed=False):
     """quant(x * smooth) and, with proj_down, lora_act = x @ proj_down.
 
-    Returns (qact uint8 [M, K/2], ascales uint8 [K/16, M], lora_act bf16 [M, R] or None).
+    Returns (qact, ascales, lora_act): canonical qact uint8 [M, K/2] and ascales
+    uint8 [K/16, M]; or, with packed=True, one packed uint8 buffer (the packed
+    weight layout with rows = tokens) and ascales None. lora_act bf16 [M, R] or None.
     """
     _need(x, "x", torch.bfloat16, 2)
     M, K = x.shape
@@ -61,18 +63,22 @@ def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=No
         _need(proj_down, "proj_down", torch.bfloat16, 2)
         R = proj_down.shape[1]
     dev = x.device
-    if qact is None:
-        qact = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-    if ascales is None:
-        ascales = torch.empty((K // 16, M), dtype=torch.uint8, device=dev)
+    L = _lib.lib()
+    if packed:
+        nbytes = L.svdq_packed_act_bytes(M, K)
+        if qact is None:
+            qact = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        ascales = None
+    else:
+        if qact is None:
+            qact = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        if ascales is None:
+            ascales = torch.empty((K // 16, M), dtype=torch.uint8, device=dev)
     if R > 0 and lora_act is None:
         lora_act = torch.empty((M, R), dtype=torch.bfloat16, device=dev)
-    L = _lib.lib()
-    ws_bytes = L.svdq_quantize_act_workspace_bytes(M, K, R)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
     _lib.check("svdq_quantize_act", L.svdq_quantize_act(
-        _p(x), _p(smooth), M, K, _p(proj_down), R, _p(qact), _p(ascales),
-        _p(lora_act) if R > 0 else None, _p(ws), ws_bytes, _stream(dev)))
+        _p(x), _p(smooth), M, K, _p(proj_down), R, ACT_PACKED if packed else ACT_CANONICAL,
+        _p(qact), _p(ascales), _p(lora_act) if R > 0 else None, None, 0, _stream(dev)))
     return qact, ascales, (lora_act if R > 0 else None)
 
 
@@ -148,19 +154,31 @@ def _check_layer(w: SVDQLinearWeights):
         _need(w.bias, "bias", torch.bfloat16, 1)
 
 
-def gemm_w4a4(qact, ascales, lora_act, w: SVDQLinearWeights, y=None):
-    """The scaled GEMM + low-rank up-projection + epilogue from quantised activations."""
+def gemm_w4a4(qact, ascales, lora_act, w: SVDQLinearWeights, y=None, M=None):
+    """The scaled GEMM + low-rank up-projection + epilogue from quantised activations.
+
+    Canonical activations: qact [M, K/2], ascales [K/16, M]. Packed activations
+    (from quantize_act(..., packed=True)): qact is the packed buffer, ascales
+    None, and M must be given; the layer's weight must be packed too.
+    """
     _check_layer(w)
-    _need(qact, "qact", torch.uint8, 2)
-    _need(ascales, "ascales", torch.uint8, 2)
-    M = qact.shape[0]
+    act_packed = ascales is None
+    if act_packed:
+        _need(qact, "qact (packed)", torch.uint8, 1)
+        if M is None:
+            raise ValueError("M is required with packed activations")
+    else:
+        _need(qact, "qact", torch.uint8, 2)
+        _need(ascales, "ascales", torch.uint8, 2)
+        M = qact.shape[0]
     if w.R > 0:
         _need(lora_act, "lora_act", torch.bfloat16, 2)
     if y is None:
         y = torch.empty((M, w.N), dtype=torch.bfloat16, device=qact.device)
     L = _lib.lib()
     _lib.check("svdq_gemm_w4a4", L.svdq_gemm_w4a4(
-        _p(qact), _p(ascales), _p(lora_act) if w.R > 0 else None,
+        _p(qact), _p(ascales), ACT_PACKED if act_packed else ACT_CANONICAL,
+        _p(lora_act) if w.R > 0 else None,
         _p(_bytes(w.weight)), _p(_bytes(w.wscales)) if w.wscales is not None else None, w.layout,
         _p(w.wcscales), _p(w.wtscale), _p(w.proj_up) if w.R > 0 else None, _p(w.bias),
         M, w.N, w.K, w.R, _p(y), _stream(qact.device)))

@@ -75,6 +75,15 @@ enum {
   SVDQ_WEIGHT_PACKED = 1     /* one buffer from svdq_repack_weight; wscales must be NULL    */
 };
 
+/* Layouts of quantised activations (codes + scales).                                     */
+enum {
+  SVDQ_ACT_CANONICAL = 0,    /* qact [M, K/2] + ascales [K/16, M]                            */
+  SVDQ_ACT_PACKED = 1        /* one buffer of svdq_packed_act_bytes(M, K) in the packed
+                                weight layout with rows = tokens; ascales must be NULL.
+                                Rows beyond M in the last 32-row panel are unspecified;
+                                positions beyond K are zero.                               */
+};
+
 #define SVDQ_ABI_VERSION 1
 
 int svdq_abi_version(void);
@@ -88,17 +97,20 @@ const char* svdq_last_error(void);
  * the activation operand of scaled_mma and the (x @ proj_down) factor).
  *
  *   x [M, K] bf16, smooth [K] bf16          inputs
- *   qact [M, K/2] u8, ascales [K/16, M] u8  outputs (rule in the file header)
+ *   act_layout SVDQ_ACT_CANONICAL: qact [M, K/2] u8, ascales [K/16, M] u8;
+ *              SVDQ_ACT_PACKED: qact = packed buffer (svdq_packed_act_bytes(M, K)
+ *              bytes), ascales NULL. Outputs follow the rule in the file header.
  *   proj_down [K, R] bf16, lora_act [M, R] bf16: used when R > 0 (both
  *     required then); lora_act = bf16(x @ proj_down) with fp32 accumulation.
  *   workspace: device scratch of at least svdq_quantize_act_workspace_bytes(M, K, R)
- *     bytes (may be NULL when that size is 0); its contents need no
- *     initialisation and are garbage afterwards.
+ *     bytes; the fused kernel needs none, so that size is 0 and workspace may
+ *     be NULL (the argument keeps the signature stable).
  * qact and ascales are bit-exact functions of x and smooth.
  */
 size_t svdq_quantize_act_workspace_bytes(int64_t M, int64_t K, int64_t R);
+size_t svdq_packed_act_bytes(int64_t M, int64_t K);
 int svdq_quantize_act(const void* x, const void* smooth, int64_t M, int64_t K,
-                      const void* proj_down, int64_t R,
+                      const void* proj_down, int64_t R, int act_layout,
                       void* qact, void* ascales, void* lora_act,
                       void* workspace, size_t workspace_bytes, void* stream);
 
@@ -133,7 +145,9 @@ int svdq_unpack_weight(const void* packed, size_t packed_bytes, int64_t N, int64
  *   y = bf16( scaled_mma(qact, weight, ascales, wscales) * wtscale * wcscales[n]
  *             + lora_act @ proj_up^T + bias[n] )
  *
- *   qact [M, K/2] u8, ascales [K/16, M] u8, lora_act [M, R] bf16 (R > 0)
+ *   qact [M, K/2] u8 + ascales [K/16, M] u8 (act_layout SVDQ_ACT_CANONICAL), or
+ *     a packed activation buffer with ascales NULL (SVDQ_ACT_PACKED; needs
+ *     SVDQ_WEIGHT_PACKED weights); lora_act [M, R] bf16 (R > 0)
  *   weight: qweight [N, K/2] (SVDQ_WEIGHT_CANONICAL, wscales [K/16, N] given)
  *           or a packed buffer (SVDQ_WEIGHT_PACKED, wscales NULL)
  *   wcscales [N] bf16, wtscale [1] bf16, proj_up [N, R] bf16 (R > 0), bias [N] bf16 or NULL
@@ -142,14 +156,15 @@ int svdq_unpack_weight(const void* packed, size_t packed_bytes, int64_t N, int64
  * f16 and multiplied on the matrix cores with fp32 accumulation); the sum
  * over blocks and the epilogue round in fp32.
  */
-int svdq_gemm_w4a4(const void* qact, const void* ascales, const void* lora_act,
+int svdq_gemm_w4a4(const void* qact, const void* ascales, int act_layout, const void* lora_act,
                    const void* weight, const void* wscales, int weight_layout,
                    const void* wcscales, const void* wtscale, const void* proj_up,
                    const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
                    void* y, void* stream);
 
 /*
- * The whole layer: svdq_quantize_act into the workspace, then svdq_gemm_w4a4.
+ * The whole layer: svdq_quantize_act into the workspace, then svdq_gemm_w4a4
+ * (activations packed in the workspace when the weight is packed).
  *   x [M, K] bf16, smooth [K] bf16, weight/wscales/weight_layout as above,
  *   wcscales, wtscale, proj_down [K, R], proj_up [N, R], bias (or NULL),
  *   y [M, N] bf16; workspace of at least svdq_linear_workspace_bytes(M, N, K, R)

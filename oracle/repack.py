@@ -32,7 +32,43 @@ def packed_bytes(N, K):
 
 
 def repack(qweight, wscales):
-    """qweight [N, K/2] uint8, wscales [K/16, N] uint8 -> packed uint8 buffer."""
+    """qweight [N, K/2] uint8, wscales [K/16, N] uint8 -> packed uint8 buffer.
+
+    Array form of the index map: pad to whole panels with zeros, then read the
+    byte axis of a row as (p, t, h, byte) since k/2 = 32p + 8t + 4h + byte, and
+    order the code bytes as [p, q, h, c, t, byte], the scales as [p, q, c, t].
+    (repack_loops states the same map element by element.)
+    """
+    qweight = np.asarray(qweight, dtype=np.uint8)
+    wscales = np.asarray(wscales, dtype=np.uint8)
+    N, Kh = qweight.shape
+    K = 2 * Kh
+    NP = -(-N // PANEL_N)
+    KP = -(-K // PANEL_K)
+    qw = np.zeros((NP * 32, KP * 32), dtype=np.uint8)
+    qw[:N, :Kh] = qweight
+    ws = np.zeros((KP * 4, NP * 32), dtype=np.uint8)
+    ws[:K // 16, :N] = wscales
+    codes = qw.reshape(NP, 32, KP, 4, 2, 4).transpose(2, 0, 4, 1, 3, 5)   # [p, q, h, c, t, byte]
+    scales = ws.reshape(KP, 4, NP, 32).transpose(0, 2, 3, 1)              # [p, q, c, t]
+    return np.concatenate([codes.ravel(), scales.ravel()])
+
+
+def unpack(packed, N, K):
+    """Inverse of repack: packed buffer -> (qweight [N, K/2], wscales [K/16, N])."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    NP = -(-N // PANEL_N)
+    KP = -(-K // PANEL_K)
+    nc = NP * KP * 1024
+    codes = packed[:nc].reshape(KP, NP, 2, 32, 4, 4).transpose(1, 3, 0, 4, 2, 5)  # [q, c, p, t, h, byte]
+    scales = packed[nc:nc + NP * KP * 128].reshape(KP, NP, 32, 4).transpose(0, 3, 1, 2)  # [p, t, q, c]
+    qweight = codes.reshape(NP * 32, KP * 32)[:N, :K // 2]
+    wscales = scales.reshape(KP * 4, NP * 32)[:K // 16, :N]
+    return np.ascontiguousarray(qweight), np.ascontiguousarray(wscales)
+
+
+def repack_loops(qweight, wscales):
+    """The same map written element by element (used to pin the array form)."""
     qweight = np.asarray(qweight, dtype=np.uint8)
     wscales = np.asarray(wscales, dtype=np.uint8)
     N, Kh = qweight.shape
@@ -62,8 +98,8 @@ def repack(qweight, wscales):
     return out
 
 
-def unpack(packed, N, K):
-    """Inverse of repack: packed buffer -> (qweight [N, K/2], wscales [K/16, N])."""
+def unpack_loops(packed, N, K):
+    """Inverse of repack_loops, element by element."""
     packed = np.asarray(packed, dtype=np.uint8)
     NP = -(-N // PANEL_N)
     KP = -(-K // PANEL_K)

@@ -68,11 +68,11 @@ def fake(i):
 def q(**kw):
     args = dict(x=fake(1), smooth=fake(2), M=64, K=256, proj_down=fake(3), R=16,
                 qact=fake(4), ascales=fake(5), lora_act=fake(6), ws=fake(7), ws_bytes=1 << 30,
-                stream=None)
+                layout=0, stream=None)
     args.update(kw)
     L = _lib.lib()
     return L.svdq_quantize_act(args["x"], args["smooth"], args["M"], args["K"], args["proj_down"],
-                               args["R"], args["qact"], args["ascales"], args["lora_act"],
+                               args["R"], args["layout"], args["qact"], args["ascales"], args["lora_act"],
                                args["ws"], args["ws_bytes"], args["stream"])
 
 
@@ -84,20 +84,18 @@ def q(**kw):
     (dict(proj_down=None), 1), (dict(lora_act=None), 1),
     (dict(x=fake(1) + 8), 4), (dict(ascales=fake(5) + 4), 4),
     (dict(qact=fake(1) + 64), 6), (dict(lora_act=fake(3)), 6), (dict(ascales=fake(4)), 6),
+    (dict(layout=2), 8), (dict(layout=1), 8),           # packed needs ascales NULL
+    (dict(layout=1, ascales=None, qact=fake(2) - 1024 * 4), 6),
 ])
 def test_quantize_act_rejections(kw, code):
     assert q(**kw) == code
     assert _lib.lib().svdq_last_error().decode() != ""
 
 
-@no_gpu_only
-def test_quantize_act_workspace_checks():
+def test_quantize_act_needs_no_workspace():
     L = _lib.lib()
-    need = L.svdq_quantize_act_workspace_bytes(4096, 3840, 128)
-    assert need > 0
-    assert q(M=4096, K=3840, R=128, ws_bytes=need - 1) == 5
-    assert q(M=4096, K=3840, R=128, ws=None) == 1
-    assert q(M=4096, K=3840, R=128, ws=fake(7) + 8) == 4
+    for M, K, R in [(4096, 3840, 128), (64, 256, 16), (16896, 10240, 128), (7, 16, 0)]:
+        assert L.svdq_quantize_act_workspace_bytes(M, K, R) == 0
 
 
 @no_gpu_only
@@ -106,12 +104,13 @@ def test_empty_problem_is_ok_without_pointers():
 
 
 def gemm(**kw):
-    args = dict(qact=fake(1), ascales=fake(2), lora=fake(3), weight=fake(4), wscales=fake(5), layout=0,
-                wcscales=fake(6), wtscale=fake(7), proj_up=fake(8), bias=fake(9),
+    args = dict(qact=fake(1), ascales=fake(2), act_layout=0, lora=fake(3), weight=fake(4), wscales=fake(5),
+                layout=0, wcscales=fake(6), wtscale=fake(7), proj_up=fake(8), bias=fake(9),
                 M=64, N=128, K=256, R=16, y=fake(10), stream=None)
     args.update(kw)
     L = _lib.lib()
-    return L.svdq_gemm_w4a4(args["qact"], args["ascales"], args["lora"], args["weight"], args["wscales"],
+    return L.svdq_gemm_w4a4(args["qact"], args["ascales"], args["act_layout"], args["lora"], args["weight"],
+                            args["wscales"],
                             args["layout"], args["wcscales"], args["wtscale"], args["proj_up"],
                             args["bias"], args["M"], args["N"], args["K"], args["R"], args["y"],
                             args["stream"])
@@ -124,6 +123,9 @@ def gemm(**kw):
     (dict(qact=None), 1), (dict(y=None), 1), (dict(wtscale=None), 1), (dict(proj_up=None), 1),
     (dict(lora=None), 1), (dict(bias=fake(9) + 2), 4), (dict(weight=fake(4) + 1), 4),
     (dict(y=fake(1)), 6), (dict(y=fake(6) - 64), 6),
+    (dict(act_layout=3), 8), (dict(act_layout=1), 8),                         # ascales must be NULL
+    (dict(act_layout=1, ascales=None), 8),                                     # needs packed weights
+    (dict(act_layout=1, ascales=None, layout=1, wscales=None, qact=None), 1),
 ])
 def test_gemm_rejections(kw, code):
     assert gemm(**kw) == code

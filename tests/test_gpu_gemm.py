@@ -103,3 +103,43 @@ def test_gemm_deterministic(gpu_lib):
     a, _ = gemm_case(gpu_lib, cfg)
     b, _ = gemm_case(gpu_lib, cfg)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(M=64, K=256, N=128, R=16, kind="tiny", seed=1001),
+    dict(M=200, K=3840, N=384, R=128, kind="dit", seed=21),
+    dict(M=130, K=336, N=4100, R=32, kind="dit", seed=24),
+    dict(M=257, K=1024, N=257, R=0, kind="dit", seed=25),
+])
+def test_gemm_packed_activations(gpu_lib, cfg):
+    """Packed activations (placed by the oracle's statement of the layout) through the
+    LDS-free kernel: within tolerance of the oracle and bit-identical to the
+    canonical-activation kernel on the same operands."""
+    from oracle import repack as P
+    d, layer, qact, ascales, lora_bits = _oracle_inputs(cfg, True, False)
+    R = d["R"]
+    pl = layer.packed()
+    lora = dev_bf16(lora_bits) if R > 0 else None
+    y_pk = gpu_lib.gemm_w4a4(dev_u8(P.repack(qact, ascales)), None, lora, pl, M=d["M"])
+    y_can = gpu_lib.gemm_w4a4(dev_u8(qact), dev_u8(ascales), lora, pl)
+    torch.cuda.synchronize()
+    a, b = host_bits(y_pk), host_bits(y_can)
+    assert np.array_equal(a, b)
+    y64 = S.gemm_w4a4(qact, ascales, F.bf16_to_f64(lora_bits) if R > 0 else None, d["qweight"],
+                      d["wscales"], d["wcscales"], d["wtscale"], d["proj_up"] if R > 0 else None, d["bias"])
+    assert S.normwise_rel_err(F.bf16_to_f64(a), y64) <= TOL
+
+
+def test_gemm_packed_full_ffn_shape_sampled_rows(gpu_lib):
+    from oracle import repack as P
+    cfg = workloads.FFN_W1_1024
+    d, layer, qact, ascales, lora_bits = _oracle_inputs(cfg, True, False)
+    y = gpu_lib.gemm_w4a4(dev_u8(P.repack(qact, ascales)), None, dev_bf16(lora_bits), layer.packed(),
+                          M=d["M"])
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(6).choice(cfg["M"], size=40, replace=False))
+    y64 = S.gemm_w4a4(qact[rows], ascales[:, rows], F.bf16_to_f64(lora_bits)[rows], d["qweight"],
+                      d["wscales"], d["wcscales"], d["wtscale"], d["proj_up"], d["bias"])
+    got = host_bits(y)[rows]
+    assert S.normwise_rel_err(F.bf16_to_f64(got), y64) <= TOL
+    assert within_ulps(got, y64, 1).mean() >= 0.999

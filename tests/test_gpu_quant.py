@@ -130,3 +130,53 @@ def test_quant_empty(gpu_lib):
     sm = torch.ones(256, dtype=torch.bfloat16, device="cuda")
     qact, ascales, lora = gpu_lib.quantize_act(x, sm)
     assert qact.shape == (0, 128) and ascales.shape == (16, 0) and lora is None
+
+
+def _unspecified_rows_mask(M, K):
+    """Bytes of a packed activation buffer that belong to rows >= M (left unspecified)."""
+    from oracle import repack as P
+    MP, KP = -(-M // 32), -(-K // 64)
+    total = P.packed_bytes(M, K)
+    mask = np.zeros(total, dtype=bool)
+    d = np.arange(256)
+    c_of_dword = (d // 4) % 32
+    for q in range(MP):
+        bad_c = 32 * q + np.arange(32) >= M
+        if not bad_c.any():
+            continue
+        for p in range(KP):
+            base = 1024 * (p * MP + q)
+            rows_bad = bad_c[c_of_dword]
+            for k in range(4):
+                mask[base + 4 * d[rows_bad] + k] = True
+            sbase = 1024 * KP * MP + 128 * (p * MP + q)
+            for b in range(128):
+                if bad_c[b // 4]:
+                    mask[sbase + b] = True
+    return mask
+
+
+@pytest.mark.parametrize("M,K,R,kind,seed", [
+    (64, 256, 16, "tiny", 1001),
+    (77, 336, 32, "dit", 51),        # ragged M, K % 64 == 16
+    (600, 3840, 128, "dit", 52),
+    (96, 10240, 128, "swiglu", 53),
+])
+def test_quant_packed_layout_bit_exact(gpu_lib, M, K, R, kind, seed):
+    """Packed activation output == the oracle's codes/scales placed by the oracle's
+    own statement of the packed layout (zero beyond K; rows beyond M unspecified)."""
+    from oracle import repack as P
+    d = workloads.make_linear(M, K, 16, R, kind=kind, seed=seed, with_bias=False)
+    buf, asc, lora = gpu_lib.quantize_act(dev_bf16(d["x"]), dev_bf16(d["smooth"]),
+                                          dev_bf16(d["proj_down"]) if R > 0 else None, packed=True)
+    torch.cuda.synchronize()
+    assert asc is None
+    got = host_u8(buf)
+    q_ref, s_ref = S.quantize_act(d["x"], d["smooth"])
+    expect = P.repack(q_ref, s_ref)
+    assert got.size == expect.size
+    keep = ~_unspecified_rows_mask(M, K)
+    bad = np.argwhere((got != expect) & keep)
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:4].ravel().tolist()}"
+    q2, s2 = P.unpack(got, M, K)
+    assert np.array_equal(q2, q_ref) and np.array_equal(s2, s_ref)

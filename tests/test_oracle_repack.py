@@ -16,6 +16,10 @@ def test_round_trip_and_bijection(N, K):
     assert packed.size == P.packed_bytes(N, K)
     q2, w2 = P.unpack(packed, N, K)
     assert np.array_equal(q2, qw) and np.array_equal(w2, ws)
+    # the array form and the element-by-element form state the same map
+    assert np.array_equal(P.repack_loops(qw, ws), packed)
+    q3, w3 = P.unpack_loops(packed, N, K)
+    assert np.array_equal(q3, qw) and np.array_equal(w3, ws)
     # every canonical byte appears exactly once, padding is zero
     pad = packed.size - qw.size - ws.size
     assert np.array_equal(np.sort(packed), np.sort(np.concatenate([qw.ravel(), ws.ravel(), np.zeros(pad, np.uint8)])))
