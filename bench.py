@@ -210,7 +210,7 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
     tflops = flops_linear / (ms_per_step * 1e-3) / 1e12
     print(f"[bench] linear: {ms_per_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s "
-          f"(wall {wall * 1e3 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
+          f"(wall {wall * 1e6 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
 
     # ---- per-kernel timings, same stream and rotation, the kernels the step runs ----
     packed = args.layout == "packed"

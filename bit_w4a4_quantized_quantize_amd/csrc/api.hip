@@ -349,7 +349,7 @@ int svdq_gemm_w4a4(const void* qact, const void* ascales, int act_layout, const 
   a.y = static_cast<uint16_t*>(y);
   a.M = M; a.N = N; a.K = K; a.R = R;
   a.packed = weight_layout == SVDQ_WEIGHT_PACKED;
-  hipError_t e = act_packed ? svdq::launch_gemm_packed(a, static_cast<hipStream_t>(stream))
+  hipError_t e = act_packed ? svdq::launch_gemm_lds(a, static_cast<hipStream_t>(stream))
                             : svdq::launch_gemm_w4a4(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return ok();
@@ -418,7 +418,7 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   a.y = static_cast<uint16_t*>(y);
   a.M = M; a.N = N; a.K = K; a.R = R;
   a.packed = packed;
-  hipError_t e = packed ? svdq::launch_gemm_packed(a, s) : svdq::launch_gemm_w4a4(a, s);
+  hipError_t e = packed ? svdq::launch_gemm_lds(a, s) : svdq::launch_gemm_w4a4(a, s);
   if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -37,8 +37,11 @@ struct GemmArgs {
 };
 // canonical activations (LDS-staged), canonical or packed weights
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
-// packed activations (qact holds the packed buffer, ascales unused) and packed weights
+// packed activations (qact holds the packed buffer, ascales unused) and packed weights:
+// per-wave register dequantisation (gemm_packed.hip) ...
 hipError_t launch_gemm_packed(const GemmArgs& a, hipStream_t stream);
+// ... or dequantisation once per workgroup into LDS (gemm_lds.hip), the default
+hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream);
 
 // a3: load-time repack of qweight/wscales into the MFMA-order layout, and back.
 // The same chunk layout holds packed activations (rows = tokens).

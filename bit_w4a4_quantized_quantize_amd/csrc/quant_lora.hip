@@ -5,9 +5,10 @@
 // the (x @ proj_down) factor of the SVD residual; raw x feeds the residual).
 //
 // A workgroup owns 16*RT rows and the whole K range, so the down-projection
-// needs no cross-workgroup reduction: its 8 waves take interleaved 32-wide K
-// steps and their partial sums are added in a fixed order through LDS at the
-// end (deterministic). Each lane holds 8 consecutive k of one row (a 16-byte
+// needs no cross-workgroup reduction: its waves take interleaved 32-wide K
+// steps (loading the next step's operands while working on the current one)
+// and their partial sums are added in a fixed order through LDS at the end
+// (deterministic). Each lane holds 8 consecutive k of one row (a 16-byte
 // load), which is at once the A fragment of v_mfma_f32_16x16x32_bf16 and half
 // of an NVFP4 block; the other half sits in lane ^ 16.
 //
@@ -32,8 +33,6 @@ namespace svdq {
 
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRChunk = 128;
 
 __device__ __forceinline__ float snap21(float q) {
@@ -46,6 +45,13 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t lo_src, uint32_t hi_src) {
   return __builtin_amdgcn_perm(hi_src, lo_src, 0x07060302u);
 }
 
+template <int RT>
+struct StepRegs {
+  u32x4 x[RT];   // 8 consecutive k of this lane's row(s)
+  u32x4 sm;      // smooth at the same 8 k
+  u32x4 p[8];    // proj_down rows kg .. kg+7, columns rcol .. rcol+7
+};
+
 struct QLArgs {
   const uint16_t* x;
   const uint16_t* smooth;
@@ -56,8 +62,8 @@ struct QLArgs {
   int M, K, R;
 };
 
-template <int RT, bool PACKED>
-__global__ __launch_bounds__(kThreads) void quant_lora_kernel(QLArgs a) {
+template <int RT, int kWaves, bool PACKED>
+__global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
   constexpr int ROWS = 16 * RT;
   __shared__ f32x4 s_red[kWaves / 2][RT][8][64];
 
@@ -88,34 +94,44 @@ __global__ __launch_bounds__(kThreads) void quant_lora_kernel(QLArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int st = wave; st < steps; st += kWaves) {
+    // software pipeline: the operands of this wave's next step load while
+    // the current step is quantised and multiplied
+    auto load = [&](StepRegs<RT>& r, int st) {
       const int kg = st * 32 + 8 * g;
-      const bool k_in = kg < K;
-      u32x4 xw[RT];
+      const bool k_in = st < steps && kg < K;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int m = m0 + 16 * t + c;
-        xw[t] = zero4();
-        if (k_in && m < M) xw[t] = *reinterpret_cast<const u32x4*>(a.x + (size_t)m * K + kg);
+        r.x[t] = zero4();
+        if (k_in && m < M) r.x[t] = *reinterpret_cast<const u32x4*>(a.x + (size_t)m * K + kg);
       }
-      u32x4 p[8];
+      r.sm = zero4();
+      if (do_quant && k_in) r.sm = *reinterpret_cast<const u32x4*>(a.smooth + kg);
       if (R > 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p[j] = zero4();
-          if (r_in && kg + j < K)
-            p[j] = *reinterpret_cast<const u32x4*>(a.proj_down + (size_t)(kg + j) * R + rcol);
+          r.p[j] = zero4();
+          if (r_in && k_in && kg + j < K)
+            r.p[j] = *reinterpret_cast<const u32x4*>(a.proj_down + (size_t)(kg + j) * R + rcol);
         }
       }
+    };
+
+    StepRegs<RT> cur, nxt;
+    load(cur, wave);
+    for (int st = wave; st < steps; st += kWaves) {
+      load(nxt, st + kWaves);
+      const int kg = st * 32 + 8 * g;
+      const bool k_in = kg < K;
+      const u32x4* xw = cur.x;
+      const u32x4* p = cur.p;
 
       if (do_quant) {
         float sm[8];
-        u32x4 s4 = zero4();
-        if (k_in) s4 = *reinterpret_cast<const u32x4*>(a.smooth + kg);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          sm[2 * j] = bf16lo_to_f32(s4[j]);
-          sm[2 * j + 1] = bf16hi_to_f32(s4[j]);
+          sm[2 * j] = bf16lo_to_f32(cur.sm[j]);
+          sm[2 * j + 1] = bf16hi_to_f32(cur.sm[j]);
         }
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
@@ -168,10 +184,11 @@ __global__ __launch_bounds__(kThreads) void quant_lora_kernel(QLArgs a) {
                                                                 acc[t][i], 0, 0, 0);
         }
       }
+      cur = nxt;
     }
 
     if (R > 0) {
-      // fixed-order tree over the 8 waves: 4+..→0..3, 2,3→0,1, 1→0
+      // fixed-order tree over the waves (8: 4..7 -> 0..3, 2,3 -> 0,1, 1 -> 0)
 #pragma unroll
       for (int half = kWaves / 2; half >= 1; half >>= 1) {
         __syncthreads();
@@ -218,12 +235,14 @@ hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const ui
   QLArgs a{x, smooth, proj_down, qact, ascales, lora_act, (int)M, (int)K, (int)R};
   const int rt = quant_lora_row_tiles(M);
   dim3 grid((unsigned)((M + 16 * rt - 1) / (16 * rt)));
+  // 16 rows: 8 waves per workgroup (2 per SIMD); 32 rows: 4 waves, so each wave
+  // may hold two row tiles of operands and accumulators in registers
   if (rt == 2) {
-    if (packed_out) hipLaunchKernelGGL((quant_lora_kernel<2, true>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((quant_lora_kernel<2, false>), grid, dim3(kThreads), 0, stream, a);
+    if (packed_out) hipLaunchKernelGGL((quant_lora_kernel<2, 4, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((quant_lora_kernel<2, 4, false>), grid, dim3(256), 0, stream, a);
   } else {
-    if (packed_out) hipLaunchKernelGGL((quant_lora_kernel<1, true>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((quant_lora_kernel<1, false>), grid, dim3(kThreads), 0, stream, a);
+    if (packed_out) hipLaunchKernelGGL((quant_lora_kernel<1, 8, true>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((quant_lora_kernel<1, 8, false>), grid, dim3(512), 0, stream, a);
   }
   return hipGetLastError();
 }
