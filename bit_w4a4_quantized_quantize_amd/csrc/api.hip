@@ -72,6 +72,17 @@ int check_mk(int64_t M, int64_t K, int64_t R) {
   return SVDQ_OK;
 }
 
+// The quantisation kernels address x, proj_down, lora_act and the code buffers
+// through buffer descriptors with 32-bit sizes; keep each under 2 GiB.
+int check_rsrc_sizes(int64_t M, int64_t K, int64_t R) {
+  const int64_t lim = int64_t(1) << 31;
+  if (M * K * 2 >= lim || K * R * 2 >= lim || M * R * 2 >= lim ||
+      (int64_t)svdq::packed_weight_bytes(M, K) >= lim)
+    return fail(SVDQ_ERR_UNSUPPORTED, "a tensor of the quantisation step exceeds 2 GiB (M=%lld K=%lld R=%lld)",
+                (long long)M, (long long)K, (long long)R);
+  return SVDQ_OK;
+}
+
 int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
   for (int i = 0; i < n; ++i)
     if (ptrs[i] == nullptr) return fail(SVDQ_ERR_NULL, "%s is NULL", names[i]);
@@ -175,6 +186,7 @@ int svdq_quantize_act(const void* x, const void* smooth, int64_t M, int64_t K,
   (void)workspace_bytes;   // no scratch is needed (size query returns 0)
   int st = check_mk(M, K, R);
   if (st) return st;
+  if ((st = check_rsrc_sizes(M, K, R))) return st;
   if (act_layout != SVDQ_ACT_CANONICAL && act_layout != SVDQ_ACT_PACKED)
     return fail(SVDQ_ERR_INVALID, "act_layout %d is not a known layout", act_layout);
   const bool packed = act_layout == SVDQ_ACT_PACKED;
@@ -368,6 +380,7 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
                      size_t workspace_bytes, void* stream) {
   int st = check_mk(M, K, R);
   if (st) return st;
+  if ((st = check_rsrc_sizes(M, K, R))) return st;
   if ((st = check_nk(N, K))) return st;
   if (M == 0 || N == 0) return ok();
   {

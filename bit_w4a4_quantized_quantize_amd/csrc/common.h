@@ -56,6 +56,31 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float s) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
+// Block scale of a 16-block: e4m3(max|v| / 6). Multiplying by RN(1/6) gives the
+// same code as the exact quotient: an exact e4m3 rounding midpoint mu (at most 5
+// significant bits) comes out as mu * (1 + 2^-25), which rounds back to mu in
+// fp32, and every other quotient is at least 2^-16 (relative) from a midpoint.
+__device__ __forceinline__ uint32_t block_scale_code(float amax) {
+  return f32_to_e4m3_sat(amax * (1.0f / 6.0f));
+}
+
+// 1 / s_d for a decoded nonzero e4m3 scale (a normal fp32 in [2^-9, 448]):
+// hardware reciprocal plus one Newton step, within about 1 unit in the last
+// place, which the 21-bit rounding of the quotients (below) tolerates.
+__device__ __forceinline__ float scale_reciprocal(float sd) {
+  const float r = __builtin_amdgcn_rcpf(sd);
+  return __builtin_fmaf(__builtin_fmaf(-sd, r, 1.0f), r, r);
+}
+
+// Round a quotient v / s_d, computed as v * (1/s_d) within 3 units in the last
+// place, to 21 significant bits: an exact E2M1 rounding midpoint (at most 3
+// significant bits) is restored exactly, and every other quotient (at least
+// 2^-16 relative away from any midpoint, since v has at most 16 significant
+// bits and s_d at most 4) stays on its side of every midpoint.
+__device__ __forceinline__ float snap21(float q) {
+  return __uint_as_float((__float_as_uint(q) + 4u) & ~7u);
+}
+
 // Dequantise one dword of 8 E2M1 codes (low nibble first = lower k) times the
 // block scale `s` (an exactly representable f16) into 8 f16 values, exactly.
 __device__ __forceinline__ f16x8 dequant8_f16(uint32_t codes, _Float16 s) {
@@ -71,5 +96,13 @@ __device__ __forceinline__ f16x8 dequant8_f16(uint32_t codes, _Float16 s) {
 }
 
 __device__ __forceinline__ u32x4 zero4() { u32x4 z = {0u, 0u, 0u, 0u}; return z; }
+
+// Raw buffer resource over [base, base + bytes): loads at an offset at or past
+// `bytes` return zero and stores there are dropped, so bounds checks become
+// offset selects instead of branches. Every access in this library is either
+// entirely inside or entirely outside the range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 }  // namespace svdq

@@ -22,7 +22,8 @@
 //
 // Tile order is XCD-aware (as in gemm_packed.hip). Epilogue: accumulators *
 // wtscale * wcscales[n], then R/16 bf16 matrix instructions add
-// lora_act @ proj_up^T, then bias, then bf16 (RNE) stores.
+// lora_act @ proj_up^T, then bias, then bf16 (RNE), staged through LDS so the
+// output leaves as coalesced 16-byte row pieces.
 #include "common.h"
 #include "kernels.h"
 
@@ -180,46 +181,83 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] *= alpha[j];
 
+  // low-rank up-projection: R/16 bf16 matrix instructions per tile; the
+  // operands of step s+2 load while step s multiplies
   const int R = (int)a.R;
-  for (int rb = 0; rb < R; rb += 128) {
+  const int r_steps = R / 16;
+  auto load_res = [&](bf16x8* la, bf16x8* pu, int rs) {
+    const int r0 = 16 * rs;
 #pragma unroll
-    for (int rs = 0; rs < 8; ++rs) {
-      const int r0 = rb + 16 * rs;
-      if (r0 < R) {
-        bf16x8 la[TM], pu[TN];
+    for (int i = 0; i < TM; ++i) {
+      const int m = m_w + 32 * i + l32;
+      u32x4 v = zero4();
+      if (rs < r_steps && m < M) v = *reinterpret_cast<const u32x4*>(a.lora_act + (size_t)m * R + r0 + 8 * h);
+      la[i] = __builtin_bit_cast(bf16x8, v);
+    }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int m = m_w + 32 * i + l32;
-          u32x4 v = zero4();
-          if (m < M) v = *reinterpret_cast<const u32x4*>(a.lora_act + (size_t)m * R + r0 + 8 * h);
-          la[i] = __builtin_bit_cast(bf16x8, v);
-        }
+    for (int j = 0; j < TN; ++j) {
+      u32x4 v = zero4();
+      if (rs < r_steps && ncol[j] < N) v = *reinterpret_cast<const u32x4*>(a.proj_up + (size_t)ncol[j] * R + r0 + 8 * h);
+      pu[j] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
+  if (r_steps > 0) {
+    bf16x8 la0[TM], pu0[TN], la1[TM], pu1[TN];
+    load_res(la0, pu0, 0);
+    load_res(la1, pu1, 1);
+    for (int rs = 0; rs < r_steps; rs += 2) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          u32x4 v = zero4();
-          if (ncol[j] < N) v = *reinterpret_cast<const u32x4*>(a.proj_up + (size_t)ncol[j] * R + r0 + 8 * h);
-          pu[j] = __builtin_bit_cast(bf16x8, v);
-        }
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la0[i], pu0[j], acc[i][j], 0, 0, 0);
+      load_res(la0, pu0, rs + 2);
+      if (rs + 1 < r_steps) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], pu[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la1[i], pu1[j], acc[i][j], 0, 0, 0);
       }
+      load_res(la1, pu1, rs + 3);
     }
   }
 
+  // bf16 output through LDS (free after the main loop): each wave writes one
+  // 32-row slice of its tile row-major, then stores whole 16-byte row pieces
+  constexpr int kCols = 32 * TN;                 // columns of a wave tile
+  constexpr int kPieces = kCols / 8;             // 16-byte pieces per row
+  uint16_t* stage_out = reinterpret_cast<uint16_t*>(smem + wave * (32 * kCols * 2));
+  const bool vec_ok = (N % 8) == 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      if (ncol[j] >= N) continue;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m_w + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M) a.y[(size_t)m * N + ncol[j]] = (uint16_t)f32_to_bf16_rne(acc[i][j][r] + bias_v[j]);
+        const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+        stage_out[row * kCols + 32 * j + l32] = (uint16_t)f32_to_bf16_rne(acc[i][j][r] + bias_v[j]);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < (32 * kPieces + 63) / 64; ++u) {
+      const int idx = lane + 64 * u;
+      if (idx < 32 * kPieces) {
+        const int row = idx / kPieces, piece = idx % kPieces;
+        const int m = m_w + 32 * i + row;
+        const int n = n_w + 8 * piece;
+        if (m < M && n < N) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + row * kCols + 8 * piece);
+          uint16_t* dst = a.y + (size_t)m * N + n;
+          if (vec_ok && n + 8 <= N) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+          } else {
+            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+          }
+        }
       }
     }
+    __syncthreads();
   }
 }
 

@@ -7,14 +7,14 @@
 // codes = E2M1 nearest even of v / s_d (saturating, sign kept), packed two per
 // byte with the even k in the low nibble.
 //
-// Exactness of the code decision without a division per element: v has at
+// Exactness of the code decision without a division (see common.h): v has at
 // most 16 significant bits and s_d at most 4, so v / s_d is either exactly an
-// E2M1 rounding midpoint (at most 5 significant bits) or at least 2^-16
-// (relative) away from every midpoint. q = v * RN(1/s_d) is within 2 units in
-// the last place of v / s_d. Rounding q to 21 significant bits (adding 4 to
-// its bit pattern and clearing the low 3 bits) therefore puts an exact
-// midpoint back exactly on it and leaves every other quotient on its side of
-// every midpoint; the hardware E2M1 conversion then rounds ties to even.
+// E2M1 rounding midpoint or at least 2^-16 (relative) away from every
+// midpoint. q = v * (1/s_d), with the reciprocal within about 1 unit in the
+// last place, is within 3 units of v / s_d; rounding q to 21 significant bits
+// puts an exact midpoint back exactly on it and leaves every other quotient on
+// its side of every midpoint; the hardware E2M1 conversion then rounds ties to
+// even. The scale itself is e4m3(max|v| * RN(1/6)), equal to the exact rule.
 //
 // HBM-bound: one workgroup covers 32 rows x 256 columns; each lane loads 8
 // consecutive bf16 (16 bytes) per row, a wave reads two 512-byte row
@@ -32,9 +32,6 @@ constexpr int kRows = 32;     // rows per workgroup
 constexpr int kChunk = 256;   // K elements per workgroup (16 blocks)
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float snap21(float q) {
-  return __uint_as_float((__float_as_uint(q) + 4u) & ~7u);
-}
 
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ smooth,
@@ -84,9 +81,9 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     // the other half of this 16-block sits in the neighbouring lane
     amax = fmaxf(amax, __shfl_xor(amax, 1));
 
-    const uint32_t sc = f32_to_e4m3_sat(__fdiv_rn(amax, 6.0f));
+    const uint32_t sc = block_scale_code(amax);
     const float sd = e4m3_to_f32(sc, 0);
-    const float inv = sd > 0.0f ? __fdiv_rn(1.0f, sd) : 0.0f;
+    const float inv = sd > 0.0f ? scale_reciprocal(sd) : 0.0f;
 
     uint32_t packed = 0u;
     packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[0] * inv), snap21(v[1] * inv), 1.0f, 0);

@@ -6,7 +6,7 @@
 //
 // A workgroup owns 16*RT rows and the whole K range, so the down-projection
 // needs no cross-workgroup reduction: its waves take interleaved 32-wide K
-// steps (loading the next step's operands while working on the current one)
+// steps (loading the operands two steps ahead while working on the current one)
 // and their partial sums are added in a fixed order through LDS at the end
 // (deterministic). Each lane holds 8 consecutive k of one row (a 16-byte
 // load), which is at once the A fragment of v_mfma_f32_16x16x32_bf16 and half
@@ -35,9 +35,6 @@ namespace {
 
 constexpr int kRChunk = 128;
 
-__device__ __forceinline__ float snap21(float q) {
-  return __uint_as_float((__float_as_uint(q) + 4u) & ~7u);
-}
 __device__ __forceinline__ uint32_t perm_lo(uint32_t lo_src, uint32_t hi_src) {
   return __builtin_amdgcn_perm(hi_src, lo_src, 0x05040100u);
 }
@@ -77,9 +74,22 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
   const int MP = (M + 31) / 32;
   const int KP = (K + 63) / 64;
   // packed output covers whole 64-wide panels: positions beyond K get zero codes
-  // and zero scales (the GEMM multiplies them by the weight's zero padding)
+  // and zero scales (the GEMM multiplies them by the weight's zero padding); its
+  // rows beyond M inside the last 32-row panel are written as zeros too
   const int steps = PACKED ? 2 * KP : (K + 31) / 32;
-  const size_t code_bytes = (size_t)MP * KP * 1024;
+  const uint32_t code_bytes = (uint32_t)MP * KP * 1024;
+
+  const uint32_t x_bytes = (uint32_t)M * K * 2;
+  const uint32_t pd_bytes = (uint32_t)K * R * 2;
+  const uint32_t q_bytes = PACKED ? code_bytes + (uint32_t)MP * KP * 128 : (uint32_t)M * (K / 2);
+  const uint32_t s_bytes = PACKED ? 0u : (uint32_t)(K / 16) * M;
+  const uint32_t l_bytes = (uint32_t)M * R * 2;
+  const auto rx = make_rsrc(a.x, x_bytes);
+  const auto rsm = make_rsrc(a.smooth, (uint32_t)K * 2);
+  const auto rpd = make_rsrc(a.proj_down, pd_bytes);
+  const auto rq = make_rsrc(a.qact, q_bytes);
+  const auto rsc = make_rsrc(a.ascales, s_bytes);
+  const auto rl = make_rsrc(a.lora_act, l_bytes);
 
   const int n_chunks = R > 0 ? (R + kRChunk - 1) / kRChunk : 1;
   for (int rc_i = 0; rc_i < n_chunks; ++rc_i) {
@@ -94,37 +104,35 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // software pipeline: the operands of this wave's next step load while
-    // the current step is quantised and multiplied
+    // operands of one 32-wide step; positions outside the tensors read as zero
     auto load = [&](StepRegs<RT>& r, int st) {
       const int kg = st * 32 + 8 * g;
       const bool k_in = st < steps && kg < K;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int m = m0 + 16 * t + c;
-        r.x[t] = zero4();
-        if (k_in && m < M) r.x[t] = *reinterpret_cast<const u32x4*>(a.x + (size_t)m * K + kg);
+        const uint32_t off = k_in ? ((uint32_t)m * K + kg) * 2 : x_bytes;
+        r.x[t] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
       }
       r.sm = zero4();
-      if (do_quant && k_in) r.sm = *reinterpret_cast<const u32x4*>(a.smooth + kg);
+      if (do_quant) r.sm = __builtin_amdgcn_raw_buffer_load_b128(rsm, k_in ? kg * 2 : K * 2, 0, 0);
       if (R > 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          r.p[j] = zero4();
-          if (r_in && k_in && kg + j < K)
-            r.p[j] = *reinterpret_cast<const u32x4*>(a.proj_down + (size_t)(kg + j) * R + rcol);
+          const uint32_t off = (r_in && k_in) ? ((uint32_t)(kg + j) * R + rcol) * 2 : pd_bytes;
+          r.p[j] = __builtin_amdgcn_raw_buffer_load_b128(rpd, off, 0, 0);
         }
       }
     };
 
-    StepRegs<RT> cur, nxt;
+    // two steps of lookahead (three register sets in flight)
+    StepRegs<RT> cur, nxt, nxt2;
     load(cur, wave);
+    load(nxt, wave + kWaves);
     for (int st = wave; st < steps; st += kWaves) {
-      load(nxt, st + kWaves);
+      load(nxt2, st + 2 * kWaves);
       const int kg = st * 32 + 8 * g;
       const bool k_in = kg < K;
-      const u32x4* xw = cur.x;
-      const u32x4* p = cur.p;
 
       if (do_quant) {
         float sm[8];
@@ -140,31 +148,32 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
           float amax = 0.0f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            v[2 * j] = bf16lo_to_f32(xw[t][j]) * sm[2 * j];
-            v[2 * j + 1] = bf16hi_to_f32(xw[t][j]) * sm[2 * j + 1];
+            v[2 * j] = bf16lo_to_f32(cur.x[t][j]) * sm[2 * j];
+            v[2 * j + 1] = bf16hi_to_f32(cur.x[t][j]) * sm[2 * j + 1];
           }
 #pragma unroll
           for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
           amax = fmaxf(amax, __shfl_xor(amax, 16));   // other half of the block
-          const uint32_t sc = f32_to_e4m3_sat(__fdiv_rn(amax, 6.0f));
+          const uint32_t sc = block_scale_code(amax);
           const float sd = e4m3_to_f32(sc, 0);
-          const float inv = sd > 0.0f ? __fdiv_rn(1.0f, sd) : 0.0f;
+          const float inv = sd > 0.0f ? scale_reciprocal(sd) : 0.0f;
           uint32_t packed = 0u;
           packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[0] * inv), snap21(v[1] * inv), 1.0f, 0);
           packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[2] * inv), snap21(v[3] * inv), 1.0f, 1);
           packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[4] * inv), snap21(v[5] * inv), 1.0f, 2);
           packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[6] * inv), snap21(v[7] * inv), 1.0f, 3);
-          if (m < M && (PACKED || k_in)) {
-            if (PACKED) {
-              const int pp = kg >> 6, tt = (kg >> 4) & 3, hh = (kg >> 3) & 1;
-              const int q = m >> 5, cc = m & 31;
-              const size_t chunk = (size_t)pp * MP + q;
-              *reinterpret_cast<uint32_t*>(a.qact + chunk * 1024 + ((hh * 32 + cc) * 4 + tt) * 4) = packed;
-              if (hh == 0) a.qact[code_bytes + chunk * 128 + cc * 4 + tt] = (uint8_t)sc;
-            } else {
-              *reinterpret_cast<uint32_t*>(a.qact + (size_t)m * (K / 2) + kg / 2) = packed;
-              if ((g & 1) == 0) a.ascales[(size_t)(kg >> 4) * M + m] = (uint8_t)sc;
-            }
+          if (PACKED) {
+            const int pp = kg >> 6, tt = (kg >> 4) & 3, hh = (kg >> 3) & 1;
+            const int q = m >> 5, cc = m & 31;
+            const uint32_t chunk = (uint32_t)pp * MP + q;
+            __builtin_amdgcn_raw_buffer_store_b32(packed, rq, chunk * 1024 + ((hh * 32 + cc) * 4 + tt) * 4, 0, 0);
+            if (hh == 0)
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rq, code_bytes + chunk * 128 + cc * 4 + tt, 0, 0);
+          } else {
+            const bool ok = k_in && m < M;
+            __builtin_amdgcn_raw_buffer_store_b32(packed, rq, ok ? (uint32_t)m * (K / 2) + kg / 2 : q_bytes, 0, 0);
+            if ((g & 1) == 0)
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rsc, ok ? (uint32_t)(kg >> 4) * M + m : s_bytes, 0, 0);
           }
         }
       }
@@ -175,16 +184,17 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
           u32x4 f;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            f[q] = (i & 1) ? perm_hi(p[2 * q][i >> 1], p[2 * q + 1][i >> 1])
-                           : perm_lo(p[2 * q][i >> 1], p[2 * q + 1][i >> 1]);
+            f[q] = (i & 1) ? perm_hi(cur.p[2 * q][i >> 1], cur.p[2 * q + 1][i >> 1])
+                           : perm_lo(cur.p[2 * q][i >> 1], cur.p[2 * q + 1][i >> 1]);
           const bf16x8 b = __builtin_bit_cast(bf16x8, f);
 #pragma unroll
           for (int t = 0; t < RT; ++t)
-            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xw[t]), b,
+            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.x[t]), b,
                                                                 acc[t][i], 0, 0, 0);
         }
       }
       cur = nxt;
+      nxt = nxt2;
     }
 
     if (R > 0) {
@@ -206,19 +216,17 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
             for (int i = 0; i < 8; ++i) acc[t][i] += s_red[wave][t][i][lane];
         }
       }
-      if (wave == 0 && r_in) {
+      if (wave == 0) {
         // lane holds rows 16t + 4g + q and columns rcol .. rcol+7
 #pragma unroll
         for (int t = 0; t < RT; ++t)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int m = m0 + 16 * t + 4 * g + q;
-            if (m < M) {
-              u32x4 o;
+            u32x4 o;
 #pragma unroll
-              for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(acc[t][2 * w][q], acc[t][2 * w + 1][q]);
-              *reinterpret_cast<u32x4*>(a.lora_act + (size_t)m * R + rcol) = o;
-            }
+            for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(acc[t][2 * w][q], acc[t][2 * w + 1][q]);
+            __builtin_amdgcn_raw_buffer_store_b128(o, rl, r_in ? ((uint32_t)m * R + rcol) * 2 : l_bytes, 0, 0);
           }
       }
     }

@@ -45,6 +45,9 @@
  *  - K must be a positive multiple of 16 (the NVFP4 block). R must be 0 or a
  *    multiple of 16 (SVDQ_ERR_UNSUPPORTED otherwise). Every pointer must be
  *    16-byte aligned (SVDQ_ERR_ALIGN).
+ *  - The quantisation step (also inside svdq_linear_w4a4) needs x, proj_down,
+ *    lora_act and the packed activation buffer each below 2 GiB
+ *    (SVDQ_ERR_UNSUPPORTED otherwise).
  *  - NaN or Inf inputs are not checked; results are then unspecified.
  */
 #ifndef SVDQ_H

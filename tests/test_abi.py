@@ -79,7 +79,7 @@ def q(**kw):
 @no_gpu_only
 @pytest.mark.parametrize("kw,code", [
     (dict(M=-1), 2), (dict(K=0), 2), (dict(K=24), 2), (dict(R=-16), 2),
-    (dict(R=8), 3), (dict(K=1 << 25), 3),
+    (dict(R=8), 3), (dict(K=1 << 25), 3), (dict(M=1 << 20, K=1 << 12), 3),
     (dict(x=None), 1), (dict(smooth=None), 1), (dict(qact=None), 1), (dict(ascales=None), 1),
     (dict(proj_down=None), 1), (dict(lora_act=None), 1),
     (dict(x=fake(1) + 8), 4), (dict(ascales=fake(5) + 4), 4),

@@ -180,3 +180,35 @@ def test_quant_packed_layout_bit_exact(gpu_lib, M, K, R, kind, seed):
     assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:4].ravel().tolist()}"
     q2, s2 = P.unpack(got, M, K)
     assert np.array_equal(q2, q_ref) and np.array_equal(s2, s_ref)
+
+
+def test_quant_every_scale_with_ties_at_every_midpoint(gpu_lib):
+    """For each of the 126 nonzero e4m3 scales s: a block with amax = 6 s (so the
+    scale code is exactly s) holding the 7 E2M1 midpoints times s, both signs, and
+    their bf16 neighbours just below and above. Exercises the exact tie handling
+    (scale rule, reciprocal, 21-bit rounding) for every scale the format has."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    rows = []
+    for code in range(1, 0x7F):
+        s = F.e4m3_decode(np.array([code]))[0]
+        if 6 * s > 3.0e38:
+            continue
+        for variant in range(3):
+            blk = np.zeros(16)
+            blk[0] = 6 * s
+            vals = mids * s
+            if variant == 1:      # next bf16 value below each midpoint
+                vals = F.bf16_to_f64(F.f64_to_bf16(vals)) - F.bf16_to_f64(F.f64_to_bf16(vals)) * 2.0 ** -8
+            if variant == 2:      # next bf16 value above
+                vals = vals + vals * 2.0 ** -7
+            blk[1:8] = vals
+            blk[8:15] = -vals
+            blk[15] = -6 * s
+            rows.append(blk)
+    vals = np.array(rows)
+    x = F.f64_to_bf16(vals)
+    ones = F.f64_to_bf16(np.ones(16))
+    assert_exact(gpu_lib, x, ones)
+    q_ref, s_ref = S.quantize_act(x, ones)
+    # the tie rows really produce the intended scale codes
+    assert set(np.unique(s_ref)) >= set(range(0x20, 0x7F))
