@@ -13,8 +13,8 @@ the roofline of the dominant kernel (the GEMM, bound by the f16 matrix cores),
 the activation-quantisation kernel's HBM bandwidth, and the CPU oracle timed
 on the same workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--layout packed|canonical]
-                       [--no-cpu-baseline] [--warm]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 50] [--layout packed|canonical]
+                       [--no-cpu-baseline] [--warm] [--copy-calibration]
 """
 
 import argparse
@@ -31,26 +31,33 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 SVDQuant linear TFLOP/s and % MFMA peak at M=4096,K=3840,N=10240, 1 GPU"
 PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense f16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
-GEMM_KERNEL_SOURCE = os.path.join(ROOT, "bit_w4a4_quantized_quantize_amd", "csrc", "gemm_packed.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_ffn_w1_1024_traffic.txt")
+CSRC = os.path.join(ROOT, "bit_w4a4_quantized_quantize_amd", "csrc")
+GEMM_KERNEL_SOURCES = [os.path.join(CSRC, "gemm_lds.hip"), os.path.join(CSRC, "common.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_lds_ffn_w1_1024_traffic.txt")
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=50,
+                   help="untimed steps first (the chip takes ~15 ms of matrix work to reach its sustained clock)")
     p.add_argument("--layout", choices=["packed", "canonical"], default="packed")
     p.add_argument("--sets", type=int, default=6, help="distinct input/weight sets rotated (cold cache)")
     p.add_argument("--warm", action="store_true", help="reuse one set (warm cache)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--kernel-iters", type=int, default=20)
+    p.add_argument("--kernel-iters", type=int, default=100)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="finish with a plain 512 MiB device copy (to calibrate HBM byte counters)")
     return p.parse_args()
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_traffic():
@@ -64,7 +71,7 @@ def read_traffic():
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != source_hash(GEMM_KERNEL_SOURCE):
+    if vals.get("kernel_source_sha256") != source_hash(GEMM_KERNEL_SOURCES):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -239,16 +246,17 @@ def main():
         s = sets[i]
         ops.quantize_act(s["x"], s["layer"].smooth, None, qact=s["qact"], ascales=s["ascales"])
 
-    gemm_ms = time_loop(gemm, n_sets, args.kernel_iters, 3, stream)
-    quant_ms = time_loop(quant, n_sets, args.kernel_iters, 3, stream)
-    qd_ms = time_loop(quant_down, n_sets, args.kernel_iters, 3, stream)
+    kw = max(1, args.warmup // 2)
+    gemm_ms = time_loop(gemm, n_sets, args.kernel_iters, kw, stream)
+    quant_ms = time_loop(quant, n_sets, args.kernel_iters, kw, stream)
+    qd_ms = time_loop(quant_down, n_sets, args.kernel_iters, kw, stream)
     gemm_tflops = flops_gemm / (gemm_ms * 1e-3) / 1e12
     quant_bytes_a1 = M * K * 2 + K * 2 + M * K // 2 + (K // 16) * M
     quant_gbs = quant_bytes_a1 / (quant_ms * 1e-3) / 1e9
     print(f"[bench] gemm kernel {gemm_ms * 1e3:.1f} us ({gemm_tflops:.1f} TFLOP/s), quant {quant_ms * 1e3:.2f} us "
           f"({quant_gbs:.0f} GB/s), quant+down {qd_ms * 1e3:.2f} us", file=sys.stderr, flush=True)
 
-    traffic = read_traffic()
+    traffic = read_traffic() if packed else None   # counters were taken on the packed-path GEMM
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -272,7 +280,7 @@ def main():
         },
         "pct_mfma_peak": round(100.0 * tflops / PEAK_F16_MFMA_TFLOPS, 2),
         "roofline": {
-            "kernel": "gemm_packed_kernel (scaled GEMM + low-rank up-projection + epilogue)"
+            "kernel": "gemm_lds_kernel (scaled GEMM + low-rank up-projection + epilogue)"
                       if args.layout == "packed" else
                       "gemm_w4a4_kernel (scaled GEMM + low-rank up-projection + epilogue)",
             "bound": "mfma",
@@ -293,6 +301,13 @@ def main():
             "fused_with_down_projection_us": round(qd_ms * 1e3, 3),
         },
     }
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the same workload", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(d, cfg)

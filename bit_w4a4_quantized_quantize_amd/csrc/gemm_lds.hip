@@ -20,7 +20,11 @@
 // (p+1)%2, and after that issues the global loads of its panel p+2 chunks into
 // registers, a whole panel ahead of their use.
 //
-// Tile order is XCD-aware (as in gemm_packed.hip). Epilogue: accumulators *
+// Tile order: workgroup w is dispatched to XCD w % 8 and each XCD has its own
+// L2, so the 8 XCDs get contiguous ranges of tiles; inside a range, tiles walk
+// down kGroupM row blocks before moving right, so the workgroups resident on
+// one XCD share activation rows and weight columns. The grid is padded to a
+// multiple of 8; the padding workgroups exit at once. Epilogue: accumulators *
 // wtscale * wcscales[n], then R/16 bf16 matrix instructions add
 // lora_act @ proj_up^T, then bias, then bf16 (RNE), staged through LDS so the
 // output leaves as coalesced 16-byte row pieces.
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   const size_t a_code_bytes = (size_t)KP * MP * 1024;
   const size_t b_code_bytes = (size_t)KP * NP * 1024;
 
-  // XCD-aware grouped tile order (see gemm_packed.hip)
+  // XCD-aware grouped tile order (see the header comment)
   const int NBX = (N + C::BN - 1) / C::BN;
   const int NBY = (M + C::BM - 1) / C::BM;
   const int T = NBX * NBY;

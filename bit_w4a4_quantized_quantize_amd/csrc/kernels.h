@@ -14,7 +14,7 @@ hipError_t launch_quant_act(const uint16_t* x, const uint16_t* smooth, uint8_t* 
 
 // a1 + a2 fused: one pass over x gives quant(x * smooth) and
 // lora_act [M, R] = bf16(x @ proj_down) (R may be 0). Output codes/scales in the
-// canonical layout or in the packed fragment layout read by gemm_packed.
+// canonical layout or in the packed fragment layout read by gemm_lds.
 int quant_lora_row_tiles(int64_t M);
 hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down,
                              uint8_t* qact, uint8_t* ascales, uint16_t* lora_act, int64_t M,
@@ -37,10 +37,8 @@ struct GemmArgs {
 };
 // canonical activations (LDS-staged), canonical or packed weights
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
-// packed activations (qact holds the packed buffer, ascales unused) and packed weights:
-// per-wave register dequantisation (gemm_packed.hip) ...
-hipError_t launch_gemm_packed(const GemmArgs& a, hipStream_t stream);
-// ... or dequantisation once per workgroup into LDS (gemm_lds.hip), the default
+// packed activations (qact holds the packed buffer, ascales unused) and packed
+// weights: each element dequantised once per workgroup into LDS
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream);
 
 // a3: load-time repack of qweight/wscales into the MFMA-order layout, and back.
