@@ -68,6 +68,22 @@ def test_linear_full_ffn_shape_sampled_rows(gpu_lib):
     linear_case(gpu_lib, cfg, packed=True, rows=rows)
 
 
+@pytest.mark.parametrize("name,cfg", [
+    ("qkv_1024", workloads.QKV_1024),
+    ("w2_1024", workloads.FFN_W2_1024),
+    ("qkv_2048px", workloads.LAYERS_2048["qkv"]),
+    ("out_2048px", workloads.LAYERS_2048["out"]),
+    ("w2_2048px", workloads.LAYERS_2048["w2"]),
+])
+def test_linear_full_size_sampled_rows(gpu_lib, name, cfg):
+    """The other full-size layers (fused QKV N = 11520; w2 with K = 10240 on SwiGLU-like
+    inputs; the 2048px token count M = 16896), whole output computed with packed weights
+    as the layer runs, 24 sampled rows checked against the oracle."""
+    rows = np.sort(np.random.default_rng(cfg["seed"]).choice(cfg["M"], size=24, replace=False))
+    rows[0], rows[-1] = 0, cfg["M"] - 1
+    linear_case(gpu_lib, cfg, packed=True, rows=rows)
+
+
 def test_linear_workspace_reuse_and_smaller_second_call(gpu_lib):
     """The same workspace serves a large call then a smaller one (no stale state)."""
     cfg1 = dict(M=600, K=1024, N=256, R=128, kind="dit", seed=44)

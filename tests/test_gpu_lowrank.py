@@ -1,8 +1,9 @@
 """GPU parity of the down-projection lora_act = bf16(x @ proj_down) against the oracle's
 float64 product: each element within bf16 rounding plus fp32 accumulation error.
 
-Covers the K-split path with its arrival counters (few rows), the unsplit path
-(many rows), ragged M, R = 16 and R = 128, K = 16 and 10240, and determinism.
+The down-projection runs inside the fused quantisation kernel, one 32-row tile
+per wave (fewer than 8192 rows) or two (8192 rows or more). Covers both, ragged
+M, R = 16 .. 256, K = 16 and 10240, and determinism.
 """
 
 import numpy as np
@@ -35,8 +36,8 @@ def check_lora(ops, M, K, R, kind, seed):
 
 @pytest.mark.parametrize("M,K,R,kind,seed", [
     (64, 256, 16, "tiny", 1001),
-    (4096, 3840, 128, "dit", 1003),     # split over K (arrival counters)
-    (17000, 256, 32, "dit", 12),        # many rows: unsplit, ragged last tile
+    (4096, 3840, 128, "dit", 1003),     # the 1024^2 activation
+    (17000, 256, 32, "dit", 12),        # many rows: two row tiles per wave, ragged last tile
     (100, 10240, 128, "swiglu", 13),    # long K, ragged M
     (33, 16, 16, "tiny", 14),           # a single 16-wide K block
     (48, 384, 256, "dit", 15),          # R above one 128-wide chunk

@@ -13,7 +13,7 @@ import torch
 import workloads
 from oracle import formats as F
 from oracle import svdq as S
-from tests.gpu_util import dev_bf16, host_u8
+from tests.gpu_util import dev_bf16, host_bits, host_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -212,3 +212,27 @@ def test_quant_every_scale_with_ties_at_every_midpoint(gpu_lib):
     q_ref, s_ref = S.quantize_act(x, ones)
     # the tie rows really produce the intended scale codes
     assert set(np.unique(s_ref)) >= set(range(0x20, 0x7F))
+
+
+def test_quant_packed_2048px_sampled_rows(gpu_lib):
+    """The 2048px activation (M = 16384 + 512 tokens, K = 3840, R = 128), packed output with
+    the down-projection, in the configuration the whole layer launches: codes and scales of
+    48 sampled rows bit-exact (through the oracle's unpack of the whole buffer), lora_act
+    of the same rows within bf16 rounding plus fp32 accumulation."""
+    from oracle import repack as P
+    cfg = workloads.LAYERS_2048["w1"]
+    M, K, R = cfg["M"], cfg["K"], cfg["R"]
+    d = workloads.make_linear(M, K, 16, R, kind=cfg["kind"], seed=cfg["seed"], with_bias=False)
+    buf, _, lora = gpu_lib.quantize_act(dev_bf16(d["x"]), dev_bf16(d["smooth"]), dev_bf16(d["proj_down"]),
+                                        packed=True)
+    torch.cuda.synchronize()
+    q_all, s_all = P.unpack(host_u8(buf), M, K)
+    rows = np.sort(np.random.default_rng(61).choice(M, size=48, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    q_ref, s_ref = S.quantize_act(d["x"][rows], d["smooth"])
+    assert np.array_equal(q_all[rows], q_ref)
+    assert np.array_equal(s_all[:, rows], s_ref)
+    got = F.bf16_to_f64(host_bits(lora)[rows])
+    ref = S.lowrank_down(d["x"][rows], d["proj_down"])
+    scale = np.abs(F.bf16_to_f64(d["x"][rows])) @ np.abs(F.bf16_to_f64(d["proj_down"]))
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + scale * K * 2.0 ** -23 + 1e-30)
