@@ -83,6 +83,16 @@ int check_rsrc_sizes(int64_t M, int64_t K, int64_t R) {
   return SVDQ_OK;
 }
 
+// The packed-operand GEMM addresses both packed buffers through 32-bit buffer
+// offsets (out-of-range panels read as zero).
+int check_packed_gemm_sizes(int64_t M, int64_t N, int64_t K) {
+  const int64_t lim = int64_t(1) << 31;
+  if ((int64_t)svdq::packed_weight_bytes(M, K) >= lim || (int64_t)svdq::packed_weight_bytes(N, K) >= lim)
+    return fail(SVDQ_ERR_UNSUPPORTED, "a packed GEMM operand exceeds 2 GiB (M=%lld N=%lld K=%lld)",
+                (long long)M, (long long)N, (long long)K);
+  return SVDQ_OK;
+}
+
 int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
   for (int i = 0; i < n; ++i)
     if (ptrs[i] == nullptr) return fail(SVDQ_ERR_NULL, "%s is NULL", names[i]);
@@ -332,6 +342,7 @@ int svdq_gemm_w4a4(const void* qact, const void* ascales, int act_layout, const 
   int st = check_mk(M, K, R);
   if (st) return st;
   if ((st = check_nk(N, K))) return st;
+  if (act_layout == SVDQ_ACT_PACKED && (st = check_packed_gemm_sizes(M, N, K))) return st;
   if (M == 0 || N == 0) return ok();
   if ((st = validate_gemm(qact, ascales, act_layout, lora_act, weight, wscales, weight_layout, wcscales,
                           wtscale, proj_up, bias, M, N, K, R, y, true)))
@@ -382,6 +393,7 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   if (st) return st;
   if ((st = check_rsrc_sizes(M, K, R))) return st;
   if ((st = check_nk(N, K))) return st;
+  if (weight_layout == SVDQ_WEIGHT_PACKED && (st = check_packed_gemm_sizes(M, N, K))) return st;
   if (M == 0 || N == 0) return ok();
   {
     const char* names[] = {"x", "smooth", "workspace"};

@@ -17,19 +17,26 @@
 // Pipeline (one barrier per panel, two LDS stages): while the waves multiply
 // panel p out of stage p%2, each also dequantises its share of panel p+1 (one
 // 16-K slice per step, interleaved with its matrix instructions) into stage
-// (p+1)%2, and after that issues the global loads of its panel p+2 chunks into
-// registers, a whole panel ahead of their use.
+// (p+1)%2, then issues the global loads of its panel p+2 chunks into
+// registers. Chunk loads go through buffer resources, so a panel past the end
+// of M or N reads as zeros without a branch; the last panel is peeled.
 //
 // Tile order: workgroup w is dispatched to XCD w % 8 and each XCD has its own
 // L2, so the 8 XCDs get contiguous ranges of tiles; inside a range, tiles walk
 // down kGroupM row blocks before moving right, so the workgroups resident on
 // one XCD share activation rows and weight columns. The grid is padded to a
-// multiple of 8; the padding workgroups exit at once. Epilogue: accumulators *
-// wtscale * wcscales[n], then R/16 bf16 matrix instructions add
-// lora_act @ proj_up^T, then bias, then bf16 (RNE), staged through LDS so the
-// output leaves as coalesced 16-byte row pieces.
+// multiple of 8; the padding workgroups exit at once.
+//
+// Epilogue: wcscales and bias load while the last panel multiplies;
+// accumulators * wtscale * wcscales[n]; then lora_act @ proj_up^T: the
+// operand fragments of up to 8 rank steps (both LDS stages, 144 KB) are copied
+// into LDS by direct global-to-LDS loads, one wait, and R/16 bf16 matrix
+// instructions per tile read them from there; then bias, then bf16 (RNE),
+// staged through LDS so the output leaves as coalesced 16-byte row pieces.
 #include "common.h"
 #include "kernels.h"
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 namespace svdq {
 
@@ -46,8 +53,11 @@ struct LdsCfg {
   static constexpr int kChunksA = BM / 32;
   static constexpr int kChunksB = BN / 32;
   static constexpr int kChunks = kChunksA + kChunksB;
-  static constexpr int kPerWave = (kChunks + kWaves - 1) / kWaves;   // chunks a wave dequantises
-  static constexpr int kStageBytes = kChunks * 4096;                  // f16 fragments of one panel
+  static constexpr int kFull = kChunks / kWaves;                 // chunks every wave dequantises
+  static constexpr int kRest = kChunks - kFull * kWaves;         // waves 0..kRest-1 take one more
+  static constexpr int kPerWave = kFull + (kRest ? 1 : 0);
+  static constexpr int kStageBytes = kChunks * 4096;
+  static constexpr int kResSteps = (2 * kStageBytes) / (kChunks * 1024);   // R/16 steps per LDS residual pass
 };
 
 template <int WM, int WN, int TM, int TN>
@@ -67,10 +77,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   const int KP = (K + 63) / 64;
   const int MP = (M + 31) / 32;
   const int NP = (N + 31) / 32;
-  const size_t a_code_bytes = (size_t)KP * MP * 1024;
-  const size_t b_code_bytes = (size_t)KP * NP * 1024;
+  const uint32_t a_code_bytes = (uint32_t)KP * MP * 1024;
+  const uint32_t b_code_bytes = (uint32_t)KP * NP * 1024;
 
-  // XCD-aware grouped tile order (see the header comment)
   const int NBX = (N + C::BN - 1) / C::BN;
   const int NBY = (M + C::BM - 1) / C::BM;
   const int T = NBX * NBY;
@@ -85,42 +94,41 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   const int mp0 = by * (C::BM / 32);
   const int np0 = bx * (C::BN / 32);
 
-  // this wave's dequantisation chunks: c = wave + kWaves * s (A chunks first)
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.qact, a_code_bytes + (uint32_t)KP * MP * 128);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.weight, b_code_bytes + (uint32_t)KP * NP * 128);
+
+  // chunk c = wave + kWaves * s; A chunks first. Out-of-range panels read as zero.
   u32x4 cc[C::kPerWave];
   uint32_t cs[C::kPerWave];
+  auto load_one = [&](int s, int kp) {
+    const int c = wave + C::kWaves * s;
+    const bool is_a = c < C::kChunksA;
+    const int row = is_a ? mp0 + c : np0 + (c - C::kChunksA);
+    const int rows = is_a ? MP : NP;
+    const uint32_t code_bytes = is_a ? a_code_bytes : b_code_bytes;
+    const uint32_t chunk = (uint32_t)kp * rows + row;
+    const bool in = row < rows;
+    const uint32_t off_c = in ? chunk * 1024 + lane * 16 : 0x80000000u;
+    const uint32_t off_s = in ? code_bytes + chunk * 128 + l32 * 4 : 0x80000000u;
+    const __amdgpu_buffer_rsrc_t r = is_a ? ra : rb;
+    cc[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off_c, 0, 0));
+    cs[s] = __builtin_amdgcn_raw_buffer_load_b32(r, off_s, 0, 0);
+  };
   auto load_chunks = [&](int kp) {
 #pragma unroll
-    for (int s = 0; s < C::kPerWave; ++s) {
-      const int c = wave + C::kWaves * s;
-      cc[s] = zero4();
-      cs[s] = 0u;
-      if (c < C::kChunksA) {
-        if (mp0 + c < MP) {
-          const size_t chunk = (size_t)kp * MP + mp0 + c;
-          cc[s] = *reinterpret_cast<const u32x4*>(a.qact + chunk * 1024 + lane * 16);
-          cs[s] = *reinterpret_cast<const uint32_t*>(a.qact + a_code_bytes + chunk * 128 + l32 * 4);
-        }
-      } else if (c < C::kChunks) {
-        if (np0 + c - C::kChunksA < NP) {
-          const size_t chunk = (size_t)kp * NP + np0 + (c - C::kChunksA);
-          cc[s] = *reinterpret_cast<const u32x4*>(a.weight + chunk * 1024 + lane * 16);
-          cs[s] = *reinterpret_cast<const uint32_t*>(a.weight + b_code_bytes + chunk * 128 + l32 * 4);
-        }
-      }
-    }
+    for (int s = 0; s < C::kFull; ++s) load_one(s, kp);
+    if (C::kRest && wave < C::kRest) load_one(C::kFull, kp);
   };
-  // dequantise 16-K slice t of this wave's chunks into an LDS stage
+  auto dq_one = [&](uint8_t* stage, int s, int t) {
+    const int c = wave + C::kWaves * s;
+    const f16x2 sp = t >= 2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cs[s], 1.0f, true)
+                            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cs[s], 1.0f, false);
+    *reinterpret_cast<f16x8*>(stage + c * 4096 + t * 1024 + lane * 16) = dequant8_f16(cc[s][t], sp[t & 1]);
+  };
   auto dequant_slice = [&](uint8_t* stage, int t) {
 #pragma unroll
-    for (int s = 0; s < C::kPerWave; ++s) {
-      const int c = wave + C::kWaves * s;
-      if (c < C::kChunks) {
-        const f16x2 sp = t >= 2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cs[s], 1.0f, true)
-                                : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cs[s], 1.0f, false);
-        const f16x8 f = dequant8_f16(cc[s][t], sp[t & 1]);
-        *reinterpret_cast<f16x8*>(stage + c * 4096 + t * 1024 + lane * 16) = f;
-      }
-    }
+    for (int s = 0; s < C::kFull; ++s) dq_one(stage, s, t);
+    if (C::kRest && wave < C::kRest) dq_one(stage, C::kFull, t);
   };
 
   f32x16 acc[TM][TN];
@@ -134,49 +142,75 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   uint8_t* stage0 = smem;
   uint8_t* stage1 = smem + C::kStageBytes;
 
-  // prologue: panel 0 into stage 0, panel 1 into registers
   load_chunks(0);
 #pragma unroll
   for (int t = 0; t < 4; ++t) dequant_slice(stage0, t);
   if (KP > 1) load_chunks(1);
   __syncthreads();
 
-  for (int kp = 0; kp < KP; ++kp) {
-    uint8_t* cur = (kp & 1) ? stage1 : stage0;
-    uint8_t* nxt = (kp & 1) ? stage0 : stage1;
-    const bool more = kp + 1 < KP;
+  auto mma_step = [&](const uint8_t* cur, int t) {
+    f16x8 fa[TM], fb[TN];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f16x8 fa[TM], fb[TN];
+    for (int i = 0; i < TM; ++i)
+      fa[i] = *reinterpret_cast<const f16x8*>(cur + (wave_m * TM + i) * 4096 + t * 1024 + lane * 16);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = *reinterpret_cast<const f16x8*>(cur + (wave_m * TM + i) * 4096 + t * 1024 + lane * 16);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[j] = *reinterpret_cast<const f16x8*>(cur + (C::kChunksA + wave_n * TN + j) * 4096 + t * 1024 + lane * 16);
-      if (more) dequant_slice(nxt, t);
+    for (int j = 0; j < TN; ++j)
+      fb[j] = *reinterpret_cast<const f16x8*>(cur + (C::kChunksA + wave_n * TN + j) * 4096 + t * 1024 + lane * 16);
+    return [&, fa, fb]() mutable {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+  };
+
+  // panels 0 .. KP-2: multiply panel kp, dequantise panel kp+1, load panel kp+2
+  for (int kp = 0; kp + 1 < KP; ++kp) {
+    const uint8_t* cur = (kp & 1) ? stage1 : stage0;
+    uint8_t* nxt = (kp & 1) ? stage0 : stage1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      auto mm = mma_step(cur, t);
+      dequant_slice(nxt, t);
+      mm();
     }
     if (kp + 2 < KP) load_chunks(kp + 2);
     __syncthreads();
   }
-
-  // ---- epilogue ----
+  // epilogue operands load while the last panel multiplies
   const int m_w = (mp0 + wave_m * TM) * 32;
   const int n_w = (np0 + wave_n * TN) * 32;
-  const float wt = bf16lo_to_f32(a.wtscale[0]);
   int ncol[TN];
+  uint32_t wc_raw[TN], bias_raw[TN];
+  {
+    const __amdgpu_buffer_rsrc_t rwc = make_rsrc(a.wcscales, (uint32_t)N * 2);
+    const __amdgpu_buffer_rsrc_t rbi = make_rsrc(a.bias, a.bias != nullptr ? (uint32_t)N * 2 : 0u);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      ncol[j] = n_w + 32 * j + l32;
+      const uint32_t off = ncol[j] < N ? (uint32_t)ncol[j] * 2 : 0x80000000u;
+      wc_raw[j] = __builtin_amdgcn_raw_buffer_load_b16(rwc, off, 0, 0);
+      bias_raw[j] = __builtin_amdgcn_raw_buffer_load_b16(rbi, off, 0, 0);
+    }
+  }
+  const uint32_t wt_raw = a.wtscale[0];
+  {
+    const uint8_t* cur = ((KP - 1) & 1) ? stage1 : stage0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      auto mm = mma_step(cur, t);
+      mm();
+    }
+  }
+
+  // ---- epilogue ----
+  const float wt = bf16lo_to_f32(wt_raw);
   float alpha[TN], bias_v[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    ncol[j] = n_w + 32 * j + l32;
-    const bool in = ncol[j] < N;
-    alpha[j] = in ? wt * bf16lo_to_f32(a.wcscales[ncol[j]]) : 0.0f;
-    bias_v[j] = (in && a.bias != nullptr) ? bf16lo_to_f32(a.bias[ncol[j]]) : 0.0f;
+    alpha[j] = wt * bf16lo_to_f32(wc_raw[j]);
+    bias_v[j] = bf16lo_to_f32(bias_raw[j]);
   }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -185,52 +219,57 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] *= alpha[j];
 
-  // low-rank up-projection: R/16 bf16 matrix instructions per tile; the
-  // operands of step s+2 load while step s multiplies
   const int R = (int)a.R;
   const int r_steps = R / 16;
-  auto load_res = [&](bf16x8* la, bf16x8* pu, int rs) {
-    const int r0 = 16 * rs;
+  // Residual through LDS: per pass of up to kResSteps 16-wide R steps, every
+  // operand fragment (32 rows x 16 R of lora_act or proj_up) is copied by DMA
+  // into a 1 KB LDS block in the matrix-instruction operand order, then the
+  // waves multiply out of LDS. Rows beyond M or N are clamped to the last row.
+  {
+    const int m_wg = mp0 * 32, n_wg = np0 * 32;
+    for (int r0 = 0; r0 < r_steps; r0 += C::kResSteps) {
+      const int S = min(C::kResSteps, r_steps - r0);
+      const int blocks = C::kChunks * S;
+      __syncthreads();   // LDS free (main loop or the previous pass is done)
+      for (int b = wave; b < blocks; b += C::kWaves) {
+        const bool is_a = b < C::kChunksA * S;
+        const int bb = is_a ? b : b - C::kChunksA * S;
+        const int g = bb / S, rs = bb % S;
+        const int col = 16 * (r0 + rs) + 8 * h;
+        const uint16_t* src;
+        if (is_a) {
+          const int m = min(m_wg + 32 * g + l32, M - 1);
+          src = a.lora_act + (size_t)m * R + col;
+        } else {
+          const int n = min(n_wg + 32 * g + l32, N - 1);
+          src = a.proj_up + (size_t)n * R + col;
+        }
+        __builtin_amdgcn_global_load_lds(src, LDS_PTR(smem + b * 1024), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      __syncthreads();
+      for (int rs = 0; rs < S; ++rs) {
+        bf16x8 la[TM], pu[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m_w + 32 * i + l32;
-      u32x4 v = zero4();
-      if (rs < r_steps && m < M) v = *reinterpret_cast<const u32x4*>(a.lora_act + (size_t)m * R + r0 + 8 * h);
-      la[i] = __builtin_bit_cast(bf16x8, v);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      u32x4 v = zero4();
-      if (rs < r_steps && ncol[j] < N) v = *reinterpret_cast<const u32x4*>(a.proj_up + (size_t)ncol[j] * R + r0 + 8 * h);
-      pu[j] = __builtin_bit_cast(bf16x8, v);
-    }
-  };
-  if (r_steps > 0) {
-    bf16x8 la0[TM], pu0[TN], la1[TM], pu1[TN];
-    load_res(la0, pu0, 0);
-    load_res(la1, pu1, 1);
-    for (int rs = 0; rs < r_steps; rs += 2) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
+          la[i] = *reinterpret_cast<const bf16x8*>(smem + ((wave_m * TM + i) * S + rs) * 1024 + lane * 16);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la0[i], pu0[j], acc[i][j], 0, 0, 0);
-      load_res(la0, pu0, rs + 2);
-      if (rs + 1 < r_steps) {
+          pu[j] = *reinterpret_cast<const bf16x8*>(smem + (C::kChunksA * S + (wave_n * TN + j) * S + rs) * 1024 + lane * 16);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la1[i], pu1[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], pu[j], acc[i][j], 0, 0, 0);
       }
-      load_res(la1, pu1, rs + 3);
     }
   }
 
-  // bf16 output through LDS (free after the main loop): each wave writes one
-  // 32-row slice of its tile row-major, then stores whole 16-byte row pieces
-  constexpr int kCols = 32 * TN;                 // columns of a wave tile
-  constexpr int kPieces = kCols / 8;             // 16-byte pieces per row
+  // bf16 output through LDS: each wave writes one 32-row slice of its tile
+  // row-major, then stores whole 16-byte row pieces
+  __syncthreads();
+  constexpr int kCols = 32 * TN;
+  constexpr int kPieces = kCols / 8;
   uint16_t* stage_out = reinterpret_cast<uint16_t*>(smem + wave * (32 * kCols * 2));
   const bool vec_ok = (N % 8) == 0;
 #pragma unroll
@@ -270,8 +309,6 @@ hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
   using C = LdsCfg<WM, WN, TM, TN>;
   const int64_t tiles = ((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM);
   const unsigned lds = 2 * C::kStageBytes;
-  // more than 64 KB of dynamic LDS must be allowed explicitly (set on every
-  // launch: cheap, and correct for whichever device is current)
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -46,8 +46,9 @@
  *    multiple of 16 (SVDQ_ERR_UNSUPPORTED otherwise). Every pointer must be
  *    16-byte aligned (SVDQ_ERR_ALIGN).
  *  - The quantisation step (also inside svdq_linear_w4a4) needs x, proj_down,
- *    lora_act and the packed activation buffer each below 2 GiB
- *    (SVDQ_ERR_UNSUPPORTED otherwise).
+ *    lora_act and the packed activation buffer each below 2 GiB, and the
+ *    GEMM on packed operands needs the packed activation and packed weight
+ *    buffers each below 2 GiB (SVDQ_ERR_UNSUPPORTED otherwise).
  *  - NaN or Inf inputs are not checked; results are then unspecified.
  */
 #ifndef SVDQ_H

@@ -126,6 +126,8 @@ def gemm(**kw):
     (dict(act_layout=3), 8), (dict(act_layout=1), 8),                         # ascales must be NULL
     (dict(act_layout=1, ascales=None), 8),                                     # needs packed weights
     (dict(act_layout=1, ascales=None, layout=1, wscales=None, qact=None), 1),
+    (dict(act_layout=1, ascales=None, layout=1, wscales=None, M=1 << 20, K=1 << 12), 3),   # packed act > 2 GiB
+    (dict(act_layout=1, ascales=None, layout=1, wscales=None, N=1 << 20, K=1 << 12), 3),   # packed weight > 2 GiB
 ])
 def test_gemm_rejections(kw, code):
     assert gemm(**kw) == code
@@ -161,6 +163,7 @@ def test_linear_rejections():
     assert lin(y=fake(10)) == 6          # y overlaps the workspace
     assert lin(K=17) == 2
     assert lin(M=0) == 0
+    assert lin(layout=1, wscales=None, N=1 << 20, K=1 << 12) == 3   # packed weight > 2 GiB
 
 
 @no_gpu_only

@@ -67,6 +67,7 @@ def gemm_case(ops, cfg, packed=False, with_bias=True, zero_weight=False, rows=No
     dict(M=130, K=336, N=4100, R=32, kind="dit", seed=24),     # K % 64 != 0, ragged N
     dict(M=257, K=1024, N=257, R=0, kind="dit", seed=25),      # R = 0
     dict(M=96, K=10240, N=256, R=128, kind="swiglu", seed=26),
+    dict(M=300, K=512, N=700, R=272, kind="dit", seed=27),      # rank in three passes (8 + 8 + 1 steps)
 ])
 @pytest.mark.parametrize("packed", [False, True])
 def test_gemm_parity(gpu_lib, cfg, packed):
@@ -110,6 +111,8 @@ def test_gemm_deterministic(gpu_lib):
     dict(M=200, K=3840, N=384, R=128, kind="dit", seed=21),
     dict(M=130, K=336, N=4100, R=32, kind="dit", seed=24),
     dict(M=257, K=1024, N=257, R=0, kind="dit", seed=25),
+    dict(M=300, K=512, N=700, R=272, kind="dit", seed=27),
+    dict(M=33, K=64, N=40, R=16, kind="dit", seed=28),          # one panel: only the peeled iteration
 ])
 def test_gemm_packed_activations(gpu_lib, cfg):
     """Packed activations (placed by the oracle's statement of the layout) through the
