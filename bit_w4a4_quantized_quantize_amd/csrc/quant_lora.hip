@@ -6,7 +6,8 @@
 //
 // A workgroup owns 16*RT rows and the whole K range, so the down-projection
 // needs no cross-workgroup reduction: its waves take interleaved 32-wide K
-// steps (loading the operands two steps ahead while working on the current one)
+// steps (loading the operands two steps ahead while working on the current one,
+// three register sets rotated by name)
 // and their partial sums are added in a fixed order through LDS at the end
 // (deterministic). Each lane holds 8 consecutive k of one row (a 16-byte
 // load), which is at once the A fragment of v_mfma_f32_16x16x32_bf16 and half
@@ -57,9 +58,13 @@ struct QLArgs {
   uint8_t* ascales;    // canonical [K/16, M] (unused when packed)
   uint16_t* lora_act;  // [M, R]
   int M, K, R;
+  int r_base;          // first of the (up to kRChunk) lora_act columns this launch computes
 };
 
-template <int RT, int kWaves, bool PACKED>
+// QUANT: write the codes and scales; LORA: compute lora_act columns
+// r_base .. r_base + kRChunk - 1. A rank above kRChunk takes further launches
+// with QUANT = false.
+template <int RT, int kWaves, bool PACKED, bool QUANT, bool LORA>
 __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
   constexpr int ROWS = 16 * RT;
   __shared__ f32x4 s_red[kWaves / 2][RT][8][64];
@@ -91,11 +96,8 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
   const auto rsc = make_rsrc(a.ascales, s_bytes);
   const auto rl = make_rsrc(a.lora_act, l_bytes);
 
-  const int n_chunks = R > 0 ? (R + kRChunk - 1) / kRChunk : 1;
-  for (int rc_i = 0; rc_i < n_chunks; ++rc_i) {
-    const bool do_quant = rc_i == 0;
-    const int r_base = rc_i * kRChunk;
-    const int rcol = r_base + 8 * c;
+  {
+    const int rcol = a.r_base + 8 * c;
     const bool r_in = rcol < R;
 
     f32x4 acc[RT][8];
@@ -114,9 +116,8 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
         const uint32_t off = k_in ? ((uint32_t)m * K + kg) * 2 : x_bytes;
         r.x[t] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
       }
-      r.sm = zero4();
-      if (do_quant) r.sm = __builtin_amdgcn_raw_buffer_load_b128(rsm, k_in ? kg * 2 : K * 2, 0, 0);
-      if (R > 0) {
+      if (QUANT) r.sm = __builtin_amdgcn_raw_buffer_load_b128(rsm, k_in ? kg * 2 : K * 2, 0, 0);
+      if (LORA) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint32_t off = (r_in && k_in) ? ((uint32_t)(kg + j) * R + rcol) * 2 : pd_bytes;
@@ -125,16 +126,12 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
       }
     };
 
-    // two steps of lookahead (three register sets in flight)
-    StepRegs<RT> cur, nxt, nxt2;
-    load(cur, wave);
-    load(nxt, wave + kWaves);
-    for (int st = wave; st < steps; st += kWaves) {
-      load(nxt2, st + 2 * kWaves);
+    // one 32-wide step on the operands in `cur`
+    auto process = [&](const StepRegs<RT>& cur, int st) {
       const int kg = st * 32 + 8 * g;
       const bool k_in = kg < K;
 
-      if (do_quant) {
+      if (QUANT) {
         float sm[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -178,7 +175,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
         }
       }
 
-      if (R > 0) {
+      if (LORA) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           u32x4 f;
@@ -193,11 +190,26 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
                                                                 acc[t][i], 0, 0, 0);
         }
       }
-      cur = nxt;
-      nxt = nxt2;
+    };
+
+    // two steps of lookahead: three register sets used in rotation by name
+    // (the loop is unrolled by three), so a load's destination is never
+    // copied while it is in flight
+    StepRegs<RT> r0, r1, r2;
+    load(r0, wave);
+    load(r1, wave + kWaves);
+    for (int st = wave; st < steps; st += 3 * kWaves) {
+      load(r2, st + 2 * kWaves);
+      process(r0, st);
+      if (st + kWaves >= steps) break;
+      load(r0, st + 3 * kWaves);
+      process(r1, st + kWaves);
+      if (st + 2 * kWaves >= steps) break;
+      load(r1, st + 4 * kWaves);
+      process(r2, st + 2 * kWaves);
     }
 
-    if (R > 0) {
+    if (LORA) {
       // fixed-order tree over the waves (8: 4..7 -> 0..3, 2,3 -> 0,1, 1 -> 0)
 #pragma unroll
       for (int half = kWaves / 2; half >= 1; half >>= 1) {
@@ -240,17 +252,31 @@ int quant_lora_row_tiles(int64_t M) { return (M + 31) / 32 >= 256 ? 2 : 1; }
 hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down,
                              uint8_t* qact, uint8_t* ascales, uint16_t* lora_act, int64_t M,
                              int64_t K, int64_t R, bool packed_out, hipStream_t stream) {
-  QLArgs a{x, smooth, proj_down, qact, ascales, lora_act, (int)M, (int)K, (int)R};
+  QLArgs a{x, smooth, proj_down, qact, ascales, lora_act, (int)M, (int)K, (int)R, 0};
   const int rt = quant_lora_row_tiles(M);
   dim3 grid((unsigned)((M + 16 * rt - 1) / (16 * rt)));
   // 16 rows: 8 waves per workgroup (2 per SIMD); 32 rows: 4 waves, so each wave
   // may hold two row tiles of operands and accumulators in registers
-  if (rt == 2) {
-    if (packed_out) hipLaunchKernelGGL((quant_lora_kernel<2, 4, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((quant_lora_kernel<2, 4, false>), grid, dim3(256), 0, stream, a);
-  } else {
-    if (packed_out) hipLaunchKernelGGL((quant_lora_kernel<1, 8, true>), grid, dim3(512), 0, stream, a);
-    else hipLaunchKernelGGL((quant_lora_kernel<1, 8, false>), grid, dim3(512), 0, stream, a);
+  auto launch = [&](bool quant, bool lora) {
+#define SVDQ_QL(RT, W, P, Q, L) hipLaunchKernelGGL((quant_lora_kernel<RT, W, P, Q, L>), grid, dim3(64 * W), 0, stream, a)
+#define SVDQ_QL_RT(RT, W)                                                              \
+    if (packed_out) {                                                                  \
+      if (quant && lora) SVDQ_QL(RT, W, true, true, true);                             \
+      else if (quant) SVDQ_QL(RT, W, true, true, false);                               \
+      else SVDQ_QL(RT, W, true, false, true);                                          \
+    } else {                                                                           \
+      if (quant && lora) SVDQ_QL(RT, W, false, true, true);                            \
+      else if (quant) SVDQ_QL(RT, W, false, true, false);                              \
+      else SVDQ_QL(RT, W, false, false, true);                                         \
+    }
+    if (rt == 2) { SVDQ_QL_RT(2, 4) } else { SVDQ_QL_RT(1, 8) }
+#undef SVDQ_QL_RT
+#undef SVDQ_QL
+  };
+  launch(true, R > 0);
+  for (int64_t r0 = kRChunk; r0 < R; r0 += kRChunk) {
+    a.r_base = (int)r0;
+    launch(false, true);
   }
   return hipGetLastError();
 }
