@@ -25,6 +25,11 @@ than itself: the E2M1 grid and bit structure, the e4m3fn range, exhaustive
 decode tables, torch's float8_e4m3fn cast, exact rational brute force on tiny
 shapes, the int64-exact form of the main term, and the formula's closed-form
 special cases (R = 0, qweight = 0, lossless inputs).
+
+Parity unpinned: agreement with third-party implementations of the layer
+(nunchaku, vLLM, the CuTe kernels). The pages publish no checkpoint, kernel
+output or test vector, so the activation quantiser is pinned only to the
+readings stated in svdq.py, not to any published artifact.
 """
 
 from . import formats, svdq, repack  # noqa: F401

@@ -163,3 +163,25 @@ def test_normwise_metric():
     a = np.array([[3.0, 4.0]])
     assert S.normwise_rel_err(a, a) == 0.0
     assert S.normwise_rel_err(np.array([[3.0, 0.0]]), a) == pytest.approx(4.0 / 5.0)
+
+
+def test_lowrank_exact_rational_brute_force():
+    """(x @ proj_down) @ proj_up^T on a tiny slice with Python Fractions (exact), against
+    the oracle's float64 result within float64 rounding of the sums."""
+    d = _tiny()
+    rows, cols = [0, 7, 63], [0, 5, 127]
+    x = F.bf16_to_f64(d["x"])
+    pd = F.bf16_to_f64(d["proj_down"])
+    pu = F.bf16_to_f64(d["proj_up"])
+    K, R = pd.shape
+    lr = S.lowrank(d["x"], d["proj_down"], d["proj_up"])
+    down = S.lowrank_down(d["x"], d["proj_down"])
+    for m in rows:
+        t = [sum(Fraction(float(x[m, k])) * Fraction(float(pd[k, r])) for k in range(K)) for r in range(R)]
+        mag = [sum(abs(Fraction(float(x[m, k])) * Fraction(float(pd[k, r]))) for k in range(K)) for r in range(R)]
+        for r in range(R):
+            assert abs(Fraction(float(down[m, r])) - t[r]) <= mag[r] * Fraction(K + 1, 2 ** 52)
+        for n in cols:
+            exact = sum(t[r] * Fraction(float(pu[n, r])) for r in range(R))
+            bound = sum(mag[r] * abs(Fraction(float(pu[n, r]))) for r in range(R)) * Fraction(K + R + 2, 2 ** 52)
+            assert abs(Fraction(float(lr[m, n])) - exact) <= bound
