@@ -101,15 +101,17 @@ int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
   return SVDQ_OK;
 }
 
+// Scratch of the quantisation step: fp32 partial sums of the down-projection
+// when it splits K across workgroups (small M), otherwise none.
 size_t quant_ws_bytes(int64_t M, int64_t K, int64_t R) {
-  (void)M; (void)K; (void)R;
-  return 0;   // the fused quantisation / down-projection needs no scratch
+  return R > 0 ? align256(svdq::quant_lora_workspace_bytes(M, K, R)) : 0;
 }
 
 // Whole-layer workspace: the quantised activations (canonical, or packed when
-// the weight is packed: the packed form is never smaller) and lora_act.
+// the weight is packed: the packed form is never smaller), lora_act, and the
+// quantisation step's scratch.
 struct LinearWs {
-  size_t act, ascales, lora, total;
+  size_t act, ascales, lora, partial, total;
 };
 LinearWs linear_ws(int64_t M, int64_t K, int64_t R) {
   LinearWs w;
@@ -118,13 +120,14 @@ LinearWs linear_ws(int64_t M, int64_t K, int64_t R) {
   const size_t canonical_end = align256(w.ascales + (size_t)(K / 16) * (size_t)M);
   const size_t packed_end = align256(svdq::packed_weight_bytes(M, K));
   w.lora = canonical_end > packed_end ? canonical_end : packed_end;
-  w.total = w.lora + (size_t)M * (size_t)R * 2;
+  w.partial = align256(w.lora + (size_t)M * (size_t)R * 2);
+  w.total = w.partial + quant_ws_bytes(M, K, R);
   return w;
 }
 
 // enqueue a1 (+ a2): pointers already validated
 int run_quantize(const void* x, const void* smooth, int64_t M, int64_t K, const void* proj_down,
-                 int64_t R, void* qact, void* ascales, void* lora_act, bool packed_out,
+                 int64_t R, void* qact, void* ascales, void* lora_act, void* scratch, bool packed_out,
                  hipStream_t s) {
   hipError_t e;
   if (R == 0 && !packed_out) {
@@ -133,8 +136,8 @@ int run_quantize(const void* x, const void* smooth, int64_t M, int64_t K, const 
   } else {
     e = svdq::launch_quant_lora(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
                                 static_cast<const uint16_t*>(proj_down), static_cast<uint8_t*>(qact),
-                                static_cast<uint8_t*>(ascales), static_cast<uint16_t*>(lora_act), M, K,
-                                R, packed_out, s);
+                                static_cast<uint8_t*>(ascales), static_cast<uint16_t*>(lora_act),
+                                static_cast<float*>(scratch), M, K, R, packed_out, s);
   }
   if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "quantisation launch: %s", hipGetErrorString(e));
   return ok();
@@ -192,8 +195,6 @@ int svdq_quantize_act(const void* x, const void* smooth, int64_t M, int64_t K,
                       const void* proj_down, int64_t R, int act_layout, void* qact,
                       void* ascales, void* lora_act, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;   // no scratch is needed (size query returns 0)
   int st = check_mk(M, K, R);
   if (st) return st;
   if ((st = check_rsrc_sizes(M, K, R))) return st;
@@ -218,15 +219,24 @@ int svdq_quantize_act(const void* x, const void* smooth, int64_t M, int64_t K,
     const void* ptrs[] = {proj_down, lora_act};
     if ((st = check_ptrs(names, ptrs, 2))) return st;
   }
+  const size_t ws_need = quant_ws_bytes(M, K, R);
+  if (ws_need > 0) {
+    if (workspace_bytes < ws_need)
+      return fail(SVDQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws_need);
+    const char* names[] = {"workspace"};
+    const void* ptrs[] = {workspace};
+    if ((st = check_ptrs(names, ptrs, 1))) return st;
+  }
   const size_t qbytes = packed ? svdq::packed_weight_bytes(M, K) : (size_t)M * (K / 2);
   const Range in[] = {range("x", x, (size_t)M * K * 2), range("smooth", smooth, (size_t)K * 2),
                       range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2)};
   const Range out[] = {range("qact", qact, qbytes),
                        range("ascales", packed ? nullptr : ascales, (size_t)(K / 16) * M),
-                       range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2)};
-  if ((st = check_alias(in, 3, out, 3))) return st;
-  return run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora_act, packed,
-                      static_cast<hipStream_t>(stream));
+                       range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
+                       range("workspace", ws_need > 0 ? workspace : nullptr, ws_need)};
+  if ((st = check_alias(in, 3, out, 4))) return st;
+  return run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora_act,
+                      ws_need > 0 ? workspace : nullptr, packed, static_cast<hipStream_t>(stream));
 }
 
 size_t svdq_repack_weight_bytes(int64_t N, int64_t K) {
@@ -429,7 +439,8 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   void* ascales = packed ? nullptr : (void*)(w + ws.ascales);
   void* lora = R > 0 ? (void*)(w + ws.lora) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora, packed, s))) return st;
+  void* scratch = ws.total > ws.partial ? (void*)(w + ws.partial) : nullptr;
+  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora, scratch, packed, s))) return st;
   svdq::GemmArgs a;
   a.qact = static_cast<const uint8_t*>(qact);
   a.ascales = static_cast<const uint8_t*>(ascales);

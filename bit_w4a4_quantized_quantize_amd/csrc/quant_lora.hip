@@ -59,12 +59,14 @@ struct QLArgs {
   uint16_t* lora_act;  // [M, R]
   int M, K, R;
   int r_base;          // first of the (up to kRChunk) lora_act columns this launch computes
+  float* partial;      // [splits, M, R] fp32 partial sums when K is split (else NULL)
+  int split_steps;     // 32-wide K steps per split (blockIdx.y selects the split)
 };
 
 // QUANT: write the codes and scales; LORA: compute lora_act columns
 // r_base .. r_base + kRChunk - 1. A rank above kRChunk takes further launches
 // with QUANT = false.
-template <int RT, int kWaves, bool PACKED, bool QUANT, bool LORA>
+template <int RT, int kWaves, int DEPTH, bool PACKED, bool QUANT, bool LORA>
 __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
   constexpr int ROWS = 16 * RT;
   __shared__ f32x4 s_red[kWaves / 2][RT][8][64];
@@ -75,6 +77,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
   const int c = lane & 15;   // row within a 16-row tile; column group of proj_down
   const int g = lane >> 4;   // k group of 8 within a 32-wide step
   const int m0 = blockIdx.x * ROWS;
+  const int ks = blockIdx.y;
   const int M = a.M, K = a.K, R = a.R;
   const int MP = (M + 31) / 32;
   const int KP = (K + 63) / 64;
@@ -82,6 +85,8 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
   // and zero scales (the GEMM multiplies them by the weight's zero padding); its
   // rows beyond M inside the last 32-row panel are written as zeros too
   const int steps = PACKED ? 2 * KP : (K + 31) / 32;
+  const int s_begin = ks * a.split_steps;
+  const int s_end = min(steps, s_begin + a.split_steps);
   const uint32_t code_bytes = (uint32_t)MP * KP * 1024;
 
   const uint32_t x_bytes = (uint32_t)M * K * 2;
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
     // operands of one 32-wide step; positions outside the tensors read as zero
     auto load = [&](StepRegs<RT>& r, int st) {
       const int kg = st * 32 + 8 * g;
-      const bool k_in = st < steps && kg < K;
+      const bool k_in = st < s_end && kg < K;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int m = m0 + 16 * t + c;
@@ -161,11 +166,14 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
           packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[6] * inv), snap21(v[7] * inv), 1.0f, 3);
           if (PACKED) {
             const int pp = kg >> 6, tt = (kg >> 4) & 3, hh = (kg >> 3) & 1;
+            // rows of the last 32-row panel beyond M are written (as zeros); a
+            // workgroup's rows past that panel are not stored at all
             const int q = m >> 5, cc = m & 31;
+            const bool in_panel = q < MP;
             const uint32_t chunk = (uint32_t)pp * MP + q;
-            __builtin_amdgcn_raw_buffer_store_b32(packed, rq, chunk * 1024 + ((hh * 32 + cc) * 4 + tt) * 4, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(packed, rq, in_panel ? chunk * 1024 + ((hh * 32 + cc) * 4 + tt) * 4 : q_bytes, 0, 0);
             if (hh == 0)
-              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rq, code_bytes + chunk * 128 + cc * 4 + tt, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rq, in_panel ? code_bytes + chunk * 128 + cc * 4 + tt : q_bytes, 0, 0);
           } else {
             const bool ok = k_in && m < M;
             __builtin_amdgcn_raw_buffer_store_b32(packed, rq, ok ? (uint32_t)m * (K / 2) + kg / 2 : q_bytes, 0, 0);
@@ -192,21 +200,33 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
       }
     };
 
-    // two steps of lookahead: three register sets used in rotation by name
-    // (the loop is unrolled by three), so a load's destination is never
-    // copied while it is in flight
-    StepRegs<RT> r0, r1, r2;
-    load(r0, wave);
-    load(r1, wave + kWaves);
-    for (int st = wave; st < steps; st += 3 * kWaves) {
-      load(r2, st + 2 * kWaves);
-      process(r0, st);
-      if (st + kWaves >= steps) break;
-      load(r0, st + 3 * kWaves);
-      process(r1, st + kWaves);
-      if (st + 2 * kWaves >= steps) break;
-      load(r1, st + 4 * kWaves);
-      process(r2, st + 2 * kWaves);
+    // DEPTH steps of lookahead: DEPTH + 1 register sets used in rotation by
+    // name (the loop is unrolled by DEPTH + 1), so a load's destination is
+    // never copied while it is in flight
+    if constexpr (DEPTH == 2) {
+      StepRegs<RT> r0, r1, r2;
+      load(r0, s_begin + wave);
+      load(r1, s_begin + wave + kWaves);
+      for (int st = s_begin + wave; st < s_end; st += 3 * kWaves) {
+        load(r2, st + 2 * kWaves);
+        process(r0, st);
+        if (st + kWaves >= s_end) break;
+        load(r0, st + 3 * kWaves);
+        process(r1, st + kWaves);
+        if (st + 2 * kWaves >= s_end) break;
+        load(r1, st + 4 * kWaves);
+        process(r2, st + 2 * kWaves);
+      }
+    } else {
+      StepRegs<RT> r0, r1;
+      load(r0, s_begin + wave);
+      for (int st = s_begin + wave; st < s_end; st += 2 * kWaves) {
+        load(r1, st + kWaves);
+        process(r0, st);
+        if (st + kWaves >= s_end) break;
+        load(r0, st + 2 * kWaves);
+        process(r1, st + kWaves);
+      }
     }
 
     if (LORA) {
@@ -230,53 +250,126 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
       }
       if (wave == 0) {
         // lane holds rows 16t + 4g + q and columns rcol .. rcol+7
+        const uint32_t p_bytes = a.partial != nullptr ? (uint32_t)gridDim.y * M * R * 4 : 0u;
+        const auto rp = make_rsrc(a.partial, p_bytes);
 #pragma unroll
         for (int t = 0; t < RT; ++t)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int m = m0 + 16 * t + 4 * g + q;
-            u32x4 o;
+            const bool ok = r_in && m < M;
+            if (a.partial == nullptr) {
+              u32x4 o;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(acc[t][2 * w][q], acc[t][2 * w + 1][q]);
-            __builtin_amdgcn_raw_buffer_store_b128(o, rl, r_in ? ((uint32_t)m * R + rcol) * 2 : l_bytes, 0, 0);
+              for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(acc[t][2 * w][q], acc[t][2 * w + 1][q]);
+              __builtin_amdgcn_raw_buffer_store_b128(o, rl, ok ? ((uint32_t)m * R + rcol) * 2 : l_bytes, 0, 0);
+            } else {
+              u32x4 o0, o1;
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                o0[w] = __float_as_uint(acc[t][w][q]);
+                o1[w] = __float_as_uint(acc[t][4 + w][q]);
+              }
+              const uint32_t off = ok ? (((uint32_t)ks * M + m) * R + rcol) * 4 : p_bytes;
+              __builtin_amdgcn_raw_buffer_store_b128(o0, rp, off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(o1, rp, ok ? off + 16 : p_bytes, 0, 0);
+            }
           }
       }
     }
   }
 }
 
+// lora_act = bf16(sum over the K splits of the fp32 partials), the splits
+// added in index order (deterministic). One thread per 8 consecutive columns.
+__global__ __launch_bounds__(256) void lora_reduce_kernel(const float* __restrict__ partial,
+                                                          uint16_t* __restrict__ lora, int M, int R,
+                                                          int splits) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // group of 8 columns
+  const int64_t groups = (int64_t)M * (R / 8);
+  if (i >= groups) return;
+  const size_t plane = (size_t)M * R;
+  f32x4 s0 = *reinterpret_cast<const f32x4*>(partial + i * 8);
+  f32x4 s1 = *reinterpret_cast<const f32x4*>(partial + i * 8 + 4);
+  for (int k = 1; k < splits; ++k) {
+    s0 += *reinterpret_cast<const f32x4*>(partial + k * plane + i * 8);
+    s1 += *reinterpret_cast<const f32x4*>(partial + k * plane + i * 8 + 4);
+  }
+  u32x4 o;
+  o[0] = pack_bf16x2(s0[0], s0[1]);
+  o[1] = pack_bf16x2(s0[2], s0[3]);
+  o[2] = pack_bf16x2(s1[0], s1[1]);
+  o[3] = pack_bf16x2(s1[2], s1[3]);
+  *reinterpret_cast<u32x4*>(lora + i * 8) = o;
+}
+
 }  // namespace
 
-int quant_lora_row_tiles(int64_t M) { return (M + 31) / 32 >= 256 ? 2 : 1; }
+// The down-projection path: a workgroup of 8 waves owns 32 rows (2 row tiles
+// per wave, accumulators for all 128 columns of an R chunk, one step of
+// lookahead), so each proj_down element read through a CU's L1 serves 32 rows
+// and each in-register transpose of it serves two row tiles. When that leaves
+// fewer than 256 workgroups, K is split across workgroups (blockIdx.y) and the
+// fp32 partials are reduced by a second kernel. (Measured on MI355X against 16
+// rows per workgroup and against 64 rows with 4 waves, which runs out of
+// registers: 20.1 us vs 22.2 and 27.5 at M=4096, K=3840, R=128.)
+constexpr int kLoraRT = 2;
+constexpr int kLoraWaves = 8;
+constexpr int kLoraDepth = 1;
+
+int quant_lora_splits(int64_t M, int64_t K, int64_t R) {
+  if (R <= 0) return 1;
+  const int64_t row_blocks = (M + 16 * kLoraRT - 1) / (16 * kLoraRT);
+  const int64_t steps = 2 * ((K + 63) / 64);
+  int64_t ks = (256 + row_blocks - 1) / row_blocks;
+  ks = ks < 1 ? 1 : ks;
+  ks = ks > 16 ? 16 : ks;
+  while (ks > 1 && steps / ks < 2 * kLoraWaves) --ks;               // at least 2 steps per wave
+  while (ks > 1 && ks * M * R * 4 >= (int64_t(1) << 31)) --ks;      // 32-bit partial offsets
+  return (int)ks;
+}
+
+size_t quant_lora_workspace_bytes(int64_t M, int64_t K, int64_t R) {
+  const int ks = quant_lora_splits(M, K, R);
+  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)R * 4 : 0;
+}
 
 hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down,
-                             uint8_t* qact, uint8_t* ascales, uint16_t* lora_act, int64_t M,
-                             int64_t K, int64_t R, bool packed_out, hipStream_t stream) {
-  QLArgs a{x, smooth, proj_down, qact, ascales, lora_act, (int)M, (int)K, (int)R, 0};
-  const int rt = quant_lora_row_tiles(M);
-  dim3 grid((unsigned)((M + 16 * rt - 1) / (16 * rt)));
-  // 16 rows: 8 waves per workgroup (2 per SIMD); 32 rows: 4 waves, so each wave
-  // may hold two row tiles of operands and accumulators in registers
-  auto launch = [&](bool quant, bool lora) {
-#define SVDQ_QL(RT, W, P, Q, L) hipLaunchKernelGGL((quant_lora_kernel<RT, W, P, Q, L>), grid, dim3(64 * W), 0, stream, a)
-#define SVDQ_QL_RT(RT, W)                                                              \
-    if (packed_out) {                                                                  \
-      if (quant && lora) SVDQ_QL(RT, W, true, true, true);                             \
-      else if (quant) SVDQ_QL(RT, W, true, true, false);                               \
-      else SVDQ_QL(RT, W, true, false, true);                                          \
-    } else {                                                                           \
-      if (quant && lora) SVDQ_QL(RT, W, false, true, true);                            \
-      else if (quant) SVDQ_QL(RT, W, false, true, false);                              \
-      else SVDQ_QL(RT, W, false, false, true);                                         \
+                             uint8_t* qact, uint8_t* ascales, uint16_t* lora_act, float* partial,
+                             int64_t M, int64_t K, int64_t R, bool packed_out, hipStream_t stream) {
+  QLArgs a{x, smooth, proj_down, qact, ascales, lora_act, (int)M, (int)K, (int)R, 0, nullptr, 0};
+  const int steps_all = packed_out ? (int)(2 * ((K + 63) / 64)) : (int)((K + 31) / 32);
+  if (R == 0) {
+    // quantisation only: 16 rows and the whole K per workgroup of 8 waves
+    a.split_steps = steps_all;
+    dim3 grid((unsigned)((M + 15) / 16));
+    if (packed_out) hipLaunchKernelGGL((quant_lora_kernel<1, 8, 2, true, true, false>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((quant_lora_kernel<1, 8, 2, false, true, false>), grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int ks = quant_lora_splits(M, K, R);
+  a.split_steps = (steps_all + ks - 1) / ks;
+  a.partial = ks > 1 ? partial : nullptr;
+  dim3 grid((unsigned)((M + 16 * kLoraRT - 1) / (16 * kLoraRT)), (unsigned)ks);
+  auto launch = [&](bool quant) {
+#define SVDQ_QL(P, Q) hipLaunchKernelGGL((quant_lora_kernel<kLoraRT, kLoraWaves, kLoraDepth, P, Q, true>), grid, \
+                                         dim3(64 * kLoraWaves), 0, stream, a)
+    if (packed_out) {
+      if (quant) SVDQ_QL(true, true); else SVDQ_QL(true, false);
+    } else {
+      if (quant) SVDQ_QL(false, true); else SVDQ_QL(false, false);
     }
-    if (rt == 2) { SVDQ_QL_RT(2, 4) } else { SVDQ_QL_RT(1, 8) }
-#undef SVDQ_QL_RT
 #undef SVDQ_QL
   };
-  launch(true, R > 0);
+  launch(true);
   for (int64_t r0 = kRChunk; r0 < R; r0 += kRChunk) {
     a.r_base = (int)r0;
-    launch(false, true);
+    launch(false);
+  }
+  if (ks > 1) {
+    const int64_t groups = M * (R / 8);
+    hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const float*>(partial), lora_act, (int)M, (int)R, ks);
   }
   return hipGetLastError();
 }

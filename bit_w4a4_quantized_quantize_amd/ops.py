@@ -48,12 +48,15 @@ def _stream(device=None):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=None, packed=False):
+def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=None, packed=False,
+                 workspace=None):
     """quant(x * smooth) and, with proj_down, lora_act = x @ proj_down.
 
     Returns (qact, ascales, lora_act): canonical qact uint8 [M, K/2] and ascales
     uint8 [K/16, M]; or, with packed=True, one packed uint8 buffer (the packed
     weight layout with rows = tokens) and ascales None. lora_act bf16 [M, R] or None.
+    workspace: optional uint8 device tensor of at least
+    quantize_act_workspace_bytes(M, K, R) bytes (allocated here when None).
     """
     _need(x, "x", torch.bfloat16, 2)
     M, K = x.shape
@@ -76,10 +79,19 @@ def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=No
             ascales = torch.empty((K // 16, M), dtype=torch.uint8, device=dev)
     if R > 0 and lora_act is None:
         lora_act = torch.empty((M, R), dtype=torch.bfloat16, device=dev)
+    ws_need = quantize_act_workspace_bytes(M, K, R)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else _need(workspace, "workspace", torch.uint8, 1).numel()
     _lib.check("svdq_quantize_act", L.svdq_quantize_act(
         _p(x), _p(smooth), M, K, _p(proj_down), R, ACT_PACKED if packed else ACT_CANONICAL,
-        _p(qact), _p(ascales), _p(lora_act) if R > 0 else None, None, 0, _stream(dev)))
+        _p(qact), _p(ascales), _p(lora_act) if R > 0 else None, _p(workspace), ws_bytes, _stream(dev)))
     return qact, ascales, (lora_act if R > 0 else None)
+
+
+def quantize_act_workspace_bytes(M, K, R):
+    """Scratch bytes svdq_quantize_act needs (fp32 partials when K is split)."""
+    return int(_lib.lib().svdq_quantize_act_workspace_bytes(M, K, R))
 
 
 def repack_weight(qweight, wscales):

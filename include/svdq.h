@@ -107,8 +107,10 @@ const char* svdq_last_error(void);
  *   proj_down [K, R] bf16, lora_act [M, R] bf16: used when R > 0 (both
  *     required then); lora_act = bf16(x @ proj_down) with fp32 accumulation.
  *   workspace: device scratch of at least svdq_quantize_act_workspace_bytes(M, K, R)
- *     bytes; the fused kernel needs none, so that size is 0 and workspace may
- *     be NULL (the argument keeps the signature stable).
+ *     bytes (SVDQ_ERR_WORKSPACE if smaller). It holds fp32 partial sums of the
+ *     down-projection when K is split across workgroups, which happens for
+ *     R > 0 and small M; otherwise the size is 0 and workspace may be NULL.
+ *     Its contents on entry do not matter and are unspecified afterwards.
  * qact and ascales are bit-exact functions of x and smooth.
  */
 size_t svdq_quantize_act_workspace_bytes(int64_t M, int64_t K, int64_t R);

@@ -92,10 +92,25 @@ def test_quantize_act_rejections(kw, code):
     assert _lib.lib().svdq_last_error().decode() != ""
 
 
-def test_quantize_act_needs_no_workspace():
+def test_quantize_act_workspace_sizes():
+    """Scratch is needed only when the down-projection splits K (R > 0, few 64-row blocks):
+    fp32 partials [splits, M, R]; none for R = 0 or many rows."""
     L = _lib.lib()
-    for M, K, R in [(4096, 3840, 128), (64, 256, 16), (16896, 10240, 128), (7, 16, 0)]:
+    for M, K, R in [(64, 256, 16), (16896, 10240, 128), (7, 16, 0), (4096, 3840, 0)]:
         assert L.svdq_quantize_act_workspace_bytes(M, K, R) == 0
+    ws = L.svdq_quantize_act_workspace_bytes(4096, 3840, 128)
+    assert ws >= 2 * 4096 * 128 * 4 and ws % (4096 * 128 * 4) == 0
+    assert L.svdq_linear_workspace_bytes(4096, 10240, 3840, 128) >= ws + 4096 * 128 * 2
+
+
+@no_gpu_only
+def test_quantize_act_workspace_rejections():
+    big = dict(M=4096, K=3840, R=128)
+    need = _lib.lib().svdq_quantize_act_workspace_bytes(4096, 3840, 128)
+    assert q(ws_bytes=need - 1, **big) == 5
+    assert q(ws=None, **big) == 1
+    assert q(ws=fake(7) + 8, **big) == 4
+    assert q(ws=fake(6), **big) == 6          # overlaps lora_act
 
 
 @no_gpu_only

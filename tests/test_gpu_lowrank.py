@@ -1,9 +1,10 @@
 """GPU parity of the down-projection lora_act = bf16(x @ proj_down) against the oracle's
 float64 product: each element within bf16 rounding plus fp32 accumulation error.
 
-The down-projection runs inside the fused quantisation kernel, one 32-row tile
-per wave (fewer than 8192 rows) or two (8192 rows or more). Covers both, ragged
-M, R = 16 .. 256, K = 16 and 10240, and determinism.
+The down-projection runs inside the fused quantisation kernel: 32 rows per
+workgroup, with K split across workgroups (fp32 partials added in a fixed order
+by a second kernel) when there are few row blocks. Covers split and unsplit K,
+ragged M, R = 16 .. 256, K = 16 and 10240, and determinism.
 """
 
 import numpy as np
@@ -41,6 +42,7 @@ def check_lora(ops, M, K, R, kind, seed):
     (100, 10240, 128, "swiglu", 13),    # long K, ragged M
     (33, 16, 16, "tiny", 14),           # a single 16-wide K block
     (48, 384, 256, "dit", 15),          # R above one 128-wide chunk
+    (300, 3840, 256, "dit", 16),        # K split over 7 workgroups, two R chunks, ragged M
 ])
 def test_lora_down(gpu_lib, M, K, R, kind, seed):
     check_lora(gpu_lib, M, K, R, kind, seed)
