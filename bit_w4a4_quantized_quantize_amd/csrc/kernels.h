@@ -18,7 +18,6 @@ hipError_t launch_quant_act(const uint16_t* x, const uint16_t* smooth, uint8_t* 
 // When R > 0 and M is small, K is split across workgroups: the fp32 partials
 // go to `partial` (quant_lora_workspace_bytes(M, K, R) bytes, NULL if 0) and a
 // second kernel adds them in split order.
-int quant_lora_splits(int64_t M, int64_t K, int64_t R);
 size_t quant_lora_workspace_bytes(int64_t M, int64_t K, int64_t R);
 hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down,
                              uint8_t* qact, uint8_t* ascales, uint16_t* lora_act, float* partial,

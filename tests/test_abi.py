@@ -96,7 +96,7 @@ def test_quantize_act_workspace_sizes():
     """Scratch is needed only when the down-projection splits K (R > 0, few 64-row blocks):
     fp32 partials [splits, M, R]; none for R = 0 or many rows."""
     L = _lib.lib()
-    for M, K, R in [(64, 256, 16), (16896, 10240, 128), (7, 16, 0), (4096, 3840, 0)]:
+    for M, K, R in [(65536, 10240, 128), (7, 16, 0), (4096, 3840, 0), (64, 64, 16)]:
         assert L.svdq_quantize_act_workspace_bytes(M, K, R) == 0
     ws = L.svdq_quantize_act_workspace_bytes(4096, 3840, 128)
     assert ws >= 2 * 4096 * 128 * 4 and ws % (4096 * 128 * 4) == 0
