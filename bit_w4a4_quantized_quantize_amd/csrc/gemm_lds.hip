@@ -319,7 +319,19 @@ hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Tile width: 320 columns (5 tiles per wave) or 256 (4 per wave). One
+// workgroup runs per CU, so the kernel takes ceil(tiles / 256) rounds; a
+// 256-wide tile does 80% of the work of a 320-wide one in about 82% of its
+// time. The cheaper estimate wins: e.g. N = 10240 keeps 320 (512 tiles at
+// M = 4096: 2 rounds), N = 11520 takes 256 (720 tiles: 3 rounds of 82%
+// instead of 576 tiles: 3 rounds of 100%).
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream) {
+  const int64_t row_blocks = (a.M + 255) / 256;
+  const int64_t tiles320 = row_blocks * ((a.N + 319) / 320);
+  const int64_t tiles256 = row_blocks * ((a.N + 255) / 256);
+  const double cost320 = (double)((tiles320 + 255) / 256);
+  const double cost256 = 0.82 * (double)((tiles256 + 255) / 256);
+  if (cost256 < cost320) return launch_lds_cfg<4, 2, 2, 4>(a, stream);
   return launch_lds_cfg<4, 2, 2, 5>(a, stream);
 }
 

@@ -74,6 +74,14 @@ def test_gemm_parity(gpu_lib, cfg, packed):
     gemm_case(gpu_lib, cfg, packed=packed)
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_wide_ragged_n(gpu_lib, packed):
+    """N = 70000 (not a multiple of 32 * 5 * 2 = 320) with one row block: the packed
+    path picks its 320-wide tiles here (more than 256 tiles of 256 columns), so the
+    ragged last column block of that configuration is covered."""
+    gemm_case(gpu_lib, dict(M=64, K=256, N=70000, R=16, kind="dit", seed=35), packed=packed)
+
+
 def test_gemm_layouts_bit_identical(gpu_lib):
     cfg = dict(M=300, K=768, N=520, R=64, kind="dit", seed=31)
     a, _ = gemm_case(gpu_lib, cfg, packed=False)
