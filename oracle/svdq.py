@@ -189,6 +189,42 @@ def linear_w4a4(x_bits, smooth_bits, qweight, wscales, wcscales_bits, wtscale_bi
     return y64, F.f64_to_bf16(y64), qact, ascales
 
 
+# ---------------------------------------------------------------------------
+# FFN neighbour: gated combination of the w1 / w3 outputs
+# ---------------------------------------------------------------------------
+#
+# The blog page's layer table and its key insight name the DiT feed-forward
+# layers w1, w2, w3 (quantised to NVFP4, unlike attention); the pages do not
+# spell out how they combine. Reading: a gated FFN, w2(silu(w1 x) * (w3 x)),
+# with w1 and w3 run as one SVDQuant layer of 2F output channels that share x,
+# smooth, wtscale, proj_down and R (columns [0, F) = w1, [F, 2F) = w3).
+
+
+def silu(z):
+    """z * sigmoid(z) = z / (1 + exp(-z)), float64."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(y64, F_out):
+    """h = silu(y[:, :F]) * y[:, F:2F] in float64 from the 2F-wide layer output."""
+    y64 = np.asarray(y64, dtype=np.float64)
+    assert y64.shape[1] == 2 * F_out
+    return silu(y64[:, :F_out]) * y64[:, F_out:]
+
+
+def linear_w4a4_swiglu(x_bits, smooth_bits, qweight, wscales, wcscales_bits, wtscale_bits,
+                       proj_down_bits, proj_up_bits, bias_bits):
+    """The fused w1/w3 layer (2F output channels) followed by the gate:
+    returns (h64 float64 [M, F], h bf16 bits). The layer output itself is not
+    rounded to bf16 here (the fused path never materialises it)."""
+    y64, _, _, _ = linear_w4a4(x_bits, smooth_bits, qweight, wscales, wcscales_bits, wtscale_bits,
+                               proj_down_bits, proj_up_bits, bias_bits)
+    F_out = y64.shape[1] // 2
+    h64 = swiglu(y64, F_out)
+    return h64, F.f64_to_bf16(h64)
+
+
 def normwise_rel_err(y, y_ref):
     """||y - y_ref||_F / ||y_ref||_F in float64 (the acceptance metric for y)."""
     y = np.asarray(y, dtype=np.float64)

@@ -185,3 +185,39 @@ def test_lowrank_exact_rational_brute_force():
             exact = sum(t[r] * Fraction(float(pu[n, r])) for r in range(R))
             bound = sum(mag[r] * abs(Fraction(float(pu[n, r]))) for r in range(R)) * Fraction(K + R + 2, 2 ** 52)
             assert abs(Fraction(float(lr[m, n])) - exact) <= bound
+
+
+# --- gated FFN combination (w1 / w3 run as one 2F-wide layer) ---
+
+def test_silu_closed_form_values():
+    """silu(0) = 0; silu(z) - silu(-z) = z (sigmoid(z) + sigmoid(-z) = 1); silu(ln 3) =
+    ln 3 * 3/4; large |z| tends to max(z, 0)."""
+    assert S.silu(0.0) == 0.0
+    z = np.linspace(-30, 30, 601)
+    assert np.allclose(S.silu(z) - S.silu(-z), z, rtol=0, atol=1e-12)
+    assert abs(S.silu(np.log(3.0)) - np.log(3.0) * 0.75) < 1e-15
+    assert abs(S.silu(50.0) - 50.0) < 1e-15 and abs(S.silu(-50.0)) < 1e-18
+
+
+def test_swiglu_pairs_column_n_with_n_plus_f():
+    """Column n of the gate half pairs with column F + n of the up half, nothing else."""
+    rng = np.random.default_rng(11)
+    F_out = 7
+    y = rng.standard_normal((3, 2 * F_out))
+    h = S.swiglu(y, F_out)
+    for m in range(3):
+        for n in range(F_out):
+            g, u = y[m, n], y[m, F_out + n]
+            assert h[m, n] == g / (1.0 + np.exp(-g)) * u
+
+
+def test_linear_swiglu_equals_gate_times_up_of_the_plain_layer():
+    d = workloads.make_linear(M=16, K=128, N=2 * 24, R=16, kind="dit", seed=12)
+    qw, ws = S.quantize_weight(d["W"], d["wcscales"], d["wtscale"])
+    y64, _, _, _ = S.linear_w4a4(d["x"], d["smooth"], qw, ws, d["wcscales"], d["wtscale"],
+                                 d["proj_down"], d["proj_up"], d["bias"])
+    h64, h = S.linear_w4a4_swiglu(d["x"], d["smooth"], qw, ws, d["wcscales"], d["wtscale"],
+                                  d["proj_down"], d["proj_up"], d["bias"])
+    gate, up = y64[:, :24], y64[:, 24:]
+    assert np.array_equal(h64, gate / (1.0 + np.exp(-gate)) * up)
+    assert np.array_equal(h, F.f64_to_bf16(h64))
