@@ -369,7 +369,7 @@ int svdq_gemm_w4a4(const void* qact, const void* ascales, int act_layout, const 
                       range("bias", bias, (size_t)N * 2)};
   const Range out[] = {range("y", y, (size_t)M * N * 2)};
   if ((st = check_alias(in, 9, out, 1))) return st;
-  svdq::GemmArgs a;
+  svdq::GemmArgs a{};
   a.qact = static_cast<const uint8_t*>(qact);
   a.ascales = static_cast<const uint8_t*>(ascales);
   a.lora_act = static_cast<const uint16_t*>(lora_act);
@@ -441,7 +441,7 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   const hipStream_t s = static_cast<hipStream_t>(stream);
   void* scratch = ws.total > ws.partial ? (void*)(w + ws.partial) : nullptr;
   if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora, scratch, packed, s))) return st;
-  svdq::GemmArgs a;
+  svdq::GemmArgs a{};
   a.qact = static_cast<const uint8_t*>(qact);
   a.ascales = static_cast<const uint8_t*>(ascales);
   a.lora_act = static_cast<const uint16_t*>(lora);
@@ -455,6 +455,119 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   a.M = M; a.N = N; a.K = K; a.R = R;
   a.packed = packed;
   hipError_t e = packed ? svdq::launch_gemm_lds(a, s) : svdq::launch_gemm_w4a4(a, s);
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---- gated FFN neighbour: the 2F-wide w1/w3 layer with silu(gate) * up ----
+
+static int check_gated_f(int64_t F) {
+  if (F < 0) return fail(SVDQ_ERR_SHAPE, "F = %lld is negative", (long long)F);
+  if (F % 32 != 0)
+    return fail(SVDQ_ERR_UNSUPPORTED, "F = %lld: the gated kernels need F to be a multiple of 32", (long long)F);
+  return SVDQ_OK;
+}
+
+static svdq::GemmArgs gated_args(const void* qact, const void* lora, const void* weight,
+                                 const void* wcscales, const void* wtscale, const void* proj_up,
+                                 const void* bias, int64_t M, int64_t F, int64_t K, int64_t R, void* h) {
+  svdq::GemmArgs a{};
+  a.qact = static_cast<const uint8_t*>(qact);
+  a.lora_act = static_cast<const uint16_t*>(lora);
+  a.weight = static_cast<const uint8_t*>(weight);
+  a.wcscales = static_cast<const uint16_t*>(wcscales);
+  a.wtscale = static_cast<const uint16_t*>(wtscale);
+  a.proj_up = static_cast<const uint16_t*>(proj_up);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.y = static_cast<uint16_t*>(h);
+  a.M = M; a.N = 2 * F; a.K = K; a.R = R;
+  a.packed = 1;
+  a.gated_f = F;
+  return a;
+}
+
+int svdq_gemm_w4a4_gated(const void* qact, const void* lora_act, const void* weight,
+                         const void* wcscales, const void* wtscale, const void* proj_up,
+                         const void* bias, int64_t M, int64_t F, int64_t K, int64_t R, void* h,
+                         void* stream) {
+  int st = check_mk(M, K, R);
+  if (st) return st;
+  if ((st = check_gated_f(F))) return st;
+  const int64_t N = 2 * F;
+  if ((st = check_nk(N, K))) return st;
+  if ((st = check_packed_gemm_sizes(M, N, K))) return st;
+  if (M == 0 || F == 0) return ok();
+  if ((st = validate_gemm(qact, nullptr, SVDQ_ACT_PACKED, lora_act, weight, nullptr, SVDQ_WEIGHT_PACKED,
+                          wcscales, wtscale, proj_up, bias, M, N, K, R, h, true)))
+    return st;
+  const Range in[] = {range("qact", qact, svdq::packed_weight_bytes(M, K)),
+                      range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
+                      range("weight", weight, svdq::packed_weight_bytes(N, K)),
+                      range("wcscales", wcscales, (size_t)N * 2),
+                      range("wtscale", wtscale, 2),
+                      range("proj_up", R > 0 ? proj_up : nullptr, (size_t)N * R * 2),
+                      range("bias", bias, (size_t)N * 2)};
+  const Range out[] = {range("h", h, (size_t)M * F * 2)};
+  if ((st = check_alias(in, 7, out, 1))) return st;
+  const svdq::GemmArgs a = gated_args(qact, lora_act, weight, wcscales, wtscale, proj_up, bias, M, F, K, R, h);
+  hipError_t e = svdq::launch_gemm_lds(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t svdq_linear_gated_workspace_bytes(int64_t M, int64_t F, int64_t K, int64_t R) {
+  (void)F;
+  if (M <= 0 || K <= 0 || K % 16 != 0 || R < 0) return 0;
+  return linear_ws(M, K, R).total;
+}
+
+int svdq_linear_w4a4_gated(const void* x, const void* smooth, const void* weight,
+                           const void* wcscales, const void* wtscale, const void* proj_down,
+                           const void* proj_up, const void* bias, int64_t M, int64_t F, int64_t K,
+                           int64_t R, void* h, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_mk(M, K, R);
+  if (st) return st;
+  if ((st = check_rsrc_sizes(M, K, R))) return st;
+  if ((st = check_gated_f(F))) return st;
+  const int64_t N = 2 * F;
+  if ((st = check_nk(N, K))) return st;
+  if ((st = check_packed_gemm_sizes(M, N, K))) return st;
+  if (M == 0 || F == 0) return ok();
+  {
+    const char* names[] = {"x", "smooth", "workspace"};
+    const void* ptrs[] = {x, smooth, workspace};
+    if ((st = check_ptrs(names, ptrs, 3))) return st;
+  }
+  if (R > 0) {
+    const char* names[] = {"proj_down"};
+    const void* ptrs[] = {proj_down};
+    if ((st = check_ptrs(names, ptrs, 1))) return st;
+  }
+  if ((st = validate_gemm(nullptr, nullptr, SVDQ_ACT_CANONICAL, nullptr, weight, nullptr,
+                          SVDQ_WEIGHT_PACKED, wcscales, wtscale, proj_up, bias, M, N, K, R, h, false)))
+    return st;
+  const LinearWs ws = linear_ws(M, K, R);
+  if (workspace_bytes < ws.total)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws.total);
+  const Range in[] = {range("x", x, (size_t)M * K * 2),
+                      range("smooth", smooth, (size_t)K * 2),
+                      range("weight", weight, svdq::packed_weight_bytes(N, K)),
+                      range("wcscales", wcscales, (size_t)N * 2),
+                      range("wtscale", wtscale, 2),
+                      range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2),
+                      range("proj_up", R > 0 ? proj_up : nullptr, (size_t)N * R * 2),
+                      range("bias", bias, (size_t)N * 2)};
+  const Range out[] = {range("h", h, (size_t)M * F * 2), range("workspace", workspace, ws.total)};
+  if ((st = check_alias(in, 8, out, 2))) return st;
+
+  char* w = static_cast<char*>(workspace);
+  void* qact = w + ws.act;
+  void* lora = R > 0 ? (void*)(w + ws.lora) : nullptr;
+  void* scratch = ws.total > ws.partial ? (void*)(w + ws.partial) : nullptr;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, nullptr, lora, scratch, true, s))) return st;
+  const svdq::GemmArgs a = gated_args(qact, lora, weight, wcscales, wtscale, proj_up, bias, M, F, K, R, h);
+  hipError_t e = svdq::launch_gemm_lds(a, s);
   if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return ok();
 }

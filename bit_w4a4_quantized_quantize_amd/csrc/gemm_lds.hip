@@ -60,9 +60,14 @@ struct LdsCfg {
   static constexpr int kResSteps = (2 * kStageBytes) / (kChunks * 1024);   // R/16 steps per LDS residual pass
 };
 
-template <int WM, int WN, int TM, int TN>
+// GATED: the weight holds 2F output channels (a.N = 2F, a.gated_f = F); the
+// workgroup's two wave columns compute matching column ranges of the two
+// halves (wave_n = 0: channels c, wave_n = 1: channels F + c), and the output
+// is h[:, c] = silu(y[:, c]) * y[:, F + c], [M, F] bf16.
+template <int WM, int WN, int TM, int TN, bool GATED>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   using C = LdsCfg<WM, WN, TM, TN>;
+  static_assert(!GATED || WN == 2, "the gated epilogue pairs the two wave columns");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -80,7 +85,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   const uint32_t a_code_bytes = (uint32_t)KP * MP * 1024;
   const uint32_t b_code_bytes = (uint32_t)KP * NP * 1024;
 
-  const int NBX = (N + C::BN - 1) / C::BN;
+  const int FO = GATED ? (int)a.gated_f : N;          // output columns
+  const int FP = (FO + 31) / 32;                       // output panels (per half when gated)
+  const int NBX = GATED ? (FP + TN - 1) / TN : (N + C::BN - 1) / C::BN;
   const int NBY = (M + C::BM - 1) / C::BM;
   const int T = NBX * NBY;
   const int per_xcd = (int)(gridDim.x / 8);
@@ -93,6 +100,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   const int bx = (tile % per_group) / group_rows;
   const int mp0 = by * (C::BM / 32);
   const int np0 = bx * (C::BN / 32);
+  // weight panel of B chunk j (0 .. kChunksB-1), and whether it exists
+  auto b_panel = [&](int j) -> int {
+    return GATED ? (j / TN) * FP + bx * TN + j % TN : np0 + j;
+  };
+  auto b_panel_in = [&](int j) -> bool {
+    return GATED ? bx * TN + j % TN < FP : np0 + j < NP;
+  };
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.qact, a_code_bytes + (uint32_t)KP * MP * 128);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.weight, b_code_bytes + (uint32_t)KP * NP * 128);
@@ -103,11 +117,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   auto load_one = [&](int s, int kp) {
     const int c = wave + C::kWaves * s;
     const bool is_a = c < C::kChunksA;
-    const int row = is_a ? mp0 + c : np0 + (c - C::kChunksA);
+    const bool in = is_a ? mp0 + c < MP : b_panel_in(c - C::kChunksA);
+    const int row = is_a ? mp0 + c : b_panel(c - C::kChunksA);
     const int rows = is_a ? MP : NP;
     const uint32_t code_bytes = is_a ? a_code_bytes : b_code_bytes;
     const uint32_t chunk = (uint32_t)kp * rows + row;
-    const bool in = row < rows;
     const uint32_t off_c = in ? chunk * 1024 + lane * 16 : 0x80000000u;
     const uint32_t off_s = in ? code_bytes + chunk * 128 + l32 * 4 : 0x80000000u;
     const __amdgpu_buffer_rsrc_t r = is_a ? ra : rb;
@@ -180,16 +194,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   }
   // epilogue operands load while the last panel multiplies
   const int m_w = (mp0 + wave_m * TM) * 32;
-  const int n_w = (np0 + wave_n * TN) * 32;
-  int ncol[TN];
+  // this wave's first output column (in the output of width FO)
+  const int n_w = GATED ? bx * TN * 32 : (np0 + wave_n * TN) * 32;
+  int ncol[TN];      // weight channel of column j of this lane
+  bool ncol_in[TN];
   uint32_t wc_raw[TN], bias_raw[TN];
   {
     const __amdgpu_buffer_rsrc_t rwc = make_rsrc(a.wcscales, (uint32_t)N * 2);
     const __amdgpu_buffer_rsrc_t rbi = make_rsrc(a.bias, a.bias != nullptr ? (uint32_t)N * 2 : 0u);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      ncol[j] = n_w + 32 * j + l32;
-      const uint32_t off = ncol[j] < N ? (uint32_t)ncol[j] * 2 : 0x80000000u;
+      const int col = n_w + 32 * j + l32;
+      ncol_in[j] = col < FO;
+      ncol[j] = (GATED ? wave_n * FO : 0) + col;
+      const uint32_t off = ncol_in[j] ? (uint32_t)ncol[j] * 2 : 0x80000000u;
       wc_raw[j] = __builtin_amdgcn_raw_buffer_load_b16(rwc, off, 0, 0);
       bias_raw[j] = __builtin_amdgcn_raw_buffer_load_b16(rbi, off, 0, 0);
     }
@@ -226,7 +244,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   // into a 1 KB LDS block in the matrix-instruction operand order, then the
   // waves multiply out of LDS. Rows beyond M or N are clamped to the last row.
   {
-    const int m_wg = mp0 * 32, n_wg = np0 * 32;
+    const int m_wg = mp0 * 32;
     for (int r0 = 0; r0 < r_steps; r0 += C::kResSteps) {
       const int S = min(C::kResSteps, r_steps - r0);
       const int blocks = C::kChunks * S;
@@ -241,7 +259,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
           const int m = min(m_wg + 32 * g + l32, M - 1);
           src = a.lora_act + (size_t)m * R + col;
         } else {
-          const int n = min(n_wg + 32 * g + l32, N - 1);
+          const int n = min(b_panel(g) * 32 + l32, N - 1);
           src = a.proj_up + (size_t)n * R + col;
         }
         __builtin_amdgcn_global_load_lds(src, LDS_PTR(smem + b * 1024), 16, 0, 0);
@@ -265,37 +283,63 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
     }
   }
 
-  // bf16 output through LDS: each wave writes one 32-row slice of its tile
-  // row-major, then stores whole 16-byte row pieces
+  // bf16 output through LDS: each writing wave stages one 32-row slice of its
+  // tile row-major, then stores whole 16-byte row pieces. Gated: the wave_n = 1
+  // waves first hand their fp32 values to their wave_n = 0 partners through
+  // LDS (exchange region, then the staging region after it).
   __syncthreads();
   constexpr int kCols = 32 * TN;
   constexpr int kPieces = kCols / 8;
-  uint16_t* stage_out = reinterpret_cast<uint16_t*>(smem + wave * (32 * kCols * 2));
-  const bool vec_ok = (N % 8) == 0;
+  constexpr int kXBytes = GATED ? WM * TN * 64 * 64 : 0;   // f32x16 per lane per column tile
+  const bool writer = !GATED || wave_n == 0;
+  uint16_t* stage_out = reinterpret_cast<uint16_t*>(smem + kXBytes + (GATED ? wave_m : wave) * (32 * kCols * 2));
+  f32x16* xchg = reinterpret_cast<f32x16*>(smem) + wave_m * TN * 64;
+  const bool vec_ok = (FO % 8) == 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    if (GATED) {
+      if (wave_n == 1) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j) {
+          f32x16 v = acc[i][j];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-        stage_out[row * kCols + 32 * j + l32] = (uint16_t)f32_to_bf16_rne(acc[i][j][r] + bias_v[j]);
+          for (int r = 0; r < 16; ++r) v[r] += bias_v[j];
+          xchg[j * 64 + lane] = v;
+        }
       }
-    __syncthreads();
+      __syncthreads();
+    }
+    if (writer) {
 #pragma unroll
-    for (int u = 0; u < (32 * kPieces + 63) / 64; ++u) {
-      const int idx = lane + 64 * u;
-      if (idx < 32 * kPieces) {
-        const int row = idx / kPieces, piece = idx % kPieces;
-        const int m = m_w + 32 * i + row;
-        const int n = n_w + 8 * piece;
-        if (m < M && n < N) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + row * kCols + 8 * piece);
-          uint16_t* dst = a.y + (size_t)m * N + n;
-          if (vec_ok && n + 8 <= N) {
-            *reinterpret_cast<u32x4*>(dst) = v;
-          } else {
-            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      for (int j = 0; j < TN; ++j) {
+        f32x16 up;
+        if (GATED) up = xchg[j * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+          float v = acc[i][j][r] + bias_v[j];
+          if (GATED) v = v / (1.0f + __expf(-v)) * up[r];
+          stage_out[row * kCols + 32 * j + l32] = (uint16_t)f32_to_bf16_rne(v);
+        }
+      }
+    }
+    __syncthreads();
+    if (writer) {
+#pragma unroll
+      for (int u = 0; u < (32 * kPieces + 63) / 64; ++u) {
+        const int idx = lane + 64 * u;
+        if (idx < 32 * kPieces) {
+          const int row = idx / kPieces, piece = idx % kPieces;
+          const int m = m_w + 32 * i + row;
+          const int n = n_w + 8 * piece;
+          if (m < M && n < FO) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + row * kCols + 8 * piece);
+            uint16_t* dst = a.y + (size_t)m * FO + n;
+            if (vec_ok && n + 8 <= FO) {
+              *reinterpret_cast<u32x4*>(dst) = v;
+            } else {
+              for (int e = 0; e < 8 && n + e < FO; ++e) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            }
           }
         }
       }
@@ -304,16 +348,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   }
 }
 
-template <int WM, int WN, int TM, int TN>
+template <int WM, int WN, int TM, int TN, bool GATED>
 hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
   using C = LdsCfg<WM, WN, TM, TN>;
-  const int64_t tiles = ((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM);
+  const int64_t col_tiles = GATED ? ((a.gated_f + 31) / 32 + TN - 1) / TN : (a.N + C::BN - 1) / C::BN;
+  const int64_t tiles = col_tiles * ((a.M + C::BM - 1) / C::BM);
   const unsigned lds = 2 * C::kStageBytes;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN, GATED>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((gemm_lds_kernel<WM, WN, TM, TN>), grid, dim3(C::kThreads), lds, stream, a);
+  hipLaunchKernelGGL((gemm_lds_kernel<WM, WN, TM, TN, GATED>), grid, dim3(C::kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -324,15 +369,22 @@ hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
 // 256-wide tile does 80% of the work of a 320-wide one in about 82% of its
 // time. The cheaper estimate wins: e.g. N = 10240 keeps 320 (512 tiles at
 // M = 4096: 2 rounds), N = 11520 takes 256 (720 tiles: 3 rounds of 82%
-// instead of 576 tiles: 3 rounds of 100%).
+// instead of 576 tiles: 3 rounds of 100%). Gated, the same choice is made for
+// the 2F-wide weight (each tile covers half its width in each half).
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream) {
+  const bool gated = a.gated_f > 0;
   const int64_t row_blocks = (a.M + 255) / 256;
-  const int64_t tiles320 = row_blocks * ((a.N + 319) / 320);
-  const int64_t tiles256 = row_blocks * ((a.N + 255) / 256);
+  const int64_t width = gated ? 2 * ((a.gated_f + 31) / 32 * 32) : a.N;
+  const int64_t tiles320 = row_blocks * ((width + 319) / 320);
+  const int64_t tiles256 = row_blocks * ((width + 255) / 256);
   const double cost320 = (double)((tiles320 + 255) / 256);
   const double cost256 = 0.82 * (double)((tiles256 + 255) / 256);
-  if (cost256 < cost320) return launch_lds_cfg<4, 2, 2, 4>(a, stream);
-  return launch_lds_cfg<4, 2, 2, 5>(a, stream);
+  if (gated) {
+    if (cost256 < cost320) return launch_lds_cfg<4, 2, 2, 4, true>(a, stream);
+    return launch_lds_cfg<4, 2, 2, 5, true>(a, stream);
+  }
+  if (cost256 < cost320) return launch_lds_cfg<4, 2, 2, 4, false>(a, stream);
+  return launch_lds_cfg<4, 2, 2, 5, false>(a, stream);
 }
 
 }  // namespace svdq

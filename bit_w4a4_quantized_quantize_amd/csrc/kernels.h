@@ -37,6 +37,7 @@ struct GemmArgs {
   uint16_t* y;              // [M, N]
   int64_t M, N, K, R;
   int packed;
+  int64_t gated_f;          // 0, or F: N = 2F and y = silu(y[:, :F]) * y[:, F:] is [M, F]
 };
 // canonical activations (LDS-staged), canonical or packed weights
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);

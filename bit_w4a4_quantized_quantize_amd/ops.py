@@ -221,3 +221,49 @@ def linear_w4a4(x, w: SVDQLinearWeights, y=None, workspace=None):
         _p(w.proj_up) if w.R > 0 else None, _p(w.bias), M, w.N, K, w.R,
         _p(y), _p(workspace), workspace.numel(), _stream(x.device)))
     return y
+
+
+def _check_gated(w: SVDQLinearWeights):
+    _check_layer(w)
+    if w.layout != WEIGHT_PACKED:
+        raise ValueError("the gated layer needs the packed weight layout (use .packed())")
+    if w.N % 2 != 0:
+        raise ValueError(f"the gated layer has 2F output channels, got N={w.N}")
+    return w.N // 2
+
+
+def gemm_w4a4_gated(qact, lora_act, w: SVDQLinearWeights, M, h=None):
+    """Gated FFN step from packed activations: h [M, F] = silu(y[:, :F]) * y[:, F:]
+    of the 2F-channel layer w (w1 and w3 as one layer), bf16."""
+    F_out = _check_gated(w)
+    _need(qact, "qact (packed)", torch.uint8, 1)
+    if w.R > 0:
+        _need(lora_act, "lora_act", torch.bfloat16, 2)
+    if h is None:
+        h = torch.empty((M, F_out), dtype=torch.bfloat16, device=qact.device)
+    L = _lib.lib()
+    _lib.check("svdq_gemm_w4a4_gated", L.svdq_gemm_w4a4_gated(
+        _p(qact), _p(lora_act) if w.R > 0 else None, _p(_bytes(w.weight)), _p(w.wcscales),
+        _p(w.wtscale), _p(w.proj_up) if w.R > 0 else None, _p(w.bias), M, F_out, w.K, w.R,
+        _p(h), _stream(qact.device)))
+    return h
+
+
+def linear_w4a4_gated(x, w: SVDQLinearWeights, h=None, workspace=None):
+    """The whole gated step from x: h [M, F] bf16 (w is the 2F-channel w1/w3 layer)."""
+    F_out = _check_gated(w)
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"x has K={K}, the layer K={w.K}")
+    if h is None:
+        h = torch.empty((M, F_out), dtype=torch.bfloat16, device=x.device)
+    L = _lib.lib()
+    nbytes = L.svdq_linear_gated_workspace_bytes(M, F_out, K, w.R)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _lib.check("svdq_linear_w4a4_gated", L.svdq_linear_w4a4_gated(
+        _p(x), _p(w.smooth), _p(_bytes(w.weight)), _p(w.wcscales), _p(w.wtscale),
+        _p(w.proj_down) if w.R > 0 else None, _p(w.proj_up) if w.R > 0 else None, _p(w.bias),
+        M, F_out, K, w.R, _p(h), _p(workspace), workspace.numel(), _stream(x.device)))
+    return h

@@ -184,6 +184,35 @@ int svdq_linear_w4a4(const void* x, const void* smooth,
                      int64_t M, int64_t N, int64_t K, int64_t R,
                      void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * FFN neighbour (gated): the DiT feed-forward layers w1 and w3 (blog page
+ * "Z-Image NVFP4 ...", layer table and its key insight: FFN w1, w2, w3 are the
+ * NVFP4 layers) run as ONE SVDQuant layer with 2F output channels that share x,
+ * smooth, wtscale, proj_down and R: channels [0, F) are w1, [F, 2F) are w3.
+ * Its output never leaves the chip: the epilogue combines it as
+ *   h[:, c] = bf16( silu(y[:, c]) * y[:, F + c] ),  silu(z) = z / (1 + exp(-z)),
+ * with y the fp32 layer result before rounding (the pages do not state the
+ * combination; this gated form is the reading). h [M, F] bf16 is w2's input.
+ *
+ *   weight: PACKED layout of the 2F-channel layer (svdq_repack_weight with
+ *     N = 2F); wcscales [2F], proj_up [2F, R], bias [2F] bf16 or NULL.
+ *   F must be a multiple of 32 (SVDQ_ERR_UNSUPPORTED otherwise).
+ *   svdq_gemm_w4a4_gated: packed activations (as svdq_gemm_w4a4 with
+ *     SVDQ_ACT_PACKED) and lora_act [M, R].
+ *   svdq_linear_w4a4_gated: the whole step from x, with a workspace of
+ *     svdq_linear_gated_workspace_bytes(M, F, K, R) bytes.
+ * Other conventions as for svdq_gemm_w4a4 / svdq_linear_w4a4.
+ */
+int svdq_gemm_w4a4_gated(const void* qact, const void* lora_act, const void* weight,
+                         const void* wcscales, const void* wtscale, const void* proj_up,
+                         const void* bias, int64_t M, int64_t F, int64_t K, int64_t R, void* h,
+                         void* stream);
+size_t svdq_linear_gated_workspace_bytes(int64_t M, int64_t F, int64_t K, int64_t R);
+int svdq_linear_w4a4_gated(const void* x, const void* smooth, const void* weight,
+                           const void* wcscales, const void* wtscale, const void* proj_down,
+                           const void* proj_up, const void* bias, int64_t M, int64_t F, int64_t K,
+                           int64_t R, void* h, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -191,3 +191,37 @@ def test_repack_rejections():
     assert L.svdq_repack_weight(fake(1), fake(2), 128, 256, fake(1) + 16, need, None) == 6
     assert L.svdq_unpack_weight(fake(1), need, 128, 256, fake(1), fake(2), None) == 6
     assert L.svdq_unpack_weight(fake(1), need, 0, 256, None, None, None) == 0
+
+
+def gated(**kw):
+    args = dict(x=fake(1), smooth=fake(2), weight=fake(3), wcscales=fake(5), wtscale=fake(6),
+                proj_down=fake(7), proj_up=fake(8), bias=None, M=64, F=128, K=256, R=16, h=fake(9),
+                ws=fake(10), ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    L = _lib.lib()
+    return L.svdq_linear_w4a4_gated(args["x"], args["smooth"], args["weight"], args["wcscales"],
+                                    args["wtscale"], args["proj_down"], args["proj_up"], args["bias"],
+                                    args["M"], args["F"], args["K"], args["R"], args["h"], args["ws"],
+                                    args["ws_bytes"], args["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(F=-32), 2), (dict(F=48), 3), (dict(K=40), 2), (dict(R=24), 3),
+    (dict(weight=None), 1), (dict(h=None), 1), (dict(x=None), 1), (dict(wtscale=None), 1),
+    (dict(proj_up=None), 1), (dict(h=fake(9) + 4), 4),
+    (dict(h=fake(3)), 6),                                   # h overlaps the weight
+    (dict(ws_bytes=0), 5),
+    (dict(F=1 << 20, K=1 << 12), 3),                        # packed 2F-channel weight > 2 GiB
+])
+def test_linear_gated_rejections(kw, code):
+    assert gated(**kw) == code
+
+
+@no_gpu_only
+def test_gated_empty_is_ok():
+    assert gated(M=0) == 0
+    assert gated(F=0) == 0
+    L = _lib.lib()
+    assert L.svdq_gemm_w4a4_gated(fake(1), fake(2), fake(3), fake(5), fake(6), fake(8), None,
+                                  64, 48, 256, 16, fake(9), None) == 3
