@@ -49,6 +49,11 @@ WORKLOADS = {
     "ffn_w2_2048": (("LAYERS_2048", "w2"), "DiT FFN w2 at 2048px"),
 }
 DEFAULT_WORKLOAD = "ffn_w1_1024"
+# the gated FFN block (w1/w3 as one 2F-channel layer with silu(gate) * up, then w2)
+FFN_BLOCKS = {
+    "ffn_block_1024": (dict(M=4096, K=3840, N=2 * 10240, R=128, kind="dit", seed=1003), "FFN_W2_1024",
+                       "DiT FFN block at 1024^2"),
+}
 
 
 def workload_cfg(name):
@@ -60,7 +65,7 @@ def workload_cfg(name):
 
 def parse():
     p = argparse.ArgumentParser()
-    p.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD,
+    p.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS), default=DEFAULT_WORKLOAD,
                    help="layer shape (the default is the headline workload; the rest are for comparison)")
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
@@ -193,8 +198,161 @@ def cpu_baseline(d, cfg, repeats=2):
             "seconds_per_call": t}
 
 
+def cpu_baseline_ffn(d13, d2, F_out):
+    """The oracle on one FFN block call (gated w1/w3 then w2), weights quantised beforehand."""
+    import numpy as np
+    from oracle import formats as Fm
+    from oracle import svdq as S
+
+    qw13, ws13 = S.quantize_weight(d13["W"], d13["wcscales"], d13["wtscale"])
+    qw2, ws2 = S.quantize_weight(d2["W"], d2["wcscales"], d2["wtscale"])
+    t0 = time.perf_counter()
+    _, h = S.linear_w4a4_swiglu(d13["x"], d13["smooth"], qw13, ws13, d13["wcscales"], d13["wtscale"],
+                                d13["proj_down"], d13["proj_up"], d13["bias"])
+    S.linear_w4a4(h, d2["smooth"], qw2, ws2, d2["wcscales"], d2["wtscale"], d2["proj_down"], d2["proj_up"],
+                  d2["bias"])
+    t = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    del np, Fm
+    return t, int(threads)
+
+
+def run_ffn_block(args):
+    """The gated FFN block: h = silu(x W1^T) * (x W3^T) by one gated call, then y = w2(h)."""
+    import torch
+
+    import workloads
+    from bit_w4a4_quantized_quantize_amd import ops
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    cfg13, w2_name, desc = FFN_BLOCKS[args.workload]
+    cfg2 = dict(getattr(workloads, w2_name))
+    M, K, R = cfg13["M"], cfg13["K"], cfg13["R"]
+    F_out = cfg13["N"] // 2
+    N2 = cfg2["N"]
+    assert cfg2["K"] == F_out and cfg2["M"] == M
+    n_sets = 1 if args.warm else args.sets
+    print(f"[bench] building {n_sets} input sets: gated M={M} K={K} F={F_out}, w2 K={F_out} N={N2}, R={R}",
+          file=sys.stderr, flush=True)
+    d13, sets13 = make_sets(cfg13, n_sets, "packed", dev)
+    d2, sets2 = make_sets(cfg2, n_sets, "packed", dev)
+    hs = [torch.empty((M, F_out), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    torch.cuda.synchronize()
+
+    flops13 = 2 * M * (2 * F_out) * K + 2 * M * R * (K + 2 * F_out)
+    flops2 = 2 * M * N2 * F_out + 2 * M * R * (F_out + N2)
+    flops_block = flops13 + flops2
+    flops_gated_gemm = 2 * M * (2 * F_out) * K + 2 * M * (2 * F_out) * R
+
+    def step(i):
+        a, b = sets13[i], sets2[i]
+        ops.linear_w4a4_gated(a["x"], a["layer"], h=hs[i], workspace=a["ws"])
+        ops.linear_w4a4(hs[i], b["layer"], y=b["y"], workspace=b["ws"])
+
+    for i in range(args.warmup):
+        step(i % n_sets)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i % n_sets)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    tflops = flops_block / (ms_per_step * 1e-3) / 1e12
+    print(f"[bench] FFN block: {ms_per_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s "
+          f"(wall {wall * 1e6 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
+
+    # per-kernel: the gated GEMM alone (packed activations, as inside the block)
+    for i in range(n_sets):
+        a = sets13[i]
+        ops.quantize_act(a["x"], a["layer"].smooth, a["layer"].proj_down, qact=a["qpk"], lora_act=a["lora"],
+                         packed=True)
+    torch.cuda.synchronize()
+
+    def gated_gemm(i):
+        a = sets13[i]
+        ops.gemm_w4a4_gated(a["qpk"], a["lora"], a["layer"], M, h=hs[i])
+
+    def w2_layer(i):
+        b = sets2[i]
+        ops.linear_w4a4(hs[i], b["layer"], y=b["y"], workspace=b["ws"])
+
+    def unfused(i):
+        # the same block without the gated epilogue: the 2F-channel layer's bf16
+        # output, the gate as separate elementwise work, then w2
+        a, b = sets13[i], sets2[i]
+        y = ops.linear_w4a4(a["x"], a["layer"])
+        h = torch.nn.functional.silu(y[:, :F_out].float()).mul_(y[:, F_out:].float()).to(torch.bfloat16)
+        ops.linear_w4a4(h, b["layer"], y=b["y"], workspace=b["ws"])
+
+    kw = max(1, args.warmup // 2)
+    gated_ms = time_loop(gated_gemm, n_sets, args.kernel_iters, kw, stream)
+    w2_ms = time_loop(w2_layer, n_sets, args.kernel_iters, kw, stream)
+    unfused_ms = time_loop(unfused, n_sets, max(10, args.kernel_iters // 4), kw, stream)
+    gated_tflops = flops_gated_gemm / (gated_ms * 1e-3) / 1e12
+    print(f"[bench] gated GEMM {gated_ms * 1e3:.1f} us ({gated_tflops:.1f} TFLOP/s), w2 layer {w2_ms * 1e3:.1f} us, "
+          f"unfused block {unfused_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    result = {
+        "metric": f"W4A4 SVDQuant FFN block (gated w1/w3 + w2) TFLOP/s at M={M},K={K},F={F_out}, 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{desc}: gated w1/w3 (one 2F-channel SVDQuant W4A4 layer, h = silu(gate) * up) "
+                        f"then w2; M={M} K={K} F={F_out} N2={N2} R={R}",
+            "cache": "warm" if args.warm else f"cold (rotating {n_sets} sets)",
+            "flop_per_step": flops_block,
+        },
+        "pct_mfma_peak": round(100.0 * tflops / PEAK_F16_MFMA_TFLOPS, 2),
+        "roofline": {
+            "kernel": "gemm_lds_kernel, gated (2F-channel GEMM + low-rank + silu(gate)*up epilogue)",
+            "bound": "mfma",
+            "achieved": round(gated_tflops, 2),
+            "peak": PEAK_F16_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gated_tflops / PEAK_F16_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "flop_per_launch": flops_gated_gemm,
+            "avg_launch_us": round(gated_ms * 1e3, 2),
+        },
+        "w2_layer_us": round(w2_ms * 1e3, 2),
+        "unfused_block_us": round(unfused_ms * 1e3, 2),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on the same block", file=sys.stderr, flush=True)
+        t, threads = cpu_baseline_ffn(d13, d2, F_out)
+        result["cpu_baseline"] = {"value": flops_block / t / 1e12, "unit": "TFLOP/s", "cores": threads,
+                                  "kind": "oracle", "seconds_per_call": t,
+                                  "sample": f"one FFN block call (M={M} K={K} F={F_out} N2={N2} R={R}); "
+                                            f"{t:.2f} s; weight quantisation excluded (load time)"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload in FFN_BLOCKS:
+        if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+            print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
+            sys.exit(2)
+        return run_ffn_block(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the layer's multi-GPU "
                                    "sharding is described in the design notes but not built"}))
