@@ -225,6 +225,30 @@ def linear_w4a4_swiglu(x_bits, smooth_bits, qweight, wscales, wcscales_bits, wts
     return h64, F.f64_to_bf16(h64)
 
 
+# ---------------------------------------------------------------------------
+# Layers kept in bf16
+# ---------------------------------------------------------------------------
+#
+# The blog page's variant table keeps some linears of the DiT in bf16 (its
+# "Ultra" variant: attention qkv/out everywhere, and every linear of blocks
+# 0-4 and 25-29). Such a layer is the original model's linear,
+# y = x @ W^T + bias, with bf16 x [M, K], W [N, K] (the layout of the bf16
+# checkpoint's weight), bias [N]; the output is rounded to bf16 once.
+
+
+def linear_bf16(x_bits, w_bits, bias_bits):
+    """Plain bf16 linear: returns (y64 float64 [M, N], y bf16 bits).
+
+    Every bf16 x bf16 product is exact in float64; only the sum over K
+    (float64) and the final bf16 cast round."""
+    x = F.bf16_to_f64(x_bits)
+    w = F.bf16_to_f64(w_bits)
+    y64 = x @ w.T
+    if bias_bits is not None:
+        y64 = y64 + F.bf16_to_f64(bias_bits)[None, :]
+    return y64, F.f64_to_bf16(y64)
+
+
 def normwise_rel_err(y, y_ref):
     """||y - y_ref||_F / ||y_ref||_F in float64 (the acceptance metric for y)."""
     y = np.asarray(y, dtype=np.float64)

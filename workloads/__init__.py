@@ -114,3 +114,52 @@ def make_activation(M, K, kind="dit", seed=0):
     """Only x and smooth, for activation-quantisation cases (same recipe)."""
     d = make_linear(M, K, 16, 0, kind=kind, seed=seed, with_bias=False)
     return d["x"], d["smooth"]
+
+
+def make_bf16_linear(M, K, N, kind="dit", seed=0, with_bias=True):
+    """Inputs of a linear kept in bf16: x (same recipe as make_linear, so
+    "dit" has the outlier channels), W ~ N(0, 0.02) and bias ~ N(0, 0.01),
+    all rounded to bf16. Draw order x, outlier channels, W, bias."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    if kind in ("dit", "swiglu"):
+        _outliers(rng, x, K)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    bias = rng.standard_normal(N, dtype=np.float32) * np.float32(0.01)
+    return dict(M=M, K=K, N=N, x=f32_to_bf16_bits(x), W=f32_to_bf16_bits(W),
+                bias=f32_to_bf16_bits(bias) if with_bias else None)
+
+
+# The mixed-precision linear sweep of a 30-block DiT at 1024^2 (M = 4096
+# tokens), 8 denoising forwards. The blog page's variant table: the "Ultra"
+# variant keeps attention (qkv, out) and blocks 0-4 and 25-29 in bf16 and
+# quantises 60 linears to NVFP4; 60 = 20 blocks x the 3 FFN linears w1, w3, w2.
+SWEEP_M = 4096
+SWEEP_BLOCKS = 30
+SWEEP_STEPS = 8
+SWEEP_LAYERS = (("qkv", 3840, 11520), ("out", 3840, 3840),
+                ("w1", 3840, 10240), ("w3", 3840, 10240), ("w2", 10240, 3840))
+SWEEP_R = 128
+
+
+def sweep_precision(block, name):
+    """"bf16" or "w4a4" for one linear of the sweep (Ultra variant)."""
+    if name in ("qkv", "out") or block < 5 or block >= 25:
+        return "bf16"
+    return "w4a4"
+
+
+def sweep_layers():
+    """The sweep's linears in execution order: dicts with block, name, K, N,
+    precision and the weight seed 5000 + 10 * block + layer index."""
+    out = []
+    for b in range(SWEEP_BLOCKS):
+        for li, (name, K, N) in enumerate(SWEEP_LAYERS):
+            out.append(dict(block=b, name=name, K=K, N=N, precision=sweep_precision(b, name),
+                            seed=5000 + 10 * b + li))
+    return out
+
+
+def sweep_activation_seed(step, layer_index):
+    """Seed of the fresh activations of one (forward step, linear) pair."""
+    return 6000 + 1000 * step + layer_index
