@@ -40,6 +40,7 @@ SIGNATURES = {
     "svdq_linear_w4a4_gated": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                       _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
                                       _c_void_p, _c_void_p, _size, _c_void_p]),
+    "svdq_linear_bf16": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p]),
 }
 
 STATUS = {

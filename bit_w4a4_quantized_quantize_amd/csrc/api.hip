@@ -572,4 +572,36 @@ int svdq_linear_w4a4_gated(const void* x, const void* smooth, const void* weight
   return ok();
 }
 
+int svdq_linear_bf16(const void* x, const void* weight, const void* bias, int64_t M, int64_t N,
+                     int64_t K, void* y, void* stream) {
+  int st = check_mk(M, K, 0);
+  if (st) return st;
+  if (N < 0) return fail(SVDQ_ERR_SHAPE, "N = %lld is negative", (long long)N);
+  if (N > kMaxDim) return fail(SVDQ_ERR_UNSUPPORTED, "dimension above 2^24 (N=%lld)", (long long)N);
+  if (M == 0 || N == 0) return ok();
+  {
+    const char* names[] = {"x", "weight", "y"};
+    const void* ptrs[] = {x, weight, y};
+    if ((st = check_ptrs(names, ptrs, 3))) return st;
+  }
+  if (bias != nullptr && !aligned16(bias)) return fail(SVDQ_ERR_ALIGN, "bias is not 16-byte aligned");
+  if (svdq::gemm_bf16_tiles(M, N) >= (int64_t(1) << 30))
+    return fail(SVDQ_ERR_UNSUPPORTED, "too many output tiles (M=%lld N=%lld)", (long long)M, (long long)N);
+  const Range in[] = {range("x", x, (size_t)M * K * 2), range("weight", weight, (size_t)N * K * 2),
+                      range("bias", bias, (size_t)N * 2)};
+  const Range out[] = {range("y", y, (size_t)M * N * 2)};
+  if ((st = check_alias(in, 3, out, 1))) return st;
+  svdq::Bf16GemmArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(weight);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.y = static_cast<uint16_t*>(y);
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  hipError_t e = svdq::launch_gemm_bf16(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "bf16 gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -354,8 +354,9 @@ hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t col_tiles = GATED ? ((a.gated_f + 31) / 32 + TN - 1) / TN : (a.N + C::BN - 1) / C::BN;
   const int64_t tiles = col_tiles * ((a.M + C::BM - 1) / C::BM);
   const unsigned lds = 2 * C::kStageBytes;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN, GATED>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN, GATED>),
+                                    (int)lds, lds_set);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((tiles + 7) / 8 * 8));
   hipLaunchKernelGGL((gemm_lds_kernel<WM, WN, TM, TN, GATED>), grid, dim3(C::kThreads), lds, stream, a);

@@ -5,7 +5,23 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace svdq {
+
+// Raise a kernel's dynamic LDS limit to `bytes`, once per device and process
+// (`done` holds one bit per device ordinal), so that launches in a steady
+// state (or under stream capture) make no attribute calls.
+inline hipError_t set_lds_limit_once(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = uint64_t(1) << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // a1: quant(x * smooth) -> qact [M, K/2], ascales [K/16, M] (canonical layout;
 // the work is laid out for HBM streaming).
@@ -44,6 +60,18 @@ hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
 // packed activations (qact holds the packed buffer, ascales unused) and packed
 // weights: each element dequantised once per workgroup into LDS
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream);
+
+// Linears kept in bf16: y = bf16(x @ w^T + bias), x [M, K], w [N, K], bias [N]
+// or NULL, y [M, N]; K a multiple of 16, M and N below 2^24.
+struct Bf16GemmArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  const uint16_t* bias;
+  uint16_t* y;
+  int64_t M, N, K;
+};
+int64_t gemm_bf16_tiles(int64_t M, int64_t N);
+hipError_t launch_gemm_bf16(const Bf16GemmArgs& a, hipStream_t stream);
 
 // a3: load-time repack of qweight/wscales into the MFMA-order layout, and back.
 // The same chunk layout holds packed activations (rows = tokens).

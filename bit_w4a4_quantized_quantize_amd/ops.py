@@ -267,3 +267,28 @@ def linear_w4a4_gated(x, w: SVDQLinearWeights, h=None, workspace=None):
         _p(w.proj_down) if w.R > 0 else None, _p(w.proj_up) if w.R > 0 else None, _p(w.bias),
         M, F_out, K, w.R, _p(h), _p(workspace), workspace.numel(), _stream(x.device)))
     return h
+
+
+def linear_bf16(x, weight, bias=None, y=None):
+    """A linear kept in bf16: y [M, N] = bf16(x @ weight^T + bias), with x [M, K],
+    weight [N, K] and bias [N] (or None), all bf16."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(weight, "weight", torch.bfloat16, 2)
+    M, K = x.shape
+    N = weight.shape[0]
+    if weight.shape[1] != K:
+        raise ValueError(f"x has K={K}, weight has K={weight.shape[1]}")
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, 1)
+        if bias.numel() != N:
+            raise ValueError(f"bias has {bias.numel()} entries, N={N}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(y, "y", torch.bfloat16, 2)
+        if tuple(y.shape) != (M, N):
+            raise ValueError(f"y must be [{M}, {N}], got {tuple(y.shape)}")
+    L = _lib.lib()
+    _lib.check("svdq_linear_bf16", L.svdq_linear_bf16(
+        _p(x), _p(weight), _p(bias), M, N, K, _p(y), _stream(x.device)))
+    return y

@@ -213,6 +213,23 @@ int svdq_linear_w4a4_gated(const void* x, const void* smooth, const void* weight
                            const void* proj_up, const void* bias, int64_t M, int64_t F, int64_t K,
                            int64_t R, void* h, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Linears kept in bf16. A mixed-precision NVFP4 model leaves some linears
+ * unquantised (blog page "Z-Image NVFP4 ...", variant table: the "Ultra"
+ * variant keeps attention qkv/out and every linear of blocks 0-4 and 25-29 in
+ * bf16, and its key insight names attention as the quantisation-sensitive
+ * part). Such a layer is the original linear
+ *
+ *   y = bf16( x @ weight^T + bias[n] )
+ *
+ *   x [M, K] bf16, weight [N, K] bf16 (row-major, as stored in a bf16
+ *   checkpoint), bias [N] bf16 or NULL, y [M, N] bf16 (round to nearest even);
+ *   y must not overlap any input. Products are exact and accumulate in fp32
+ *   on the matrix cores. K: a positive multiple of 16; M, N up to 2^24.
+ */
+int svdq_linear_bf16(const void* x, const void* weight, const void* bias, int64_t M, int64_t N,
+                     int64_t K, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

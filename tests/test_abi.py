@@ -225,3 +225,31 @@ def test_gated_empty_is_ok():
     L = _lib.lib()
     assert L.svdq_gemm_w4a4_gated(fake(1), fake(2), fake(3), fake(5), fake(6), fake(8), None,
                                   64, 48, 256, 16, fake(9), None) == 3
+
+
+def bf16_linear(**kw):
+    args = dict(x=fake(1), weight=fake(2), bias=None, M=64, N=128, K=256, y=fake(3), stream=None)
+    args.update(kw)
+    L = _lib.lib()
+    return L.svdq_linear_bf16(args["x"], args["weight"], args["bias"], args["M"], args["N"], args["K"],
+                              args["y"], args["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), 2), (dict(N=-1), 2), (dict(K=0), 2), (dict(K=40), 2),
+    (dict(x=None), 1), (dict(weight=None), 1), (dict(y=None), 1),
+    (dict(y=fake(3) + 2), 4), (dict(bias=fake(4) + 8), 4),
+    (dict(y=fake(1) + 64), 6),                              # y overlaps x
+    (dict(bias=fake(3) + 16), 6),                           # y overlaps the bias
+    (dict(N=(1 << 24) + 16), 3), (dict(M=(1 << 24) + 16), 3),
+])
+def test_linear_bf16_rejections(kw, code):
+    assert bf16_linear(**kw) == code
+
+
+@no_gpu_only
+def test_linear_bf16_empty_is_ok():
+    assert bf16_linear(M=0) == 0
+    assert bf16_linear(N=0) == 0
+    assert bf16_linear(M=0, x=None, weight=None, y=None) == 0
