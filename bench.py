@@ -56,6 +56,15 @@ FFN_BLOCKS = {
 }
 
 
+# the mixed-precision linear sweep of a whole DiT forward (bf16 and W4A4 layers)
+SWEEPS = {
+    "dit_sweep_1024": "DiT mixed-precision linear sweep at 1024^2: 30 blocks x {qkv, out, w1, w3, w2}, "
+                      "M=4096; qkv/out of every block and all linears of blocks 0-4 and 25-29 in bf16, "
+                      "the other 60 FFN linears SVDQuant W4A4 NVFP4 R=128; one step = one forward (150 "
+                      "linears) with fresh activations, cycling over 8 forwards",
+}
+
+
 def workload_cfg(name):
     import workloads
     ref, desc = WORKLOADS[name]
@@ -65,7 +74,8 @@ def workload_cfg(name):
 
 def parse():
     p = argparse.ArgumentParser()
-    p.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS), default=DEFAULT_WORKLOAD,
+    p.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS) + sorted(SWEEPS),
+                   default=DEFAULT_WORKLOAD,
                    help="layer shape (the default is the headline workload; the rest are for comparison)")
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
@@ -76,6 +86,7 @@ def parse():
     p.add_argument("--warm", action="store_true", help="reuse one set (warm cache)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-iters", type=int, default=100)
+    p.add_argument("--no-graph", action="store_true", help="sweep: time eager launches only")
     p.add_argument("--copy-calibration", action="store_true",
                    help="finish with a plain 512 MiB device copy (to calibrate HBM byte counters)")
     return p.parse_args()
@@ -346,8 +357,289 @@ def run_ffn_block(args):
     print(json.dumps(result), flush=True)
 
 
+def sweep_build(dev, n_fwd):
+    """Weights of the sweep's 150 linears and fresh activations for n_fwd forwards, drawn on
+    the device (torch's generator, seeded per layer / per (forward, layer)) with the
+    distributions of the seeded host recipe: x ~ N(0,1) with 1% outlier channels x20 (fixed
+    per layer), W ~ N(0, 0.02), proj ~ N(0, 0.02), bias ~ N(0, 0.01); the NVFP4 weights come
+    from the library's own quantiser as in make_sets."""
+    import torch
+
+    import workloads
+    from bit_w4a4_quantized_quantize_amd import ops
+
+    bf = torch.bfloat16
+    M, R = workloads.SWEEP_M, workloads.SWEEP_R
+    layers = workloads.sweep_layers()
+    built = []
+    for L in layers:
+        g = torch.Generator(device=dev).manual_seed(L["seed"])
+        K, N = L["K"], L["N"]
+        idx = torch.randperm(K, generator=g, device=dev)[: int(math.floor(0.01 * K))]
+        e = dict(L, idx=idx)
+        if L["precision"] == "bf16":
+            e["W"] = (torch.randn(N, K, generator=g, device=dev) * 0.02).to(bf)
+            e["b"] = (torch.randn(N, generator=g, device=dev) * 0.01).to(bf)
+        else:
+            xcal = torch.randn(M, K, generator=g, device=dev)
+            xcal[:, idx] *= 20.0
+            absmax = xcal.to(bf).float().abs().amax(0)
+            smooth = (1.0 / absmax.clamp_min(1e-6).sqrt()).to(bf)
+            del xcal
+            W = torch.randn(N, K, generator=g, device=dev) * 0.02
+            wc = (W.abs().amax(1).double() / (6.0 * 448.0)).to(bf)
+            wt = torch.ones(1, dtype=bf, device=dev)
+            Wp = (W / (wt.float() * wc.float())[:, None]).to(bf)
+            del W
+            qw, ws, _ = ops.quantize_act(Wp, torch.ones(K, dtype=bf, device=dev))
+            del Wp
+            pd = (torch.randn(K, R, generator=g, device=dev) * 0.02).to(bf)
+            pu = (torch.randn(N, R, generator=g, device=dev) * 0.02).to(bf)
+            b = (torch.randn(N, generator=g, device=dev) * 0.01).to(bf)
+            e["layer"] = ops.SVDQLinearWeights(N=N, K=K, weight=qw, wscales=ws, wcscales=wc, wtscale=wt,
+                                               smooth=smooth, proj_down=pd, proj_up=pu, bias=b).packed()
+        built.append(e)
+    acts = []
+    for f in range(n_fwd):
+        row = []
+        for li, L in enumerate(layers):
+            g = torch.Generator(device=dev).manual_seed(workloads.sweep_activation_seed(f, li))
+            x = torch.randn(M, L["K"], generator=g, device=dev)
+            x[:, built[li]["idx"]] *= 20.0
+            row.append(x.to(bf))
+            del x
+        acts.append(row)
+    return built, acts
+
+
+def sweep_flops(L, M, R):
+    f = 2 * M * L["K"] * L["N"]
+    return f + (2 * M * R * (L["K"] + L["N"]) if L["precision"] == "w4a4" else 0)
+
+
+def cpu_baseline_sweep(M, R, layers):
+    """The oracle on one bf16 layer and one W4A4 layer of the sweep, on a row sample, scaled to
+    a whole forward by flop counts (an extrapolation: the oracle's per-flop rate at these
+    shapes times the forward's flop count per precision)."""
+    import numpy as np
+
+    import workloads
+    from oracle import svdq as S
+
+    rows = 256
+    d = workloads.make_bf16_linear(rows, 3840, 3840, kind="dit", seed=5001)
+    t0 = time.perf_counter()
+    S.linear_bf16(d["x"], d["W"], d["bias"])
+    t_bf = time.perf_counter() - t0
+    rate_bf = 2 * rows * 3840 * 3840 / t_bf
+    d = workloads.make_linear(rows, 3840, 10240, R, kind="dit", seed=5002)
+    qw, ws = S.quantize_weight(d["W"], d["wcscales"], d["wtscale"])   # load time, not timed
+    t0 = time.perf_counter()
+    S.linear_w4a4(d["x"], d["smooth"], qw, ws, d["wcscales"], d["wtscale"], d["proj_down"], d["proj_up"],
+                  d["bias"])
+    t_q = time.perf_counter() - t0
+    rate_q = (2 * rows * 3840 * 10240 + 2 * rows * R * (3840 + 10240)) / t_q
+    f_bf = sum(sweep_flops(L, M, R) for L in layers if L["precision"] == "bf16")
+    f_q = sum(sweep_flops(L, M, R) for L in layers if L["precision"] == "w4a4")
+    t_fwd = f_bf / rate_bf + f_q / rate_q
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    del np
+    return {"value": (f_bf + f_q) / t_fwd / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} rows of one bf16 out projection (3840->3840, {t_bf:.2f} s) and of one W4A4 "
+                      f"w1 layer (3840->10240, R={R}, {t_q:.2f} s, weight quantisation excluded), "
+                      f"extrapolated to one forward by flop count: {t_fwd:.1f} s per forward"}
+
+
+def run_sweep(args):
+    import torch
+
+    import workloads
+    from bit_w4a4_quantized_quantize_amd import ops
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    M, R = workloads.SWEEP_M, workloads.SWEEP_R
+    n_fwd = workloads.SWEEP_STEPS
+    print(f"[bench] building the sweep: {workloads.SWEEP_BLOCKS} blocks, {n_fwd} forwards of fresh activations",
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    built, acts = sweep_build(dev, n_fwd)
+    layers = [{k: v for k, v in e.items() if k in ("block", "name", "K", "N", "precision")} for e in built]
+    ys = {name: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for name, _, N in workloads.SWEEP_LAYERS}
+    ws_bytes = max(ops.linear_workspace_bytes(M, e["N"], e["K"], R) for e in built if e["precision"] == "w4a4")
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] built in {time.perf_counter() - t0:.1f} s; {torch.cuda.memory_allocated(dev) / 2**30:.1f} GiB "
+          f"resident", file=sys.stderr, flush=True)
+    flops_fwd = sum(sweep_flops(L, M, R) for L in layers)
+    flops_bf = sum(sweep_flops(L, M, R) for L in layers if L["precision"] == "bf16")
+    flops_q = flops_fwd - flops_bf
+
+    def forward(f, which=("bf16", "w4a4")):
+        for li, e in enumerate(built):
+            if e["precision"] not in which:
+                continue
+            x = acts[f][li]
+            if e["precision"] == "bf16":
+                ops.linear_bf16(x, e["W"], e["b"], y=ys[e["name"]])
+            else:
+                ops.linear_w4a4(x, e["layer"], y=ys[e["name"]], workspace=ws)
+
+    # eager, then one captured graph per forward (the launch sequence of a whole forward)
+    for f in range(n_fwd):
+        forward(f)
+    torch.cuda.synchronize()
+    graphs = []
+    if not args.no_graph:
+        for f in range(n_fwd):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                forward(f)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(i):
+        if graphs:
+            graphs[i % n_fwd].replay()
+        else:
+            forward(i % n_fwd)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    tflops = flops_fwd / (ms_per_step * 1e-3) / 1e12
+    print(f"[bench] sweep ({'graph' if graphs else 'eager'}): {ms_per_step:.2f} ms per forward, {tflops:.1f} TFLOP/s "
+          f"(wall {wall * 1e3 / args.steps:.2f} ms)", file=sys.stderr, flush=True)
+
+    # split: the bf16 layers alone and the W4A4 layers alone (eager), and eager whole forwards
+    def timed(fn, n):
+        for i in range(min(n, n_fwd)):
+            fn(i)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    n_part = max(2, min(args.steps, n_fwd))
+    bf_ms = timed(lambda i: forward(i % n_fwd, ("bf16",)), n_part)
+    q_ms = timed(lambda i: forward(i % n_fwd, ("w4a4",)), n_part)
+    eager_ms = timed(lambda i: forward(i % n_fwd), n_part)
+    bf_tflops = flops_bf / (bf_ms * 1e-3) / 1e12
+    q_tflops = flops_q / (q_ms * 1e-3) / 1e12
+    print(f"[bench] bf16 layers {bf_ms:.2f} ms ({bf_tflops:.1f} TFLOP/s), W4A4 layers {q_ms:.2f} ms "
+          f"({q_tflops:.1f} TFLOP/s), eager forward {eager_ms:.2f} ms", file=sys.stderr, flush=True)
+
+    # the activation quantiser alone over the same tensors (the 60 W4A4 layers of a forward)
+    qbuf = {}
+    for e in built:
+        if e["precision"] == "w4a4" and e["K"] not in qbuf:
+            K = e["K"]
+            qbuf[K] = (torch.empty(ops._lib.lib().svdq_packed_act_bytes(M, K), dtype=torch.uint8, device=dev),
+                       torch.empty((M, R), dtype=torch.bfloat16, device=dev))
+    qws = torch.empty(max(1, max(ops.quantize_act_workspace_bytes(M, K, R) for K in qbuf)), dtype=torch.uint8,
+                      device=dev)
+
+    def quant_fwd(f):
+        for li, e in enumerate(built):
+            if e["precision"] == "w4a4":
+                qa, lo = qbuf[e["K"]]
+                ops.quantize_act(acts[f][li], e["layer"].smooth, e["layer"].proj_down, qact=qa, lora_act=lo,
+                                 packed=True, workspace=qws)
+
+    quant_ms = timed(lambda i: quant_fwd(i % n_fwd), n_part)
+    qbytes = sum(2 * M * e["K"] + 2 * e["K"] + 2 * e["K"] * R + M * e["K"] // 2 + M * e["K"] // 16 + 2 * M * R
+                 for e in built if e["precision"] == "w4a4")
+    quant_gbs = qbytes / (quant_ms * 1e-3) / 1e9
+    print(f"[bench] activation quantiser over the forward's 60 W4A4 inputs: {quant_ms:.3f} ms "
+          f"({quant_gbs:.0f} GB/s)", file=sys.stderr, flush=True)
+
+    # single bf16 layer shapes, with torch's own bf16 linear (hipBLASLt) on the same operands as context
+    shapes = {}
+    for name, K, N in workloads.SWEEP_LAYERS:
+        e = next(e for e in built if e["name"] == name and e["precision"] == "bf16")
+        li = built.index(e)
+        xs = [acts[f][li] for f in range(n_fwd)]
+        ours = timed(lambda i: ops.linear_bf16(xs[i % n_fwd], e["W"], e["b"], y=ys[name]), 20)
+        ref = timed(lambda i: torch.nn.functional.linear(xs[i % n_fwd], e["W"], e["b"]), 20)
+        fl = 2 * M * K * N
+        shapes[name] = {"K": K, "N": N, "us": round(ours * 1e3, 1), "TFLOPs": round(fl / (ours * 1e-3) / 1e12, 1),
+                        "torch_linear_us": round(ref * 1e3, 1)}
+    print(f"[bench] bf16 shapes: {shapes}", file=sys.stderr, flush=True)
+
+    n_q = sum(1 for L in layers if L["precision"] == "w4a4")
+    result = {
+        "metric": f"DiT mixed-precision linear sweep TFLOP/s ({len(layers) - n_q} bf16 + {n_q} W4A4 NVFP4 linears "
+                  f"per forward) at M={M}, 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+f16",
+        "data": "synthetic",
+        "config": {
+            "workload": SWEEPS[args.workload],
+            "flop_per_step": flops_fwd,
+            "flop_bf16": flops_bf,
+            "flop_w4a4": flops_q,
+            "launch": "one HIP graph per forward" if graphs else "eager",
+            "cache": f"cold (fresh activations per (forward, layer), {n_fwd} forwards resident)",
+        },
+        "pct_mfma_peak": round(100.0 * tflops / PEAK_F16_MFMA_TFLOPS, 2),
+        "roofline": {
+            "kernel": "gemm_bf16_kernel (the bf16 layers: 55% of the forward's flops)",
+            "bound": "mfma",
+            "achieved": round(bf_tflops, 2),
+            "peak": PEAK_F16_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bf_tflops / PEAK_F16_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "flop_per_forward": flops_bf,
+            "ms_per_forward": round(bf_ms, 4),
+        },
+        "w4a4_layers": {"ms_per_forward": round(q_ms, 4), "TFLOPs": round(q_tflops, 2)},
+        "eager_ms_per_step": round(eager_ms, 4),
+        "quant_kernel": {"ms_per_forward": round(quant_ms, 4), "hbm_bytes_per_forward": qbytes,
+                         "achieved_GBps": round(quant_gbs, 1), "frac_of_hbm_peak": round(quant_gbs / PEAK_HBM_GBS, 4)},
+        "bf16_shapes": shapes,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample of the sweep's layers", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_sweep(M, R, layers)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload in SWEEPS:
+        if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+            print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
+            sys.exit(2)
+        return run_sweep(args)
     if args.workload in FFN_BLOCKS:
         if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
             print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
