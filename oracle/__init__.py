@@ -16,6 +16,10 @@ in NumPy with float64 / int64 arithmetic:
                      * wtscale * wcscales + (x @ proj_down) @ proj_up^T + bias
                  (model card "nunchaku-z-image-turbo-svdq", section
                  "What's stored on disk", runtime reconstruction formula).
+* ``prep``     - SVDQuant weight preparation from a bf16 weight: smoothing,
+                 the rank-R split (exact truncated SVD as the optimum, and the
+                 randomized range finder the device runs), the residual, the
+                 two-level scales and the residual's quantisation.
 * ``repack``   - the index map of the library's MFMA-order weight layout,
                  written independently from its definition, so the GPU repack
                  can be compared byte for byte.
@@ -32,4 +36,4 @@ output or test vector, so the activation quantiser is pinned only to the
 readings stated in svdq.py, not to any published artifact.
 """
 
-from . import formats, svdq, repack  # noqa: F401
+from . import formats, svdq, repack, prep  # noqa: F401
