@@ -41,6 +41,12 @@ SIGNATURES = {
                                       _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
                                       _c_void_p, _c_void_p, _size, _c_void_p]),
     "svdq_linear_bf16": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p]),
+    "svdq_prepare_workspace_bytes": (_size, [_i64, _i64, _i64]),
+    "svdq_prepare_weight": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p, _size, _c_void_p]),
+    "svdq_prepare_residual": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64,
+                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
 }
 
 STATUS = {

@@ -604,4 +604,103 @@ int svdq_linear_bf16(const void* x, const void* weight, const void* bias, int64_
   return ok();
 }
 
+size_t svdq_prepare_workspace_bytes(int64_t N, int64_t K, int64_t R) {
+  if (N <= 0 || K <= 0 || K % 16 != 0 || R < 0) return 0;
+  return svdq::prep_workspace_bytes(N, K, R);
+}
+
+static int check_prep(int64_t N, int64_t K, int64_t R, int iters) {
+  int st = check_nk(N, K);
+  if (st) return st;
+  if (R < 0) return fail(SVDQ_ERR_SHAPE, "R = %lld is negative", (long long)R);
+  if (R % 16 != 0 || R > 128)
+    return fail(SVDQ_ERR_UNSUPPORTED, "R = %lld: preparation needs R a multiple of 16, at most 128", (long long)R);
+  if (N > 0 && (R > N || R > K))
+    return fail(SVDQ_ERR_UNSUPPORTED, "R = %lld exceeds min(N, K) = %lld", (long long)R,
+                (long long)(N < K ? N : K));
+  if (iters < 0 || iters > 16) return fail(SVDQ_ERR_INVALID, "iters = %d outside 0..16", iters);
+  if (N > 0 && (st = check_rsrc_sizes(N, K, 0))) return st;
+  return SVDQ_OK;
+}
+
+static int prep_common(const void* weight, const void* smooth, const void* omega, const void* proj_down,
+                       const void* proj_up, bool factors_out, int64_t N, int64_t K, int64_t R, void* qweight,
+                       void* wscales, void* wcscales, void* wtscale, void* workspace, size_t workspace_bytes) {
+  int st;
+  {
+    const char* names[] = {"weight", "smooth", "qweight", "wscales", "wcscales", "wtscale", "workspace"};
+    const void* ptrs[] = {weight, smooth, qweight, wscales, wcscales, wtscale, workspace};
+    if ((st = check_ptrs(names, ptrs, 7))) return st;
+  }
+  if (R > 0) {
+    const char* names[] = {"proj_down", "proj_up"};
+    const void* ptrs[] = {proj_down, proj_up};
+    if ((st = check_ptrs(names, ptrs, 2))) return st;
+    if (factors_out) {
+      const char* n2[] = {"omega"};
+      const void* p2[] = {omega};
+      if ((st = check_ptrs(n2, p2, 1))) return st;
+    }
+  }
+  const size_t need = svdq::prep_workspace_bytes(N, K, R);
+  if (workspace_bytes < need)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t fb_d = (size_t)K * R * 2, fb_u = (size_t)N * R * 2;
+  const Range in[] = {range("weight", weight, (size_t)N * K * 2), range("smooth", smooth, (size_t)K * 2),
+                      range("omega", factors_out && R > 0 ? omega : nullptr, (size_t)K * R * 4),
+                      range("proj_down", !factors_out && R > 0 ? proj_down : nullptr, fb_d),
+                      range("proj_up", !factors_out && R > 0 ? proj_up : nullptr, fb_u)};
+  const Range out[] = {range("qweight", qweight, (size_t)N * (K / 2)),
+                       range("wscales", wscales, (size_t)(K / 16) * N),
+                       range("wcscales", wcscales, (size_t)N * 2), range("wtscale", wtscale, 2),
+                       range("proj_down", factors_out && R > 0 ? proj_down : nullptr, fb_d),
+                       range("proj_up", factors_out && R > 0 ? proj_up : nullptr, fb_u),
+                       range("workspace", workspace, need)};
+  if ((st = check_alias(in, 5, out, 7))) return st;
+  return SVDQ_OK;
+}
+
+int svdq_prepare_weight(const void* weight, const void* smooth, const void* omega, int64_t N, int64_t K,
+                        int64_t R, int iters, void* qweight, void* wscales, void* wcscales, void* wtscale,
+                        void* proj_down, void* proj_up, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_prep(N, K, R, iters);
+  if (st) return st;
+  if (N == 0) return ok();
+  if ((st = prep_common(weight, smooth, omega, proj_down, proj_up, true, N, K, R, qweight, wscales, wcscales,
+                        wtscale, workspace, workspace_bytes)))
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t e = hipSuccess;
+  if (R > 0)
+    e = svdq::launch_prepare_lowrank(static_cast<const uint16_t*>(weight), static_cast<const uint16_t*>(smooth),
+                                     static_cast<const float*>(omega), N, K, R, iters,
+                                     static_cast<uint16_t*>(proj_down), static_cast<uint16_t*>(proj_up), ws, s);
+  if (e == hipSuccess)
+    e = svdq::launch_prepare_residual(static_cast<const uint16_t*>(weight), static_cast<const uint16_t*>(smooth),
+                                      static_cast<const uint16_t*>(proj_down), static_cast<const uint16_t*>(proj_up),
+                                      N, K, R, static_cast<uint8_t*>(qweight), static_cast<uint8_t*>(wscales),
+                                      static_cast<uint16_t*>(wcscales), static_cast<uint16_t*>(wtscale), ws, s);
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "preparation launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int svdq_prepare_residual(const void* weight, const void* smooth, const void* proj_down, const void* proj_up,
+                          int64_t N, int64_t K, int64_t R, void* qweight, void* wscales, void* wcscales,
+                          void* wtscale, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_prep(N, K, R, 0);
+  if (st) return st;
+  if (N == 0) return ok();
+  if ((st = prep_common(weight, smooth, nullptr, proj_down, proj_up, false, N, K, R, qweight, wscales, wcscales,
+                        wtscale, workspace, workspace_bytes)))
+    return st;
+  hipError_t e = svdq::launch_prepare_residual(
+      static_cast<const uint16_t*>(weight), static_cast<const uint16_t*>(smooth),
+      static_cast<const uint16_t*>(proj_down), static_cast<const uint16_t*>(proj_up), N, K, R,
+      static_cast<uint8_t*>(qweight), static_cast<uint8_t*>(wscales), static_cast<uint16_t*>(wcscales),
+      static_cast<uint16_t*>(wtscale), static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "preparation launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

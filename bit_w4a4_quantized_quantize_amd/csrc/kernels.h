@@ -73,6 +73,19 @@ struct Bf16GemmArgs {
 int64_t gemm_bf16_tiles(int64_t M, int64_t N);
 hipError_t launch_gemm_bf16(const Bf16GemmArgs& a, hipStream_t stream);
 
+// Load-time SVDQuant weight preparation: the rank-R split of W / smooth by the
+// randomized range finder (omega [K, R] fp32 from the caller; writes proj_down
+// and proj_up, bf16), and the residual with its two-level scales and NVFP4
+// codes. Both use one workspace of prep_workspace_bytes(N, K, R); R <= 128.
+size_t prep_workspace_bytes(int64_t N, int64_t K, int64_t R);
+hipError_t launch_prepare_lowrank(const uint16_t* W, const uint16_t* smooth, const float* omega, int64_t N,
+                                  int64_t K, int64_t R, int iters, uint16_t* proj_down, uint16_t* proj_up,
+                                  uint8_t* workspace, hipStream_t stream);
+hipError_t launch_prepare_residual(const uint16_t* W, const uint16_t* smooth, const uint16_t* proj_down,
+                                   const uint16_t* proj_up, int64_t N, int64_t K, int64_t R, uint8_t* qweight,
+                                   uint8_t* wscales, uint16_t* wcscales, uint16_t* wtscale, uint8_t* workspace,
+                                   hipStream_t stream);
+
 // a3: load-time repack of qweight/wscales into the MFMA-order layout, and back.
 // The same chunk layout holds packed activations (rows = tokens).
 size_t packed_weight_bytes(int64_t N, int64_t K);

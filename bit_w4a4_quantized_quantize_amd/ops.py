@@ -292,3 +292,67 @@ def linear_bf16(x, weight, bias=None, y=None):
     _lib.check("svdq_linear_bf16", L.svdq_linear_bf16(
         _p(x), _p(weight), _p(bias), M, N, K, _p(y), _stream(x.device)))
     return y
+
+
+def prepare_workspace_bytes(N, K, R):
+    return _lib.lib().svdq_prepare_workspace_bytes(N, K, R)
+
+
+def _prep_outputs(N, K, R, dev):
+    u8 = torch.uint8
+    return dict(qweight=torch.empty((N, K // 2), dtype=u8, device=dev),
+                wscales=torch.empty((K // 16, N), dtype=u8, device=dev),
+                wcscales=torch.empty(N, dtype=torch.bfloat16, device=dev),
+                wtscale=torch.empty(1, dtype=torch.bfloat16, device=dev))
+
+
+def prepare_weight(weight, smooth, omega=None, iters=2, bias=None, workspace=None):
+    """SVDQuant preparation of a bf16 weight [N, K] with smooth [K]: the rank-R
+    split (R = omega.shape[1]; omega [K, R] float32 Gaussian, or None for R = 0),
+    the residual's two-level scales and NVFP4 codes. Returns SVDQLinearWeights
+    (canonical layout)."""
+    _need(weight, "weight", torch.bfloat16, 2)
+    _need(smooth, "smooth", torch.bfloat16, 1)
+    N, K = weight.shape
+    R = 0
+    if omega is not None:
+        _need(omega, "omega", torch.float32, 2)
+        if omega.shape[0] != K:
+            raise ValueError(f"omega must be [K={K}, R], got {tuple(omega.shape)}")
+        R = omega.shape[1]
+    dev = weight.device
+    out = _prep_outputs(N, K, R, dev)
+    pd = torch.empty((K, R), dtype=torch.bfloat16, device=dev) if R else None
+    pu = torch.empty((N, R), dtype=torch.bfloat16, device=dev) if R else None
+    L = _lib.lib()
+    nbytes = L.svdq_prepare_workspace_bytes(N, K, R)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _lib.check("svdq_prepare_weight", L.svdq_prepare_weight(
+        _p(weight), _p(smooth), _p(omega), N, K, R, iters, _p(out["qweight"]), _p(out["wscales"]),
+        _p(out["wcscales"]), _p(out["wtscale"]), _p(pd), _p(pu), _p(workspace), workspace.numel(),
+        _stream(dev)))
+    return SVDQLinearWeights(N=N, K=K, weight=out["qweight"], wscales=out["wscales"], wcscales=out["wcscales"],
+                             wtscale=out["wtscale"], smooth=smooth, proj_down=pd, proj_up=pu, bias=bias)
+
+
+def prepare_residual(weight, smooth, proj_down=None, proj_up=None, workspace=None):
+    """Steps 3-5 of the preparation for given bf16 factors: returns
+    (qweight, wscales, wcscales, wtscale)."""
+    _need(weight, "weight", torch.bfloat16, 2)
+    _need(smooth, "smooth", torch.bfloat16, 1)
+    N, K = weight.shape
+    R = 0 if proj_down is None else proj_down.shape[1]
+    if R:
+        _need(proj_down, "proj_down", torch.bfloat16, 2)
+        _need(proj_up, "proj_up", torch.bfloat16, 2)
+    dev = weight.device
+    out = _prep_outputs(N, K, R, dev)
+    L = _lib.lib()
+    nbytes = L.svdq_prepare_workspace_bytes(N, K, R)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _lib.check("svdq_prepare_residual", L.svdq_prepare_residual(
+        _p(weight), _p(smooth), _p(proj_down), _p(proj_up), N, K, R, _p(out["qweight"]), _p(out["wscales"]),
+        _p(out["wcscales"]), _p(out["wtscale"]), _p(workspace), workspace.numel(), _stream(dev)))
+    return out["qweight"], out["wscales"], out["wcscales"], out["wtscale"]

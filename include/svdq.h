@@ -230,6 +230,42 @@ int svdq_linear_w4a4_gated(const void* x, const void* smooth, const void* weight
 int svdq_linear_bf16(const void* x, const void* weight, const void* bias, int64_t M, int64_t N,
                      int64_t K, void* y, void* stream);
 
+/*
+ * Load-time SVDQuant weight preparation: from a bf16 weight and its smooth
+ * factor, the tensors a prepared layer stores (model card, section "What's
+ * stored on disk": qweight, wscales, wcscales, wtscale, proj_down, proj_up;
+ * the card cites SVDQuant but does not give the steps, which are read from
+ * what the runtime formula needs):
+ *   1. Ws = W / smooth[k];
+ *   2. rank-R split by the randomized range finder: Y = Ws omega, `iters`
+ *      rounds of Y = Ws orth(Ws^T orth(Y)), Q = orth(Y) (Cholesky QR, twice);
+ *      proj_up = bf16(Q), proj_down = bf16(smooth[k] * (Ws^T Q)[k, :]);
+ *   3. E = (W - proj_up proj_down^T) / smooth[k] in fp64 with the bf16
+ *      factors (r summed in order), exact up to that order;
+ *   4. wtscale = 1, wcscales[n] = bf16(max_k |E[n, k]| / (6 * 448));
+ *   5. W' = bf16(E / wcscales[n]) (0 where wcscales is 0), quantised with the
+ *      activation rule and smooth = 1 into qweight [N, K/2], wscales [K/16, N].
+ *
+ *   weight [N, K] bf16 row-major; smooth [K] bf16; omega [K, R] fp32, a
+ *   Gaussian test matrix the caller draws (deterministic given omega);
+ *   outputs as listed, canonical layout (repack with svdq_repack_weight).
+ *   R: 0 (no low-rank part; omega, proj_down, proj_up may be NULL) or a
+ *   multiple of 16, at most 128 and at most min(N, K) (SVDQ_ERR_UNSUPPORTED);
+ *   iters 0..16 (SVDQ_ERR_INVALID). workspace: at least
+ *   svdq_prepare_workspace_bytes(N, K, R) bytes, no initialisation needed.
+ *   W, N*K*2 bytes, must stay below 2 GiB (SVDQ_ERR_UNSUPPORTED).
+ * svdq_prepare_residual runs steps 3-5 for given factors (proj_down,
+ *   proj_up are inputs there); given the factors, its outputs equal the float64
+ *   definition above bit for bit.
+ */
+size_t svdq_prepare_workspace_bytes(int64_t N, int64_t K, int64_t R);
+int svdq_prepare_weight(const void* weight, const void* smooth, const void* omega, int64_t N, int64_t K,
+                        int64_t R, int iters, void* qweight, void* wscales, void* wcscales, void* wtscale,
+                        void* proj_down, void* proj_up, void* workspace, size_t workspace_bytes, void* stream);
+int svdq_prepare_residual(const void* weight, const void* smooth, const void* proj_down, const void* proj_up,
+                          int64_t N, int64_t K, int64_t R, void* qweight, void* wscales, void* wcscales,
+                          void* wtscale, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

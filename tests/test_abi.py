@@ -253,3 +253,40 @@ def test_linear_bf16_empty_is_ok():
     assert bf16_linear(M=0) == 0
     assert bf16_linear(N=0) == 0
     assert bf16_linear(M=0, x=None, weight=None, y=None) == 0
+
+
+def prep(**kw):
+    args = dict(weight=fake(1), smooth=fake(2), omega=fake(3), N=256, K=128, R=16, iters=2, qweight=fake(4),
+                wscales=fake(5), wcscales=fake(6), wtscale=fake(7), pd=fake(8), pu=fake(9), ws=fake(10),
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    L = _lib.lib()
+    return L.svdq_prepare_weight(args["weight"], args["smooth"], args["omega"], args["N"], args["K"], args["R"],
+                                 args["iters"], args["qweight"], args["wscales"], args["wcscales"], args["wtscale"],
+                                 args["pd"], args["pu"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), 2), (dict(K=40), 2), (dict(R=-16), 2), (dict(R=24), 3), (dict(R=144), 3),
+    (dict(N=64, K=32, R=48), 3),                               # R above min(N, K)
+    (dict(iters=-1), 8), (dict(iters=17), 8),
+    (dict(weight=None), 1), (dict(omega=None), 1), (dict(pd=None), 1), (dict(ws=None), 1),
+    (dict(wtscale=fake(7) + 2), 4),
+    (dict(ws_bytes=0), 5),
+    (dict(qweight=fake(1) + 32), 6),                           # qweight overlaps the weight
+    (dict(pu=fake(10)), 6),                                    # proj_up overlaps the workspace
+    (dict(N=1 << 20, K=1 << 11), 3),                           # weight of 4 GiB
+])
+def test_prepare_rejections(kw, code):
+    assert prep(**kw) == code
+
+
+@no_gpu_only
+def test_prepare_empty_and_rank_zero_pointers():
+    assert prep(N=0) == 0
+    L = _lib.lib()
+    # R = 0: omega and the factors may be NULL (rejected later only for a tiny workspace)
+    assert prep(R=0, omega=None, pd=None, pu=None, ws_bytes=0) == 5
+    assert L.svdq_prepare_workspace_bytes(10240, 3840, 128) >= 10240 * 3840 * 2
+    assert L.svdq_prepare_workspace_bytes(0, 3840, 128) == 0

@@ -163,3 +163,25 @@ def sweep_layers():
 def sweep_activation_seed(step, layer_index):
     """Seed of the fresh activations of one (forward step, linear) pair."""
     return 6000 + 1000 * step + layer_index
+
+
+def make_omega(K, R, seed):
+    """Gaussian test matrix [K, R] (float32, N(0, 1)) for the randomized rank-R
+    split of weight preparation."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.standard_normal((K, R), dtype=np.float32)
+
+
+def make_prep_weight(N, K, seed, strong=8):
+    """A bf16 weight [N, K] ~ N(0, 0.02) plus `strong` directions of decaying
+    strength (trained weights have a few large singular values; SVDQuant's
+    low-rank branch targets them), and a smooth factor from an outlier
+    activation (same recipe as "dit"). Returns (W bits, smooth bits, x bits)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    if strong:
+        A = rng.standard_normal((N, strong), dtype=np.float32) * np.geomspace(1.0, 0.3, strong).astype(np.float32)
+        B = rng.standard_normal((strong, K), dtype=np.float32) * np.float32(0.02)
+        W = W + A @ B
+    x, smooth = make_activation(64, K, kind="dit", seed=seed + 1)
+    return f32_to_bf16_bits(W), smooth, x
