@@ -65,6 +65,15 @@ SWEEPS = {
 }
 
 
+# load-time SVDQuant preparation of one weight (the FFN w1 shape at 1024^2)
+PREPS = {
+    "prep_ffn_w1_1024": dict(N=10240, K=3840, R=128, iters=2, seed=1003,
+                             desc="SVDQuant weight preparation of a DiT FFN w1 weight (N=10240, K=3840, R=128, "
+                                  "2 power rounds): randomized rank-R split, residual, two-level scales, NVFP4 codes"),
+}
+PEAK_FP64_TFLOPS = 78.6    # MI355X fp64 vector peak
+
+
 def workload_cfg(name):
     import workloads
     ref, desc = WORKLOADS[name]
@@ -74,7 +83,7 @@ def workload_cfg(name):
 
 def parse():
     p = argparse.ArgumentParser()
-    p.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS) + sorted(SWEEPS),
+    p.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS) + sorted(SWEEPS) + sorted(PREPS),
                    default=DEFAULT_WORKLOAD,
                    help="layer shape (the default is the headline workload; the rest are for comparison)")
     p.add_argument("--gpus", type=int, default=1)
@@ -633,8 +642,115 @@ def run_sweep(args):
     print(json.dumps(result), flush=True)
 
 
+def cpu_baseline_prep(W, sm, omega, iters, rows=1024):
+    """The oracle's preparation: the randomized split on the whole weight (it needs all of
+    it), the row-local residual and quantisation on `rows` rows, scaled to all rows."""
+    from oracle import prep as P
+
+    N = W.shape[0]
+    t0 = time.perf_counter()
+    pu, pd = P.lowrank_randomized(W, sm, omega, iters)
+    t_split = time.perf_counter() - t0
+    from oracle import formats as Fm
+    pu_b, pd_b = Fm.f64_to_bf16(pu), Fm.f64_to_bf16(pd)
+    t0 = time.perf_counter()
+    E = P.residual(W[:rows], sm, pu_b[:rows], pd_b)
+    P.quantize_residual(E)
+    t_rows = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    total = t_split + t_rows * N / rows
+    return total, t_split, t_rows, int(threads)
+
+
+def run_prep(args):
+    import numpy as np
+    import torch
+
+    import workloads
+    from bit_w4a4_quantized_quantize_amd import ops
+
+    cfg = PREPS[args.workload]
+    N, K, R, iters = cfg["N"], cfg["K"], cfg["R"], cfg["iters"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    W, sm, _ = workloads.make_prep_weight(N, K, seed=cfg["seed"])
+    omega = workloads.make_omega(K, R, seed=cfg["seed"] + 1)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    n_sets = 1 if args.warm else 3
+    Wd = [bf(W) for _ in range(n_sets)]
+    smd, omd = bf(sm), torch.from_numpy(omega).to(dev)
+    ws = torch.empty(ops.prepare_workspace_bytes(N, K, R), dtype=torch.uint8, device=dev)
+    steps, warmup = min(args.steps, 20), min(args.warmup, 5)
+
+    def step(i):
+        ops.prepare_weight(Wd[i % n_sets], smd, omd, iters=iters, workspace=ws)
+
+    ms = time_loop(step, n_sets, steps, warmup, stream)
+    ms0 = time_loop(lambda i: ops.prepare_weight(Wd[i % n_sets], smd, omd, iters=0, workspace=ws), n_sets,
+                    steps, warmup, stream)
+    # the residual stage alone (its own entry point, so it can be timed on the stream):
+    # two fp64 passes of N*K*R fused multiply-adds (max |E| per row, then E / wcscales)
+    lay = ops.prepare_weight(Wd[0], smd, omd, iters=iters, workspace=ws)
+    res_ms = time_loop(lambda i: ops.prepare_residual(Wd[i % n_sets], smd, lay.proj_down, lay.proj_up,
+                                                      workspace=ws), n_sets, steps, warmup, stream)
+    flops_res = 2 * 2 * N * K * R
+    res_tflops = flops_res / (res_ms * 1e-3) / 1e12
+    print(f"[bench] preparation: {ms:.2f} ms per {N}x{K} weight (R={R}, {iters} power rounds; {ms0:.2f} ms "
+          f"with none); residual stage {res_ms:.3f} ms ({res_tflops:.1f} TFLOP/s fp64)", file=sys.stderr, flush=True)
+    result = {
+        "metric": f"SVDQuant weight preparation time per weight at N={N},K={K},R={R}, 1 GPU",
+        "value": round(ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+f64",
+        "data": "synthetic",
+        "config": {"workload": cfg["desc"], "cache": "warm" if args.warm else f"rotating {n_sets} weights"},
+        "roofline": {
+            "kernel": "residual stage (svdq_prepare_residual: residual_kernel, fp64, then the quantiser); "
+                      "the preparation's time splits about evenly between it, the fp32 products and the "
+                      "Cholesky QR (profiles/prep_ffn_w1_1024_kernel_stats.txt)",
+            "bound": "alu",
+            "achieved": round(res_tflops, 2),
+            "peak": PEAK_FP64_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(res_tflops / PEAK_FP64_TFLOPS, 4),
+            "traffic": None,
+            "flop_per_launch": flops_res,
+            "avg_launch_us": round(res_ms * 1e3, 2),
+        },
+        "ms_iters0": round(ms0, 3),
+        "ms_per_power_round": round((ms - ms0) / max(iters, 1), 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on the same weight", file=sys.stderr, flush=True)
+        total, t_split, t_rows, threads = cpu_baseline_prep(W, sm, omega, iters)
+        result["cpu_baseline"] = {"value": round(total * 1e3, 1), "unit": "ms", "cores": threads, "kind": "oracle",
+                                  "sample": f"randomized split on the whole weight ({t_split:.2f} s) plus residual "
+                                            f"and quantisation of 1024 rows ({t_rows:.2f} s), scaled to {N} rows"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload in PREPS:
+        if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+            print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
+            sys.exit(2)
+        return run_prep(args)
     if args.workload in SWEEPS:
         if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
             print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)

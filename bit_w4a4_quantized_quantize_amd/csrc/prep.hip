@@ -35,42 +35,43 @@ constexpr int kRMax = 128;   // fp64 Gram / Cholesky of R x R sit in LDS
 // Tall-skinny products with Ws = W / smooth (fp32), 64 x R per workgroup
 // ---------------------------------------------------------------------------
 
-// Y[n, r] = sum_k Ws[n, k] B[k, r]; 256 threads, 64 rows, thread (rg, cg) owns
-// rows 4rg..4rg+3 and columns 8cg..8cg+7.
+// Y[n, r] = sum_k Ws[n, k] B[k, r]; 256 threads, 32 rows per workgroup (enough
+// workgroups to fill the chip at N = 10240), thread (rg, cg) owns rows
+// 2rg, 2rg+1 and columns 8cg..8cg+7.
 __global__ __launch_bounds__(256) void tsmm_nn_kernel(const uint16_t* __restrict__ W,
                                                       const uint16_t* __restrict__ smooth,
                                                       const float* __restrict__ B, float* __restrict__ Y,
                                                       int N, int K, int R) {
-  __shared__ float As[32][64 + 4];    // [k][row]
+  __shared__ float As[32][32 + 4];    // [k][row]
   __shared__ float Bs[32][kRMax];     // [k][r]
   const int t = threadIdx.x;
-  const int n0 = blockIdx.x * 64;
+  const int n0 = blockIdx.x * 32;
   const int rg = t & 15, cg = t >> 4;
-  float acc[4][8];
+  float acc[2][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
   for (int k0 = 0; k0 < K; k0 += 32) {
-    {   // A: row t / 4, 8 k from (t % 4) * 8
-      const int row = t >> 2, kk = (t & 3) * 8;
+    {   // A: row t / 8, 4 k from (t % 8) * 4 (K % 16 == 0: all 4 in or all past K)
+      const int row = t >> 3, kk = (t & 7) * 4;
       const int n = n0 + row, k = k0 + kk;
-      float v[8];
+      float v[4];
       if (n < N && k < K) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(W + (size_t)n * K + k);
-        const u32x4 s = *reinterpret_cast<const u32x4*>(smooth + k);
+        const u32x2 w = *reinterpret_cast<const u32x2*>(W + (size_t)n * K + k);
+        const u32x2 sv = *reinterpret_cast<const u32x2*>(smooth + k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
           const uint32_t wb = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          const uint32_t sb = (s[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const uint32_t sb = (sv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
           v[e] = bf16lo_to_f32(wb) / bf16lo_to_f32(sb);
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        for (int e = 0; e < 4; ++e) v[e] = 0.0f;
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) As[kk + e][row] = v[e];
+      for (int e = 0; e < 4; ++e) As[kk + e][row] = v[e];
     }
     for (int idx = t; idx < 32 * R; idx += 256) {
       const int kk = idx / R, r = idx % R;
@@ -78,15 +79,15 @@ __global__ __launch_bounds__(256) void tsmm_nn_kernel(const uint16_t* __restrict
     }
     __syncthreads();
     if (8 * cg < R) {
-#pragma unroll 4
+#pragma unroll 8
       for (int kk = 0; kk < 32; ++kk) {
-        float a[4], b[8];
+        float a[2], b[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = As[kk][4 * rg + i];
+        for (int i = 0; i < 2; ++i) a[i] = As[kk][2 * rg + i];
 #pragma unroll
         for (int j = 0; j < 8; ++j) b[j] = Bs[kk][8 * cg + j];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
       }
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(256) void tsmm_nn_kernel(const uint16_t* __restrict
   }
   if (8 * cg < R) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + 4 * rg + i;
+    for (int i = 0; i < 2; ++i) {
+      const int n = n0 + 2 * rg + i;
       if (n < N)
 #pragma unroll
         for (int j = 0; j < 8; ++j) Y[(size_t)n * R + 8 * cg + j] = acc[i][j];
@@ -228,57 +229,85 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ Y, 
     for (int j = 0; j < 8; ++j) g[(8 * bi + i) * R + 8 * bj + j] = acc[i][j];
 }
 
-// One workgroup: G = sum of the chunk Grams, right-looking Cholesky in LDS (a
-// pivot that is not positive makes its column zero), then L^-1 in place, row
-// by row (row i of L is copied aside; entry (i, c) = -sum_{c<=k<i} L[i][k]
-// Linv[k][c] / L[i][i]), and T = L^-T (fp32, upper triangular).
-// Dynamic LDS: R*R + R doubles.
-__global__ __launch_bounds__(256) void chol_inv_kernel(const double* __restrict__ Gp, int chunks, int R,
-                                                       float* __restrict__ T) {
+// G = sum of the chunk Grams, chunks added in order (one thread per entry).
+__global__ void gram_sum_kernel(const double* __restrict__ Gp, double* __restrict__ G, int chunks, int RR) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= RR) return;
+  double v = 0.0;
+  for (int c = 0; c < chunks; ++c) v += Gp[(size_t)c * RR + i];
+  G[i] = v;
+}
+
+// One workgroup: right-looking Cholesky of G in LDS (a pivot that is not
+// positive makes its column zero), then X = L^-1 right-looking (row j of X is
+// divided by L[j][j], then X[i][:] -= L[i][j] X[j][:] for i > j). One barrier
+// per step: step j updates with the still unscaled column (row) j times
+// 1/pivot, and column (row) j itself is scaled during step j+1, which does not
+// touch it otherwise. X is lower triangular like L: its off-diagonal entry
+// (i, c) is kept at the mirrored slot (c, i) of the same R x R array, its
+// diagonal aside. Output T = L^-T = X^T (fp32, upper triangular). 1024 threads
+// as 32 x 32 (ty, tx). Dynamic LDS: R*(R+1) + 2R doubles.
+__global__ __launch_bounds__(1024) void chol_inv_kernel(const double* __restrict__ G, int R, float* __restrict__ T) {
   extern __shared__ double lds_d[];
+  const int S_ = R + 1;   // padded row stride: column walks hit distinct banks
   double* L = lds_d;
-  double* row = lds_d + R * R;
+  double* xd = lds_d + R * S_;  // diagonal of X
+  double* ld = xd + R;          // diagonal of L
   const int t = threadIdx.x;
-  for (int idx = t; idx < R * R; idx += 256) {
-    double v = 0.0;
-    for (int c = 0; c < chunks; ++c) v += Gp[(size_t)c * R * R + idx];
-    L[idx] = v;
-  }
+  const int tx = t & 31, ty = t >> 5;
+  for (int idx = t; idx < R * R; idx += 1024) L[(idx / R) * S_ + idx % R] = G[idx];
   __syncthreads();
-  for (int j = 0; j < R; ++j) {
-    const double d = L[j * R + j];
+  double inv_prev = 0.0;   // 1 / pivot of the previous step
+  for (int j = 0; j <= R; ++j) {
+    if (j > 0)   // scale column j-1 below the diagonal
+      for (int i = j + t; i < R; i += 1024) L[i * S_ + j - 1] *= inv_prev;
+    if (j == R) break;
+    const double d = L[j * S_ + j];
     const bool live = d > 0.0;
     const double l = live ? sqrt(d) : 0.0;
+    const double inv_d = live ? 1.0 / d : 0.0;
+    if (t == 0) ld[j] = l;
+    // trailing block (j+1 .. R-1)^2, lower part, with the unscaled column j
+    for (int i = j + 1 + ty; i < R; i += 32) {
+      const double lij = L[i * S_ + j] * inv_d;
+      for (int k = j + 1 + tx; k <= i; k += 32) L[i * S_ + k] -= lij * L[k * S_ + j];
+    }
+    inv_prev = live ? 1.0 / l : 0.0;
     __syncthreads();
-    for (int i = j + 1 + t; i < R; i += 256) L[i * R + j] = live ? L[i * R + j] / l : 0.0;
-    if (t == 0) L[j * R + j] = l;
-    __syncthreads();
-    const int m = R - 1 - j;   // trailing block (j+1 .. R-1)^2, lower part
-    for (int idx = t; idx < m * m; idx += 256) {
-      const int i = j + 1 + idx / m, k = j + 1 + idx % m;
-      if (k <= i) L[i * R + k] -= L[i * R + j] * L[k * R + j];
+  }
+  __syncthreads();
+  // X = I: clear the upper triangle (X's off-diagonal slots), diagonal 1
+  for (int a = ty; a < R; a += 32)
+    for (int b = a + 1 + tx; b < R; b += 32) L[a * S_ + b] = 0.0;
+  for (int i = t; i < R; i += 1024) xd[i] = 1.0;
+  __syncthreads();
+  for (int j = 0; j <= R; ++j) {
+    if (j > 0) {   // scale row j-1 of X: (j-1, c) at slot (c, j-1), c < j-1; diagonal xd[j-1]
+      const double lp = ld[j - 1];
+      for (int c = t; c < j; c += 1024) {
+        if (c < j - 1) L[c * S_ + j - 1] = lp > 0.0 ? L[c * S_ + j - 1] / lp : 0.0;
+        else xd[j - 1] = lp > 0.0 ? xd[j - 1] / lp : 0.0;
+      }
+    }
+    if (j == R) break;
+    const double lj = ld[j];
+    const double inv_l = lj > 0.0 ? 1.0 / lj : 0.0;
+    for (int i = j + 1 + ty; i < R; i += 32) {
+      const double lij = L[i * S_ + j] * inv_l;
+      for (int c = tx; c <= j; c += 32) {
+        const double xjc = c < j ? L[c * S_ + j] : xd[j];   // row j of X, not yet scaled
+        L[c * S_ + i] -= lij * xjc;   // X(i, c) at slot (c, i); c <= j < i
+      }
     }
     __syncthreads();
   }
-  for (int i = 0; i < R; ++i) {
-    for (int k = t; k <= i; k += 256) row[k] = L[i * R + k];
-    __syncthreads();
-    const double lii = row[i];
-    for (int c = t; c < i; c += 256) {
-      double sum = 0.0;
-      for (int k = c; k < i; ++k) sum += row[k] * L[k * R + c];
-      L[i * R + c] = lii > 0.0 ? -sum / lii : 0.0;
-    }
-    if (t == 0) L[i * R + i] = lii > 0.0 ? 1.0 / lii : 0.0;
-    __syncthreads();
-  }
-  for (int idx = t; idx < R * R; idx += 256) {
+  __syncthreads();
+  for (int idx = t; idx < R * R; idx += 1024) {
     const int a = idx / R, b = idx % R;
-    T[idx] = b >= a ? (float)L[b * R + a] : 0.0f;
+    T[idx] = b > a ? (float)L[a * S_ + b] : (b == a ? (float)xd[a] : 0.0f);
   }
 }
 
-// O[n, :] = A[n, :] T (R x R), 64 rows per workgroup, T in LDS.
 // Dynamic LDS: R*R + 64*(R+4) floats.
 __global__ __launch_bounds__(256) void right_mul_kernel(const float* __restrict__ A, const float* __restrict__ T,
                                                         float* __restrict__ O, int rows, int R) {
@@ -426,7 +455,7 @@ __global__ void fill_u16_kernel(uint16_t* __restrict__ p, uint16_t v, int64_t n)
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct PrepWs {
-  size_t wp, ones, y, q, z, z2, zp, gp, tm, total;
+  size_t wp, ones, y, q, z, z2, zp, gp, g, tm, total;
   int splits, rows_per;
 };
 
@@ -451,6 +480,7 @@ PrepWs prep_ws(int64_t N, int64_t K, int64_t R) {
     w.z2 = o; o = al(o + (size_t)K * R * 4);
     w.zp = o; o = al(o + (size_t)S * K * R * 4);
     w.gp = o; o = al(o + (size_t)((big + kGramRows - 1) / kGramRows) * R * R * 8);
+    w.g = o; o = al(o + (size_t)R * R * 8);
     w.tm = o; o = al(o + (size_t)R * R * 4);
   }
   w.total = o;
@@ -464,12 +494,13 @@ size_t prep_workspace_bytes(int64_t N, int64_t K, int64_t R) { return prep_ws(N,
 // a <- orth(a) (Cholesky QR twice), b is scratch of the same shape
 static hipError_t orth(float* a, float* b, int rows, int R, const PrepWs& w, uint8_t* ws, hipStream_t s) {
   double* gp = reinterpret_cast<double*>(ws + w.gp);
+  double* g = reinterpret_cast<double*>(ws + w.g);
   float* tm = reinterpret_cast<float*>(ws + w.tm);
   const int chunks = (rows + kGramRows - 1) / kGramRows;
-  const int lds_chol = (R * R + R) * 8;
+  const int lds_chol = (R * (R + 1) + 2 * R) * 8;
   const int lds_mul = (R * R + 64 * (R + 4)) * 4;
   static std::atomic<uint64_t> chol_set{0}, mul_set{0};
-  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&chol_inv_kernel), (kRMax * kRMax + kRMax) * 8,
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&chol_inv_kernel), (kRMax * (kRMax + 1) + 2 * kRMax) * 8,
                                     chol_set);
   if (e != hipSuccess) return e;
   e = set_lds_limit_once(reinterpret_cast<const void*>(&right_mul_kernel), (kRMax * kRMax + 64 * (kRMax + 4)) * 4,
@@ -479,7 +510,8 @@ static hipError_t orth(float* a, float* b, int rows, int R, const PrepWs& w, uin
     float* in = pass == 0 ? a : b;
     float* out = pass == 0 ? b : a;
     hipLaunchKernelGGL(gram_kernel, dim3(chunks), dim3(256), 0, s, in, gp, rows, R);
-    hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(256), lds_chol, s, gp, chunks, R, tm);
+    hipLaunchKernelGGL(gram_sum_kernel, dim3((R * R + 255) / 256), dim3(256), 0, s, gp, g, chunks, R * R);
+    hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(1024), lds_chol, s, g, R, tm);
     hipLaunchKernelGGL(right_mul_kernel, dim3((rows + 63) / 64), dim3(256), lds_mul, s, in, tm, out, rows, R);
   }
   return hipGetLastError();
@@ -495,7 +527,7 @@ hipError_t launch_prepare_lowrank(const uint16_t* W, const uint16_t* smooth, con
   float* z2 = reinterpret_cast<float*>(ws + w.z2);
   float* zp = reinterpret_cast<float*>(ws + w.zp);
   const int n = (int)N, k = (int)K, r = (int)R;
-  const dim3 g_nn((n + 63) / 64), g_tn((k + 63) / 64, w.splits);
+  const dim3 g_nn((n + 31) / 32), g_tn((k + 63) / 64, w.splits);
   const int64_t kr = (int64_t)K * R;
   auto tn = [&](const float* qq, float* out) {
     hipLaunchKernelGGL(tsmm_tn_kernel, g_tn, dim3(256), 0, s, W, smooth, qq, zp, n, k, r, w.rows_per);
