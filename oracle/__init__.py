@@ -20,6 +20,9 @@ in NumPy with float64 / int64 arithmetic:
                  the rank-R split (exact truncated SVD as the optimum, and the
                  randomized range finder the device runs), the residual, the
                  two-level scales and the residual's quantisation.
+* ``mx``       - the MXFP4 datatype variant (E2M1 with power-of-two scales per
+                 32 K, re-rounded from the NVFP4 operands): quantiser,
+                 dequantiser and the variant layer.
 * ``repack``   - the index map of the library's MFMA-order weight layout,
                  written independently from its definition, so the GPU repack
                  can be compared byte for byte.
@@ -36,4 +39,4 @@ output or test vector, so the activation quantiser is pinned only to the
 readings stated in svdq.py, not to any published artifact.
 """
 
-from . import formats, svdq, repack, prep  # noqa: F401
+from . import formats, svdq, repack, prep, mx  # noqa: F401
