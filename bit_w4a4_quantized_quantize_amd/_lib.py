@@ -47,6 +47,16 @@ SIGNATURES = {
                                    _c_void_p, _size, _c_void_p]),
     "svdq_prepare_residual": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64,
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "svdq_mx_codes_bytes": (_size, [_i64, _i64]),
+    "svdq_mx_scales_bytes": (_size, [_i64, _i64]),
+    "svdq_reround_weight_mxfp4": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "svdq_quantize_act_mxfp4": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "svdq_gemm_mxfp4": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                               _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
+    "svdq_linear_mxfp4_workspace_bytes": (_size, [_i64, _i64, _i64]),
+    "svdq_linear_mxfp4": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, _size,
+                                 _c_void_p]),
 }
 
 STATUS = {

@@ -703,4 +703,211 @@ int svdq_prepare_residual(const void* weight, const void* smooth, const void* pr
   return ok();
 }
 
+size_t svdq_mx_codes_bytes(int64_t rows, int64_t K) {
+  if (rows <= 0 || K <= 0 || K % 128 != 0) return 0;
+  return svdq::mx_codes_bytes(rows, K);
+}
+
+size_t svdq_mx_scales_bytes(int64_t rows, int64_t K) {
+  if (rows <= 0 || K <= 0 || K % 128 != 0) return 0;
+  return (size_t)((rows + 31) / 32) * 32 * (size_t)(K / 32);
+}
+
+static int check_mx(int64_t rows, int64_t K, int64_t R) {
+  int st = check_mk(rows, K, R);
+  if (st) return st;
+  if (K % 128 != 0)
+    return fail(SVDQ_ERR_UNSUPPORTED, "K = %lld: the MXFP4 variant needs K a multiple of 128", (long long)K);
+  if ((int64_t)svdq::mx_codes_bytes(rows, K) >= (int64_t(1) << 31))
+    return fail(SVDQ_ERR_UNSUPPORTED, "MXFP4 operand of %lld rows exceeds 2 GiB", (long long)rows);
+  return SVDQ_OK;
+}
+
+int svdq_reround_weight_mxfp4(const void* qweight, const void* wscales, int64_t N, int64_t K, void* mx_codes,
+                              void* mx_scales, void* stream) {
+  int st = check_mx(N, K, 0);
+  if (st) return st;
+  if (N == 0) return ok();
+  const char* names[] = {"qweight", "wscales", "mx_codes", "mx_scales"};
+  const void* ptrs[] = {qweight, wscales, mx_codes, mx_scales};
+  if ((st = check_ptrs(names, ptrs, 4))) return st;
+  const Range in[] = {range("qweight", qweight, (size_t)N * (K / 2)), range("wscales", wscales, (size_t)(K / 16) * N)};
+  const Range out[] = {range("mx_codes", mx_codes, svdq::mx_codes_bytes(N, K)),
+                       range("mx_scales", mx_scales, svdq_mx_scales_bytes(N, K))};
+  if ((st = check_alias(in, 2, out, 2))) return st;
+  hipError_t e = svdq::launch_reround_mx(static_cast<const uint8_t*>(qweight), static_cast<const uint8_t*>(wscales),
+                                         static_cast<uint8_t*>(mx_codes), static_cast<uint8_t*>(mx_scales), N, K,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "re-round launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int svdq_quantize_act_mxfp4(const void* x, const void* smooth, int64_t M, int64_t K, void* mx_codes,
+                            void* mx_scales, void* stream) {
+  int st = check_mx(M, K, 0);
+  if (st) return st;
+  if (M == 0) return ok();
+  const char* names[] = {"x", "smooth", "mx_codes", "mx_scales"};
+  const void* ptrs[] = {x, smooth, mx_codes, mx_scales};
+  if ((st = check_ptrs(names, ptrs, 4))) return st;
+  const Range in[] = {range("x", x, (size_t)M * K * 2), range("smooth", smooth, (size_t)K * 2)};
+  const Range out[] = {range("mx_codes", mx_codes, svdq::mx_codes_bytes(M, K)),
+                       range("mx_scales", mx_scales, svdq_mx_scales_bytes(M, K))};
+  if ((st = check_alias(in, 2, out, 2))) return st;
+  hipError_t e = svdq::launch_quant_act_mx(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
+                                           static_cast<uint8_t*>(mx_codes), static_cast<uint8_t*>(mx_scales), M, K,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "MX quantisation launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static int validate_mx_gemm(const void* act_codes, const void* act_scales, const void* lora_act, const void* w_codes,
+                            const void* w_scales, const void* wcscales, const void* wtscale, const void* proj_up,
+                            const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, const void* y,
+                            bool check_act) {
+  int st;
+  {
+    const char* names[] = {"w_codes", "w_scales", "wcscales", "wtscale", "y"};
+    const void* ptrs[] = {w_codes, w_scales, wcscales, wtscale, y};
+    if ((st = check_ptrs(names, ptrs, 5))) return st;
+  }
+  if (check_act) {
+    const char* names[] = {"act_codes", "act_scales"};
+    const void* ptrs[] = {act_codes, act_scales};
+    if ((st = check_ptrs(names, ptrs, 2))) return st;
+  }
+  if (R > 0) {
+    const char* names[] = {"proj_up"};
+    const void* ptrs[] = {proj_up};
+    if ((st = check_ptrs(names, ptrs, 1))) return st;
+    if (check_act) {
+      const char* n2[] = {"lora_act"};
+      const void* p2[] = {lora_act};
+      if ((st = check_ptrs(n2, p2, 1))) return st;
+    }
+  }
+  if (bias != nullptr && !aligned16(bias)) return fail(SVDQ_ERR_ALIGN, "bias is not 16-byte aligned");
+  if (svdq::gemm_bf16_tiles(M, N) >= (int64_t(1) << 30))
+    return fail(SVDQ_ERR_UNSUPPORTED, "too many output tiles (M=%lld N=%lld)", (long long)M, (long long)N);
+  return SVDQ_OK;
+}
+
+static svdq::MxGemmArgs mx_args(const void* act_codes, const void* act_scales, const void* lora_act,
+                                const void* w_codes, const void* w_scales, const void* wcscales, const void* wtscale,
+                                const void* proj_up, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                                void* y) {
+  svdq::MxGemmArgs a{};
+  a.act_codes = static_cast<const uint8_t*>(act_codes);
+  a.act_scales = static_cast<const uint8_t*>(act_scales);
+  a.lora_act = static_cast<const uint16_t*>(lora_act);
+  a.w_codes = static_cast<const uint8_t*>(w_codes);
+  a.w_scales = static_cast<const uint8_t*>(w_scales);
+  a.wcscales = static_cast<const uint16_t*>(wcscales);
+  a.wtscale = static_cast<const uint16_t*>(wtscale);
+  a.proj_up = static_cast<const uint16_t*>(proj_up);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.y = static_cast<uint16_t*>(y);
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.R = R;
+  return a;
+}
+
+int svdq_gemm_mxfp4(const void* act_codes, const void* act_scales, const void* lora_act, const void* w_codes,
+                    const void* w_scales, const void* wcscales, const void* wtscale, const void* proj_up,
+                    const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream) {
+  int st = check_mx(M, K, R);
+  if (st) return st;
+  if ((st = check_mx(N, K, R))) return st;
+  if (M == 0 || N == 0) return ok();
+  if ((st = validate_mx_gemm(act_codes, act_scales, lora_act, w_codes, w_scales, wcscales, wtscale, proj_up, bias,
+                             M, N, K, R, y, true)))
+    return st;
+  const Range in[] = {range("act_codes", act_codes, svdq::mx_codes_bytes(M, K)),
+                      range("act_scales", act_scales, svdq_mx_scales_bytes(M, K)),
+                      range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
+                      range("w_codes", w_codes, svdq::mx_codes_bytes(N, K)),
+                      range("w_scales", w_scales, svdq_mx_scales_bytes(N, K)),
+                      range("wcscales", wcscales, (size_t)N * 2), range("wtscale", wtscale, 2),
+                      range("proj_up", R > 0 ? proj_up : nullptr, (size_t)N * R * 2),
+                      range("bias", bias, (size_t)N * 2)};
+  const Range out[] = {range("y", y, (size_t)M * N * 2)};
+  if ((st = check_alias(in, 9, out, 1))) return st;
+  const svdq::MxGemmArgs a = mx_args(act_codes, act_scales, lora_act, w_codes, w_scales, wcscales, wtscale, proj_up,
+                                     bias, M, N, K, R, y);
+  hipError_t e = svdq::launch_gemm_mx(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "MX gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+struct MxWs {
+  size_t codes, scales, lora, partial, total;
+};
+static MxWs mx_ws(int64_t M, int64_t K, int64_t R) {
+  MxWs w{};
+  w.codes = 0;
+  w.scales = align256(svdq::mx_codes_bytes(M, K));
+  w.lora = align256(w.scales + svdq_mx_scales_bytes(M, K));
+  w.partial = align256(w.lora + (size_t)M * R * 2);
+  w.total = w.partial + quant_ws_bytes(M, K, R);
+  return w;
+}
+
+size_t svdq_linear_mxfp4_workspace_bytes(int64_t M, int64_t K, int64_t R) {
+  if (M <= 0 || K <= 0 || K % 128 != 0 || R < 0) return 0;
+  return mx_ws(M, K, R).total;
+}
+
+int svdq_linear_mxfp4(const void* x, const void* smooth, const void* w_codes, const void* w_scales,
+                      const void* wcscales, const void* wtscale, const void* proj_down, const void* proj_up,
+                      const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_mx(M, K, R);
+  if (st) return st;
+  if ((st = check_mx(N, K, R))) return st;
+  if ((st = check_rsrc_sizes(M, K, R))) return st;
+  if (M == 0 || N == 0) return ok();
+  {
+    const char* names[] = {"x", "smooth", "workspace"};
+    const void* ptrs[] = {x, smooth, workspace};
+    if ((st = check_ptrs(names, ptrs, 3))) return st;
+  }
+  if (R > 0) {
+    const char* names[] = {"proj_down"};
+    const void* ptrs[] = {proj_down};
+    if ((st = check_ptrs(names, ptrs, 1))) return st;
+  }
+  if ((st = validate_mx_gemm(nullptr, nullptr, nullptr, w_codes, w_scales, wcscales, wtscale, proj_up, bias, M, N,
+                             K, R, y, false)))
+    return st;
+  const MxWs w = mx_ws(M, K, R);
+  if (workspace_bytes < w.total)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
+  const Range in[] = {range("x", x, (size_t)M * K * 2), range("smooth", smooth, (size_t)K * 2),
+                      range("w_codes", w_codes, svdq::mx_codes_bytes(N, K)),
+                      range("w_scales", w_scales, svdq_mx_scales_bytes(N, K)),
+                      range("wcscales", wcscales, (size_t)N * 2), range("wtscale", wtscale, 2),
+                      range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2),
+                      range("proj_up", R > 0 ? proj_up : nullptr, (size_t)N * R * 2),
+                      range("bias", bias, (size_t)N * 2)};
+  const Range out[] = {range("y", y, (size_t)M * N * 2), range("workspace", workspace, w.total)};
+  if ((st = check_alias(in, 9, out, 2))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t e = svdq::launch_quant_act_mx(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
+                                           ws + w.codes, ws + w.scales, M, K, s);
+  uint16_t* lora = reinterpret_cast<uint16_t*>(ws + w.lora);
+  if (e == hipSuccess && R > 0)
+    e = svdq::launch_lowrank_down(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(proj_down), lora,
+                                  reinterpret_cast<float*>(ws + w.partial), M, K, R, s);
+  if (e == hipSuccess) {
+    const svdq::MxGemmArgs a = mx_args(ws + w.codes, ws + w.scales, lora, w_codes, w_scales, wcscales, wtscale,
+                                       proj_up, bias, M, N, K, R, y);
+    e = svdq::launch_gemm_mx(a, s);
+  }
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "MX layer launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -86,6 +86,33 @@ hipError_t launch_prepare_residual(const uint16_t* W, const uint16_t* smooth, co
                                    uint8_t* wscales, uint16_t* wcscales, uint16_t* wtscale, uint8_t* workspace,
                                    hipStream_t stream);
 
+// MXFP4 variant: E2M1 with one E8M0 scale per 32 K (codes in 32-row x 64-K
+// chunks in the matrix-instruction order, mx_codes_bytes(rows, K) bytes; scales
+// canonical [K/32, rows]). K % 128 == 0 for the GEMM.
+size_t mx_codes_bytes(int64_t rows, int64_t K);
+hipError_t launch_quant_act_mx(const uint16_t* x, const uint16_t* smooth, uint8_t* codes, uint8_t* scales,
+                               int64_t M, int64_t K, hipStream_t stream);
+hipError_t launch_reround_mx(const uint8_t* qweight, const uint8_t* wscales, uint8_t* codes, uint8_t* scales,
+                             int64_t N, int64_t K, hipStream_t stream);
+struct MxGemmArgs {
+  const uint8_t* act_codes;
+  const uint8_t* act_scales;
+  const uint16_t* lora_act;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const uint16_t* wcscales;
+  const uint16_t* wtscale;
+  const uint16_t* proj_up;
+  const uint16_t* bias;
+  uint16_t* y;
+  int64_t M, N, K, R;
+};
+hipError_t launch_gemm_mx(const MxGemmArgs& a, hipStream_t stream);
+// lora_act = bf16(x @ proj_down) alone (the quantiser's down-projection without
+// the quantisation); partial as for launch_quant_lora
+hipError_t launch_lowrank_down(const uint16_t* x, const uint16_t* proj_down, uint16_t* lora_act, float* partial,
+                               int64_t M, int64_t K, int64_t R, hipStream_t stream);
+
 // a3: load-time repack of qweight/wscales into the MFMA-order layout, and back.
 // The same chunk layout holds packed activations (rows = tokens).
 size_t packed_weight_bytes(int64_t N, int64_t K);

@@ -361,4 +361,25 @@ hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const ui
   return hipGetLastError();
 }
 
+hipError_t launch_lowrank_down(const uint16_t* x, const uint16_t* proj_down, uint16_t* lora_act, float* partial,
+                               int64_t M, int64_t K, int64_t R, hipStream_t stream) {
+  if (R <= 0) return hipSuccess;
+  QLArgs a{x, nullptr, proj_down, nullptr, nullptr, lora_act, nullptr, (int)M, (int)K, (int)R, 0, 0};
+  const int ks = k_splits(M, K, R, false);
+  const int steps = (int)((K + 31) / 32);
+  a.split_steps = (steps + ks - 1) / ks;
+  a.partial = ks > 1 ? partial : nullptr;
+  dim3 grid((unsigned)((M + kRows - 1) / kRows), (unsigned)ks);
+  for (int64_t r0 = 0; r0 < R; r0 += kRChunk) {
+    a.r_base = (int)r0;
+    hipLaunchKernelGGL((quant_lora_kernel<kRowTiles, false, false, true>), grid, dim3(64 * kWaves), 0, stream, a);
+  }
+  if (ks > 1) {
+    const int64_t groups = M * (R / 8);
+    hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const float*>(partial), lora_act, (int)M, (int)R, ks);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace svdq

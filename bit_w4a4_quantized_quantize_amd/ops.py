@@ -356,3 +356,66 @@ def prepare_residual(weight, smooth, proj_down=None, proj_up=None, workspace=Non
         _p(weight), _p(smooth), _p(proj_down), _p(proj_up), N, K, R, _p(out["qweight"]), _p(out["wscales"]),
         _p(out["wcscales"]), _p(out["wtscale"]), _p(workspace), workspace.numel(), _stream(dev)))
     return out["qweight"], out["wscales"], out["wcscales"], out["wtscale"]
+
+
+def mx_buffers(rows, K, dev):
+    L = _lib.lib()
+    return (torch.empty(L.svdq_mx_codes_bytes(rows, K), dtype=torch.uint8, device=dev),
+            torch.empty(L.svdq_mx_scales_bytes(rows, K), dtype=torch.uint8, device=dev))
+
+
+def reround_weight_mxfp4(w: "SVDQLinearWeights"):
+    """MXFP4 variant: the layer's canonical NVFP4 weight re-rounded to MX codes and
+    scales (load time). Returns (mx_codes, mx_scales) uint8 buffers."""
+    _check_layer(w)
+    if w.layout != WEIGHT_CANONICAL:
+        raise ValueError("re-rounding reads the canonical weight layout")
+    codes, scales = mx_buffers(w.N, w.K, w.weight.device)
+    L = _lib.lib()
+    _lib.check("svdq_reround_weight_mxfp4", L.svdq_reround_weight_mxfp4(
+        _p(_bytes(w.weight)), _p(_bytes(w.wscales)), w.N, w.K, _p(codes), _p(scales), _stream(w.weight.device)))
+    return codes, scales
+
+
+def quantize_act_mxfp4(x, smooth):
+    """MX(x * smooth): returns (mx_codes, mx_scales) uint8 buffers."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(smooth, "smooth", torch.bfloat16, 1)
+    M, K = x.shape
+    codes, scales = mx_buffers(M, K, x.device)
+    L = _lib.lib()
+    _lib.check("svdq_quantize_act_mxfp4", L.svdq_quantize_act_mxfp4(
+        _p(x), _p(smooth), M, K, _p(codes), _p(scales), _stream(x.device)))
+    return codes, scales
+
+
+def gemm_mxfp4(act_codes, act_scales, lora_act, w_codes, w_scales, w: "SVDQLinearWeights", M, y=None):
+    """The variant's GEMM + low-rank up-projection + epilogue: y [M, N] bf16."""
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.bfloat16, device=act_codes.device)
+    L = _lib.lib()
+    _lib.check("svdq_gemm_mxfp4", L.svdq_gemm_mxfp4(
+        _p(act_codes), _p(act_scales), _p(lora_act) if w.R > 0 else None, _p(w_codes), _p(w_scales),
+        _p(w.wcscales), _p(w.wtscale), _p(w.proj_up) if w.R > 0 else None, _p(w.bias), M, w.N, w.K, w.R,
+        _p(y), _stream(act_codes.device)))
+    return y
+
+
+def linear_mxfp4(x, w: "SVDQLinearWeights", w_codes, w_scales, y=None, workspace=None):
+    """The whole MXFP4 variant layer from x (w supplies smooth, wcscales, wtscale,
+    the low-rank factors and bias; w_codes / w_scales from reround_weight_mxfp4)."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"x has K={K}, the layer K={w.K}")
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device)
+    L = _lib.lib()
+    nbytes = L.svdq_linear_mxfp4_workspace_bytes(M, K, w.R)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _lib.check("svdq_linear_mxfp4", L.svdq_linear_mxfp4(
+        _p(x), _p(w.smooth), _p(w_codes), _p(w_scales), _p(w.wcscales), _p(w.wtscale),
+        _p(w.proj_down) if w.R > 0 else None, _p(w.proj_up) if w.R > 0 else None, _p(w.bias),
+        M, w.N, K, w.R, _p(y), _p(workspace), workspace.numel(), _stream(x.device)))
+    return y

@@ -266,6 +266,45 @@ int svdq_prepare_residual(const void* weight, const void* smooth, const void* pr
                           int64_t N, int64_t K, int64_t R, void* qweight, void* wscales, void* wcscales,
                           void* wtscale, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * MXFP4 datatype variant (an out-of-tolerance speed point, not the pages'
+ * arithmetic). The pages' NVFP4 uses e4m3 scales per 16 K (model card,
+ * header); gfx950's block-scaled matrix instruction takes OCP MX instead: E2M1
+ * with one power-of-two (E8M0) scale per 32 K. Here both operands are
+ * re-rounded into that form. For a 32-block, X = floor(log2 max|v|) - 2 is
+ * clamped to [-127, 127] and stored as X + 127; each code is the E2M1
+ * nearest-even of v * 2^-X, saturating at 6. The weight is re-rounded from the
+ * exact NVFP4 values, the activation from x * smooth. Epilogue, low-rank
+ * branch and bias as in svdq_gemm_w4a4.
+ *
+ * MX operand buffers (rows = tokens or output channels, padded to 32):
+ *   codes  svdq_mx_codes_bytes(rows, K): per 64-K step s and 32-row panel p, a
+ *          1 KB chunk at 1024 * (s * P + p); byte 16 l + j (l = 32 h + c) holds
+ *          row 32 p + c, k = 64 s + 32 h + 2 j (low nibble) and + 1 (high nibble).
+ *   scales svdq_mx_scales_bytes(rows, K): [K/32, padded rows] bytes.
+ *   Padding rows hold zero codes and scale byte 0.
+ * K must be a multiple of 128 (SVDQ_ERR_UNSUPPORTED otherwise).
+ * svdq_reround_weight_mxfp4: canonical qweight/wscales -> MX codes/scales (load time).
+ * svdq_quantize_act_mxfp4: x [M, K], smooth [K] -> MX codes/scales.
+ * svdq_gemm_mxfp4: MX operands + lora_act [M, R] -> y [M, N] bf16.
+ * svdq_linear_mxfp4: the whole variant layer from x, with a workspace of
+ *   svdq_linear_mxfp4_workspace_bytes(M, K, R) bytes.
+ */
+size_t svdq_mx_codes_bytes(int64_t rows, int64_t K);
+size_t svdq_mx_scales_bytes(int64_t rows, int64_t K);
+int svdq_reround_weight_mxfp4(const void* qweight, const void* wscales, int64_t N, int64_t K, void* mx_codes,
+                              void* mx_scales, void* stream);
+int svdq_quantize_act_mxfp4(const void* x, const void* smooth, int64_t M, int64_t K, void* mx_codes,
+                            void* mx_scales, void* stream);
+int svdq_gemm_mxfp4(const void* act_codes, const void* act_scales, const void* lora_act, const void* w_codes,
+                    const void* w_scales, const void* wcscales, const void* wtscale, const void* proj_up,
+                    const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream);
+size_t svdq_linear_mxfp4_workspace_bytes(int64_t M, int64_t K, int64_t R);
+int svdq_linear_mxfp4(const void* x, const void* smooth, const void* w_codes, const void* w_scales,
+                      const void* wcscales, const void* wtscale, const void* proj_down, const void* proj_up,
+                      const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

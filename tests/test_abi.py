@@ -290,3 +290,20 @@ def test_prepare_empty_and_rank_zero_pointers():
     assert prep(R=0, omega=None, pd=None, pu=None, ws_bytes=0) == 5
     assert L.svdq_prepare_workspace_bytes(10240, 3840, 128) >= 10240 * 3840 * 2
     assert L.svdq_prepare_workspace_bytes(0, 3840, 128) == 0
+
+
+@no_gpu_only
+def test_mx_rejections_and_sizes():
+    L = _lib.lib()
+    assert L.svdq_mx_codes_bytes(33, 256) == 64 * 128
+    assert L.svdq_mx_scales_bytes(33, 256) == 64 * 8
+    assert L.svdq_mx_codes_bytes(32, 192) == 0          # K not a multiple of 128
+    assert L.svdq_quantize_act_mxfp4(fake(1), fake(2), 64, 192, fake(3), fake(4), None) == 3
+    assert L.svdq_quantize_act_mxfp4(fake(1), fake(2), 64, 200, fake(3), fake(4), None) == 2
+    assert L.svdq_quantize_act_mxfp4(None, fake(2), 64, 256, fake(3), fake(4), None) == 1
+    assert L.svdq_quantize_act_mxfp4(fake(1), fake(2), 0, 256, None, None, None) == 0
+    assert L.svdq_reround_weight_mxfp4(fake(1), fake(2), 64, 256, fake(1) + 64, fake(4), None) == 6
+    assert L.svdq_gemm_mxfp4(fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), fake(7), fake(8), None,
+                             64, 64, 256, 24, fake(9), None) == 3
+    assert L.svdq_linear_mxfp4(fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), fake(7), fake(8), None,
+                               64, 64, 256, 16, fake(9), fake(10), 0, None) == 5
