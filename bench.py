@@ -72,6 +72,9 @@ PREPS = {
                                   "2 power rounds): randomized rank-R split, residual, two-level scales, NVFP4 codes"),
 }
 PEAK_FP64_TFLOPS = 78.6    # MI355X fp64 vector peak
+PEAK_FP4_MFMA_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak
+# the MXFP4 datatype variant of a layer shape (out of the pages' tolerance: a speed point)
+MX_VARIANTS = {"ffn_w1_1024_mxfp4": "ffn_w1_1024", "qkv_1024_mxfp4": "qkv_1024", "ffn_w2_1024_mxfp4": "ffn_w2_1024"}
 
 
 def workload_cfg(name):
@@ -83,7 +86,8 @@ def workload_cfg(name):
 
 def parse():
     p = argparse.ArgumentParser()
-    p.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS) + sorted(SWEEPS) + sorted(PREPS),
+    p.add_argument("--workload",
+                   choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS) + sorted(SWEEPS) + sorted(PREPS) + sorted(MX_VARIANTS),
                    default=DEFAULT_WORKLOAD,
                    help="layer shape (the default is the headline workload; the rest are for comparison)")
     p.add_argument("--gpus", type=int, default=1)
@@ -744,8 +748,130 @@ def run_prep(args):
     print(json.dumps(result), flush=True)
 
 
+def run_mx(args):
+    """The MXFP4 variant of a layer shape, beside the NVFP4 layer on the same inputs."""
+    import torch
+
+    from bit_w4a4_quantized_quantize_amd import ops
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    cfg, desc = workload_cfg(MX_VARIANTS[args.workload])
+    M, K, N, R = cfg["M"], cfg["K"], cfg["N"], cfg["R"]
+    n_sets = 1 if args.warm else args.sets
+    print(f"[bench] building {n_sets} input sets for M={M} K={K} N={N} R={R} (NVFP4, re-rounded to MXFP4)",
+          file=sys.stderr, flush=True)
+    d, sets = make_sets(cfg, n_sets, "canonical", dev)
+    for st in sets:
+        st["packed_layer"] = st["layer"].packed()
+        st["mx_w"] = ops.reround_weight_mxfp4(st["layer"])
+        st["mx_a"] = ops.quantize_act_mxfp4(st["x"], st["layer"].smooth)
+        st["ws_mx"] = torch.empty(ops._lib.lib().svdq_linear_mxfp4_workspace_bytes(M, K, R), dtype=torch.uint8,
+                                  device=dev)
+        st["y_nv"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    flops_linear = 2 * M * N * K + 2 * M * R * (K + N)
+    flops_gemm = 2 * M * N * K + 2 * M * N * R
+
+    def step(i):
+        st = sets[i]
+        ops.linear_mxfp4(st["x"], st["layer"], st["mx_w"][0], st["mx_w"][1], y=st["y"], workspace=st["ws_mx"])
+
+    for i in range(args.warmup):
+        step(i % n_sets)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i % n_sets)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tflops = flops_linear / (ms * 1e-3) / 1e12
+    kw = max(1, args.warmup // 2)
+    for st in sets:
+        ops.quantize_act(st["x"], st["layer"].smooth, st["layer"].proj_down, qact=st["qact"],
+                         ascales=st["ascales"], lora_act=st["lora"])
+    torch.cuda.synchronize()
+    gemm_ms = time_loop(lambda i: ops.gemm_mxfp4(sets[i]["mx_a"][0], sets[i]["mx_a"][1], sets[i]["lora"],
+                                                 sets[i]["mx_w"][0], sets[i]["mx_w"][1], sets[i]["layer"], M,
+                                                 y=sets[i]["y"]), n_sets, args.kernel_iters, kw, stream)
+    nv_ms = time_loop(lambda i: ops.linear_w4a4(sets[i]["x"], sets[i]["packed_layer"], y=sets[i]["y_nv"],
+                                                workspace=sets[i]["ws"]), n_sets, args.kernel_iters, kw, stream)
+    gemm_tflops = flops_gemm / (gemm_ms * 1e-3) / 1e12
+    # distance from the NVFP4 layer (both outputs from the library, same inputs)
+    st = sets[0]
+    ops.linear_mxfp4(st["x"], st["layer"], st["mx_w"][0], st["mx_w"][1], y=st["y"], workspace=st["ws_mx"])
+    ops.linear_w4a4(st["x"], st["packed_layer"], y=st["y_nv"], workspace=st["ws"])
+    torch.cuda.synchronize()
+    dist = float(torch.linalg.vector_norm((st["y"].float() - st["y_nv"].float())) /
+                 torch.linalg.vector_norm(st["y_nv"].float()))
+    print(f"[bench] MXFP4 layer {ms * 1e3:.1f} us ({tflops:.1f} TFLOP/s), its GEMM {gemm_ms * 1e3:.1f} us "
+          f"({gemm_tflops:.1f} TFLOP/s); NVFP4 layer {nv_ms * 1e3:.1f} us; normwise distance {dist:.4f}",
+          file=sys.stderr, flush=True)
+    result = {
+        "metric": f"MXFP4 variant of the SVDQuant linear, TFLOP/s at M={M},K={K},N={N}, 1 GPU (out of the "
+                  f"NVFP4 tolerance: a speed point)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {"workload": f"{desc}, both operands re-rounded to MXFP4 (E2M1, E8M0 per 32 K); "
+                               f"M={M} K={K} N={N} R={R}",
+                   "cache": "warm" if args.warm else f"cold (rotating {n_sets} sets)",
+                   "flop_per_step": flops_linear},
+        "roofline": {
+            "kernel": "gemm_mx_kernel (scaled FP4 matrix instruction + low-rank up-projection + epilogue)",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_FP4_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP4_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "flop_per_launch": flops_gemm,
+            "avg_launch_us": round(gemm_ms * 1e3, 2),
+        },
+        "nvfp4_layer_us": round(nv_ms * 1e3, 2),
+        "speedup_vs_nvfp4": round(nv_ms / ms, 3),
+        "normwise_distance_from_nvfp4": round(dist, 5),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on the variant layer", file=sys.stderr, flush=True)
+        from oracle import mx as Xo
+        from oracle import svdq as So
+        qw, wsc = So.quantize_weight(d["W"], d["wcscales"], d["wtscale"])
+        rows = 512
+        t0 = time.perf_counter()
+        Xo.linear_mxfp4(d["x"][:rows], d["smooth"], qw, wsc, d["wcscales"], d["wtscale"], d["proj_down"],
+                        d["proj_up"], d["bias"])
+        t = time.perf_counter() - t0
+        fl = 2 * rows * N * K + 2 * rows * R * (K + N)
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        result["cpu_baseline"] = {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                                  "sample": f"{rows} of the {M} rows ({t:.2f} s, including the weight re-round)"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload in MX_VARIANTS:
+        if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+            print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
+            sys.exit(2)
+        return run_mx(args)
     if args.workload in PREPS:
         if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
             print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
