@@ -28,11 +28,12 @@
 // multiple of 8; the padding workgroups exit at once.
 //
 // Epilogue: wcscales and bias load while the last panel multiplies;
-// accumulators * wtscale * wcscales[n]; then lora_act @ proj_up^T: the
-// operand fragments of up to 8 rank steps (both LDS stages, 144 KB) are copied
-// into LDS by direct global-to-LDS loads, one wait, and R/16 bf16 matrix
-// instructions per tile read them from there; then bias, then bf16 (RNE),
-// staged through LDS so the output leaves as coalesced 16-byte row pieces.
+// accumulators * wtscale * wcscales[n]; then lora_act @ proj_up^T as
+// ceil(R/64) further panels of the same two-stage pipeline (bf16 matrix
+// instructions; each residual panel is copied into its stage by direct
+// global-to-LDS loads while the panel before it multiplies); then bias, then
+// bf16 (RNE), staged through LDS so the output leaves as coalesced 16-byte
+// row pieces.
 #include "common.h"
 #include "kernels.h"
 
@@ -57,7 +58,6 @@ struct LdsCfg {
   static constexpr int kRest = kChunks - kFull * kWaves;         // waves 0..kRest-1 take one more
   static constexpr int kPerWave = kFull + (kRest ? 1 : 0);
   static constexpr int kStageBytes = kChunks * 4096;
-  static constexpr int kResSteps = (2 * kStageBytes) / (kChunks * 1024);   // R/16 steps per LDS residual pass
 };
 
 // GATED: the weight holds 2F output channels (a.N = 2F, a.gated_f = F); the
@@ -213,8 +213,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
     }
   }
   const uint32_t wt_raw = a.wtscale[0];
+
+  // The residual lora_act @ proj_up^T runs as ceil(R/64) more panels of the
+  // same pipeline: residual panel p (R steps 4p .. 4p+3) is copied by direct
+  // global-to-LDS loads into the stage the previous panel does not use, in
+  // the matrix-instruction operand order (chunk c, 16-R step t at
+  // c*4096 + t*1024, lane l at l*16), while that previous panel multiplies.
+  // Rows beyond M or N are clamped to the last row (their results are never
+  // stored).
+  const int R = (int)a.R;
+  const int r_steps = R / 16;
+  const int RP = (r_steps + 3) / 4;
+  const int m_wg = mp0 * 32;
+  auto res_dma = [&](uint8_t* stage, int p) {
+    const int S = min(4, r_steps - 4 * p);
+    for (int b = wave; b < C::kChunks * 4; b += C::kWaves) {
+      const int c = b >> 2, t = b & 3;
+      if (t >= S) continue;
+      const int col = 16 * (4 * p + t) + 8 * h;
+      const uint16_t* src;
+      if (c < C::kChunksA) {
+        const int m = min(m_wg + 32 * c + l32, M - 1);
+        src = a.lora_act + (size_t)m * R + col;
+      } else {
+        const int n = min(b_panel(c - C::kChunksA) * 32 + l32, N - 1);
+        src = a.proj_up + (size_t)n * R + col;
+      }
+      __builtin_amdgcn_global_load_lds(src, LDS_PTR(stage + c * 4096 + t * 1024), 16, 0, 0);
+    }
+  };
   {
     const uint8_t* cur = ((KP - 1) & 1) ? stage1 : stage0;
+    if (RP > 0) res_dma(((KP - 1) & 1) ? stage0 : stage1, 0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       auto mm = mma_step(cur, t);
@@ -237,49 +267,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] *= alpha[j];
 
-  const int R = (int)a.R;
-  const int r_steps = R / 16;
-  // Residual through LDS: per pass of up to kResSteps 16-wide R steps, every
-  // operand fragment (32 rows x 16 R of lora_act or proj_up) is copied by DMA
-  // into a 1 KB LDS block in the matrix-instruction operand order, then the
-  // waves multiply out of LDS. Rows beyond M or N are clamped to the last row.
-  {
-    const int m_wg = mp0 * 32;
-    for (int r0 = 0; r0 < r_steps; r0 += C::kResSteps) {
-      const int S = min(C::kResSteps, r_steps - r0);
-      const int blocks = C::kChunks * S;
-      __syncthreads();   // LDS free (main loop or the previous pass is done)
-      for (int b = wave; b < blocks; b += C::kWaves) {
-        const bool is_a = b < C::kChunksA * S;
-        const int bb = is_a ? b : b - C::kChunksA * S;
-        const int g = bb / S, rs = bb % S;
-        const int col = 16 * (r0 + rs) + 8 * h;
-        const uint16_t* src;
-        if (is_a) {
-          const int m = min(m_wg + 32 * g + l32, M - 1);
-          src = a.lora_act + (size_t)m * R + col;
-        } else {
-          const int n = min(b_panel(g) * 32 + l32, N - 1);
-          src = a.proj_up + (size_t)n * R + col;
-        }
-        __builtin_amdgcn_global_load_lds(src, LDS_PTR(smem + b * 1024), 16, 0, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-      __syncthreads();
-      for (int rs = 0; rs < S; ++rs) {
-        bf16x8 la[TM], pu[TN];
+  for (int p = 0; p < RP; ++p) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this panel's copies have landed
+    __syncthreads();                      // ... for every wave; the other stage is free
+    const uint8_t* cur = ((KP + p) & 1) ? stage1 : stage0;
+    if (p + 1 < RP) res_dma(((KP + p) & 1) ? stage0 : stage1, p + 1);
+    const int S = min(4, r_steps - 4 * p);
+    for (int t = 0; t < S; ++t) {
+      bf16x8 la[TM], pu[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          la[i] = *reinterpret_cast<const bf16x8*>(smem + ((wave_m * TM + i) * S + rs) * 1024 + lane * 16);
+      for (int i = 0; i < TM; ++i)
+        la[i] = *reinterpret_cast<const bf16x8*>(cur + (wave_m * TM + i) * 4096 + t * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        pu[j] = *reinterpret_cast<const bf16x8*>(cur + (C::kChunksA + wave_n * TN + j) * 4096 + t * 1024 + lane * 16);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          pu[j] = *reinterpret_cast<const bf16x8*>(smem + (C::kChunksA * S + (wave_n * TN + j) * S + rs) * 1024 + lane * 16);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], pu[j], acc[i][j], 0, 0, 0);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], pu[j], acc[i][j], 0, 0, 0);
     }
   }
 
