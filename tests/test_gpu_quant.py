@@ -161,6 +161,7 @@ def _unspecified_rows_mask(M, K):
     (77, 336, 32, "dit", 51),        # ragged M, K % 64 == 16
     (600, 3840, 128, "dit", 52),
     (96, 10240, 128, "swiglu", 53),
+    (130, 1024, 0, "dit", 54),       # quantisation alone into the packed layout
 ])
 def test_quant_packed_layout_bit_exact(gpu_lib, M, K, R, kind, seed):
     """Packed activation output == the oracle's codes/scales placed by the oracle's
@@ -236,3 +237,27 @@ def test_quant_packed_2048px_sampled_rows(gpu_lib):
     ref = S.lowrank_down(d["x"][rows], d["proj_down"])
     scale = np.abs(F.bf16_to_f64(d["x"][rows])) @ np.abs(F.bf16_to_f64(d["proj_down"]))
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + scale * K * 2.0 ** -23 + 1e-30)
+
+
+@pytest.mark.parametrize("M,K,R,kind,seed", [
+    (64, 256, 16, "tiny", 1001),
+    (77, 336, 32, "dit", 55),        # ragged M, K % 64 == 16
+    (4096, 3840, 128, "dit", 1003),  # the 1024^2 activation, K split over workgroups
+    (40, 10240, 256, "swiglu", 56),  # long K, two 128-wide R chunks
+])
+def test_quant_canonical_with_down_projection_bit_exact(gpu_lib, M, K, R, kind, seed):
+    """Canonical qact/ascales written by the fused quantisation + down-projection
+    kernel (R > 0) equal the oracle bit for bit; no byte past either output."""
+    d = workloads.make_linear(M, K, 16, R, kind=kind, seed=seed, with_bias=False)
+    qbuf = torch.full((M * (K // 2) + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full(((K // 16) * M + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    qact = qbuf[: M * (K // 2)].view(M, K // 2)
+    ascales = sbuf[: (K // 16) * M].view(K // 16, M)
+    gpu_lib.quantize_act(dev_bf16(d["x"]), dev_bf16(d["smooth"]), dev_bf16(d["proj_down"]),
+                         qact=qact, ascales=ascales)
+    torch.cuda.synchronize()
+    assert np.all(host_u8(qbuf[M * (K // 2):]) == 0xA5), "qact written past its end"
+    assert np.all(host_u8(sbuf[(K // 16) * M:]) == 0x5A), "ascales written past its end"
+    q_ref, s_ref = S.quantize_act(d["x"], d["smooth"])
+    assert np.array_equal(host_u8(ascales), s_ref)
+    assert np.array_equal(host_u8(qact), q_ref)
