@@ -289,23 +289,26 @@ __global__ __launch_bounds__(256) void lora_reduce_kernel(const float* __restric
 constexpr int kRowTiles = 1;
 constexpr int kRows = 16 * kRowTiles * kWaves;
 
-// K splits. A split multiplies the workgroups (512 fit on the chip at once,
-// two per CU) but adds fp32 partial sums to write and add back. Modelled time
-// rounds * steps_per_split * 0.67 us + splits * M * R * 8 B / (4 TB/s), fitted
-// to measurements at M = 4096 and 16896 (K = 3840 and 10240, R = 128);
-// the cheapest split count wins. Without R there are no partial sums.
+// K splits. A split multiplies the workgroups but adds fp32 partial sums to
+// write and add back. Modelled time: rounds * steps_per_split * 0.65 us +
+// splits * M * R * 1.26e-6 us, where a round is one workgroup per CU (256)
+// with the down-projection and two per CU without it. Fitted to a sweep of
+// 1 .. 16 splits at M = 4096 and 16896, K = 3840 and 10240, R = 128, which it
+// reproduces within about 5%; the cheapest split count wins. Without R there
+// are no partial sums.
 int k_splits(int64_t M, int64_t K, int64_t R, bool packed_out) {
   const int64_t row_blocks = (M + kRows - 1) / kRows;
   const int64_t steps = packed_out ? 2 * ((K + 63) / 64) : (K + 31) / 32;
+  const int64_t per_round = R > 0 ? 256 : 512;
   int best = 1;
   double best_cost = 0.0;
   for (int ks = 1; ks <= 16; ++ks) {
     if (ks > 1 && steps / ks < 4) break;
     if (R > 0 && ks > 1 && ks * M * R * 4 >= (int64_t(1) << 31)) break;   // 32-bit partial offsets
-    const int64_t rounds = (row_blocks * ks + 511) / 512;
+    const int64_t rounds = (row_blocks * ks + per_round - 1) / per_round;
     const int64_t per_split = (steps + ks - 1) / ks;
-    const double cost = (double)rounds * (double)per_split * 0.67 +
-                        (R > 0 && ks > 1 ? (double)ks * (double)M * (double)R * 2e-6 : 0.0);
+    const double cost = (double)rounds * (double)per_split * 0.65 +
+                        (R > 0 && ks > 1 ? (double)ks * (double)M * (double)R * 1.26e-6 : 0.0);
     if (ks == 1 || cost < best_cost) {
       best = ks;
       best_cost = cost;
