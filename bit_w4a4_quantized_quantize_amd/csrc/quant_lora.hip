@@ -4,6 +4,11 @@
 // section "What's stored on disk": the activation operand of scaled_mma and
 // the (x @ proj_down) factor of the SVD residual; raw x feeds the residual).
 //
+// Two kernels. With a down-projection, quant_lora_ws_kernel (below) splits each
+// workgroup's waves into quantisers and matrix waves. quant_lora_kernel serves
+// the quantisation alone (R = 0, packed output), the down-projection alone, and
+// the lora_act columns past the first 128.
+//
 // Work split. A workgroup of 8 waves owns 128 * RT rows: wave w owns rows
 // 16 * RT * w .. +16 * RT - 1 (RT row tiles of 16; RT = 1 is launched). K is
 // cut into 32-wide steps; a workgroup walks the steps of its K split
@@ -260,6 +265,248 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
   }
 }
 
+// Wave-specialised form of the same operation (quantisation and the first 128
+// lora_act columns together), used for R > 0. A workgroup owns 128 rows and walks
+// the 64-wide K panels of its split. Waves 0-3 quantise: quantiser wave q reads
+// rows 32 q .. 32 q + 31 of each panel with whole 128-byte row pieces (lane l:
+// row 8 i + l / 8 of load i, k piece l % 8, so one NVFP4 block sits in a lane
+// pair), quantises them, and copies them into LDS for the down-projection. Waves
+// 4-7 (wave 4 + q shares a SIMD with quantiser wave q and takes the same rows)
+// load proj_down, and multiply lora^T = proj_down^T x^T with
+// v_mfma_f32_32x32x16_bf16: the x operand is read from LDS in the instruction's
+// layout, proj_down is stored in its own row-major layout (16-byte piece p of
+// row k at piece p ^ 4 (k % 4)) and read by the transposing ds_read_tr16_b64.
+// Both operands are double-buffered per panel, one barrier per panel; the
+// quantisers prefetch x two panels ahead, so their VALU work overlaps the
+// down-projection's matrix instructions on the same SIMD.
+constexpr int kWsRows = 128;
+constexpr int kWsX = 16384;                  // x of one panel: 4 waves x 32 rows x 128 bytes
+constexpr int kWsStage = kWsX + 64 * 256;    // + proj_down of one panel (64 k x 128 r bf16)
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define WS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+template <bool PACKED>
+__global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kWsStage];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const bool quantiser = wave < 4;
+  const int qw = wave & 3;
+  const int M = a.M, K = a.K, R = a.R;
+  if ((int)blockIdx.x * kWsRows >= M) return;
+  const int KP = (K + 63) / 64;
+  const int MP = (M + 31) / 32;
+  const int m0 = blockIdx.x * kWsRows + 32 * qw;     // first row of this wave
+  const int ks = blockIdx.y;
+  const int p_begin = ks * a.split_steps;              // split_steps counts 64-wide panels here
+  const int n = min(KP, p_begin + a.split_steps) - p_begin;
+  const uint32_t code_bytes = (uint32_t)MP * KP * 1024;
+  const uint32_t x_bytes = (uint32_t)M * K * 2;
+  const uint32_t pd_bytes = (uint32_t)K * R * 2;
+  const uint32_t q_bytes = PACKED ? code_bytes + (uint32_t)MP * KP * 128 : (uint32_t)M * (K / 2);
+  const uint32_t s_bytes = PACKED ? 0u : (uint32_t)(K / 16) * M;
+  const auto rx = make_rsrc(a.x, x_bytes);
+  const auto rsm = make_rsrc(a.smooth, (uint32_t)K * 2);
+  const auto rpd = make_rsrc(a.proj_down, pd_bytes);
+  const auto rq = make_rsrc(a.qact, q_bytes);
+  const auto rsc = make_rsrc(a.ascales, s_bytes);
+
+  // ---- quantiser waves: lane's rows r_i = 8 i + lane / 8 (i = 0..3), k piece pc
+  const int pc = lane & 7;
+  const int rl = lane >> 3;
+  auto x_off = [&](int j, int i) -> uint32_t {      // panel j of the split (j may be >= n)
+    const int m = m0 + 8 * i + rl;
+    const int k = 64 * (p_begin + j) + 8 * pc;
+    return j < n && m < M && k < K ? ((uint32_t)m * K + k) * 2 : x_bytes;
+  };
+  // x in LDS for the down-projection: row r, piece p at r * 128 + (p ^ ((r / 2) % 8)) * 16
+  auto x_slot = [](int r, int p) { return r * 128 + ((p ^ ((r >> 1) & 7)) << 4); };
+
+  // ---- down-projection waves
+  f32x16 acc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[f][r] = 0.0f;
+  // proj_down piece e = 256 u + 64 q + lane (u = 0..3) of a panel: row k = e / 16,
+  // stored slot e % 16 = lane % 16, source piece (lane % 16) ^ 4 (k % 4)
+  const int pd_r = a.r_base + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)));
+  const uint32_t pd_lane = ((uint32_t)(lane >> 4) * R + pd_r) * 2;
+  auto pd_off = [&](int j, int u) -> uint32_t {
+    const int k0 = 64 * (p_begin + j) + 16 * u + 4 * qw;   // rows k0 .. k0 + 3 (lane / 16)
+    return j < n && k0 < K && pd_r < R ? (uint32_t)k0 * R * 2 + pd_lane : pd_bytes;
+  };
+  // transposing reads: source lane (16 grp + 4 jj + qq) points at row 8 (grp / 2) + 4 h + jj,
+  // columns 32 f + 16 (grp % 2) + 4 qq of the 16-k step
+  const int grp = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3;
+  const int tr_base = (8 * (grp >> 1) + jj) * 256 + (qq & 1) * 8 + (2 * (grp & 1) + (qq >> 1)) * 16;
+
+  u32x4 X0[5], X1[5], X2[5];      // quantisers: x of three panels (4 rows) and their smooth
+  u32x4 P0[4], P1[4], P2[4];      // down-projection: proj_down of three panels
+  auto load_x = [&](u32x4 (&X)[5], int j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off(j, i), 0, 0);
+    const int k = 64 * (p_begin + j) + 8 * pc;
+    X[4] = __builtin_amdgcn_raw_buffer_load_b128(rsm, j < n && k < K ? k * 2 : K * 2, 0, 0);
+  };
+  auto put_x = [&](const u32x4 (&X)[5], int b) {
+    uint8_t* base = smem + b * kWsStage + qw * 4096;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + x_slot(8 * i + rl, pc)) = X[i];
+  };
+  auto load_pd = [&](u32x4 (&P)[4], int j) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) P[u] = __builtin_amdgcn_raw_buffer_load_b128(rpd, pd_off(j, u), 0, 0);
+  };
+  auto put_pd = [&](const u32x4 (&P)[4], int b) {
+    uint8_t* base = smem + b * kWsStage + kWsX;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(base + (256 * u + 64 * qw + lane) * 16) = P[u];
+  };
+
+  // quantise panel j from X (all four rows of the lane), store codes and scales
+  auto quantise = [&](const u32x4 (&X)[5], int j) {
+    const int p = p_begin + j;
+    const int k = 64 * p + 8 * pc;
+    const u32x4 sv = X[4];
+    float sm[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sm[2 * e] = bf16lo_to_f32(sv[e]);
+      sm[2 * e + 1] = bf16hi_to_f32(sv[e]);
+    }
+    const int t = pc >> 1, h = pc & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + rl;
+      const int m = m0 + r;
+      float v[8];
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = bf16lo_to_f32(X[i][e]) * sm[2 * e];
+        v[2 * e + 1] = bf16hi_to_f32(X[i][e]) * sm[2 * e + 1];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));   // the other half of the block
+      const uint32_t sc = block_scale_code(amax);
+      const float sd = e4m3_to_f32(sc, 0);
+      const float inv = sd > 0.0f ? scale_reciprocal(sd) : 0.0f;
+      uint32_t pk = 0u;
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(v[0] * inv), snap21(v[1] * inv), 1.0f, 0);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(v[2] * inv), snap21(v[3] * inv), 1.0f, 1);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(v[4] * inv), snap21(v[5] * inv), 1.0f, 2);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(v[6] * inv), snap21(v[7] * inv), 1.0f, 3);
+      if (PACKED) {
+        // rows of the last 32-row panel beyond M are written (as zeros); a
+        // wave's rows past that panel are not stored at all
+        const int q = m0 >> 5;
+        const bool ok = j < n && q < MP;
+        const uint32_t chunk = (uint32_t)p * MP + q;
+        __builtin_amdgcn_raw_buffer_store_b32(pk, rq, ok ? chunk * 1024 + ((h * 32 + r) * 4 + t) * 4 : q_bytes, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rq, ok && h == 0 ? code_bytes + chunk * 128 + r * 4 + t : q_bytes,
+                                             0, 0);
+      } else {
+        const bool ok = j < n && m < M && k < K;
+        __builtin_amdgcn_raw_buffer_store_b32(pk, rq, ok ? (uint32_t)m * (K / 2) + k / 2 : q_bytes, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rsc, ok && h == 0 ? (uint32_t)(k >> 4) * M + m : s_bytes, 0, 0);
+      }
+    }
+  };
+
+  // down-projection of panel j out of buffer b
+  auto multiply = [&](int b) {
+    const uint8_t* xs = smem + b * kWsStage + qw * 4096;
+    const uint8_t* ps = smem + b * kWsStage + kWsX;
+    const int mr = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(xs + x_slot(mr, 2 * tt + hh));
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int off = tt * 4096 + tr_base + 64 * (f ^ jj);
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WS_LDS(v4s, ps + off));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WS_LDS(v4s, ps + off + 1024));
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, xb, acc[f], 0, 0, 0);
+      }
+    }
+  };
+
+  // panel j (buffer j % 2): the quantisers prefetch x two panels ahead, quantise
+  // panel j and copy panel j + 1 into the other buffer; the down-projection waves
+  // prefetch proj_down two panels ahead, multiply panel j and copy panel j + 1's
+  // proj_down into the other buffer. Three register sets per role, rotated by
+  // name; panels past the split read zeros and store nothing. The role is uniform
+  // per wave, so each role runs its own loop with one barrier per panel (the
+  // same count in both), and only that role's registers are live.
+  const int n_pad = (n + 2) / 3 * 3;
+  if (quantiser) {
+    auto qstep = [&](const u32x4 (&cur)[5], const u32x4 (&nxt)[5], u32x4 (&ahead)[5], int j) {
+      load_x(ahead, j + 2);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this panel's work
+      put_x(nxt, (j + 1) & 1);
+      quantise(cur, j);
+      __syncthreads();
+    };
+    load_x(X0, 0);
+    load_x(X1, 1);
+    put_x(X0, 0);
+    __syncthreads();
+    for (int j = 0; j < n_pad; j += 3) {
+      qstep(X0, X1, X2, j);
+      qstep(X1, X2, X0, j + 1);
+      qstep(X2, X0, X1, j + 2);
+    }
+    return;
+  }
+  auto lstep = [&](const u32x4 (&pnxt)[4], u32x4 (&pahead)[4], int j) {
+    load_pd(pahead, j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < n) multiply(j & 1);
+    put_pd(pnxt, (j + 1) & 1);
+    __syncthreads();
+  };
+  load_pd(P0, 0);
+  load_pd(P1, 1);
+  put_pd(P0, 0);
+  __syncthreads();
+  for (int j = 0; j < n_pad; j += 3) {
+    lstep(P1, P2, j);
+    lstep(P2, P0, j + 1);
+    lstep(P0, P1, j + 2);
+  }
+
+  {
+    // lane holds row m0 + lane % 32 and columns r_base + 32 f + 8 G + 4 (lane / 32) + e
+    const int m = m0 + (lane & 31);
+    const int hh = lane >> 5;
+    const uint32_t l_bytes = (uint32_t)M * R * 2;
+    const uint32_t p_bytes = a.partial != nullptr ? (uint32_t)gridDim.y * M * R * 4 : 0u;
+    const auto rl2 = make_rsrc(a.lora_act, l_bytes);
+    const auto rp = make_rsrc(a.partial, p_bytes);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        const int r = a.r_base + 32 * f + 8 * G + 4 * hh;
+        const bool ok = m < M && r < R;
+        if (a.partial == nullptr) {
+          const u32x2 o = {pack_bf16x2(acc[f][4 * G], acc[f][4 * G + 1]), pack_bf16x2(acc[f][4 * G + 2], acc[f][4 * G + 3])};
+          __builtin_amdgcn_raw_buffer_store_b64(o, rl2, ok ? ((uint32_t)m * R + r) * 2 : l_bytes, 0, 0);
+        } else {
+          const f32x4 o = {acc[f][4 * G], acc[f][4 * G + 1], acc[f][4 * G + 2], acc[f][4 * G + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rp,
+                                                 ok ? (((uint32_t)ks * M + m) * R + r) * 4 : p_bytes, 0, 0);
+        }
+      }
+  }
+}
+
 // lora_act = bf16(sum over the K splits of the fp32 partials), the splits
 // added in index order (deterministic). One thread per 8 consecutive columns.
 __global__ __launch_bounds__(256) void lora_reduce_kernel(const float* __restrict__ partial,
@@ -336,6 +583,16 @@ hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const ui
   a.partial = (R > 0 && ks > 1) ? partial : nullptr;
   dim3 grid((unsigned)((M + kRows - 1) / kRows), (unsigned)ks);
   auto launch = [&](bool quant, bool lora) {
+    if (quant && lora) {
+      // the wave-specialised kernel walks 64-wide panels; same splits and partial planes
+      QLArgs w = a;
+      const int64_t KP = (K + 63) / 64;
+      w.split_steps = (int)((KP + ks - 1) / ks);
+      const dim3 wgrid((unsigned)((M + kWsRows - 1) / kWsRows), (unsigned)ks);
+      if (packed_out) hipLaunchKernelGGL((quant_lora_ws_kernel<true>), wgrid, dim3(512), 0, stream, w);
+      else hipLaunchKernelGGL((quant_lora_ws_kernel<false>), wgrid, dim3(512), 0, stream, w);
+      return;
+    }
 #define SVDQ_QL(RT, P, Q, L) hipLaunchKernelGGL((quant_lora_kernel<RT, P, Q, L>), grid, dim3(64 * kWaves), 0, stream, a)
 #define SVDQ_QL_RT(RT)                                                                 \
     if (packed_out) {                                                                  \
