@@ -596,12 +596,10 @@ hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const ui
 #define SVDQ_QL(RT, P, Q, L) hipLaunchKernelGGL((quant_lora_kernel<RT, P, Q, L>), grid, dim3(64 * kWaves), 0, stream, a)
 #define SVDQ_QL_RT(RT)                                                                 \
     if (packed_out) {                                                                  \
-      if (quant && lora) SVDQ_QL(RT, true, true, true);                                \
-      else if (quant) SVDQ_QL(RT, true, true, false);                                  \
+      if (quant) SVDQ_QL(RT, true, true, false);                                       \
       else SVDQ_QL(RT, true, false, true);                                             \
     } else {                                                                           \
-      if (quant && lora) SVDQ_QL(RT, false, true, true);                               \
-      else if (quant) SVDQ_QL(RT, false, true, false);                                 \
+      if (quant) SVDQ_QL(RT, false, true, false);                                      \
       else SVDQ_QL(RT, false, false, true);                                            \
     }
     SVDQ_QL_RT(kRowTiles)
