@@ -392,7 +392,8 @@ __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1));   // the other half of the block
+      // the other half of the block sits in lane ^ 1 (a DPP lane swap, no LDS round trip)
+      amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, false)));
       const uint32_t sc = block_scale_code(amax);
       const float sd = e4m3_to_f32(sc, 0);
       const float inv = sd > 0.0f ? scale_reciprocal(sd) : 0.0f;
@@ -423,28 +424,35 @@ __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
     const uint8_t* xs = smem + b * kWsStage + qw * 4096;
     const uint8_t* ps = smem + b * kWsStage + kWsX;
     const int mr = lane & 31, hh = lane >> 5;
+    bf16x8 xb[4];
+    v4s lo[4][4], hi[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(xs + x_slot(mr, 2 * tt + hh));
+      xb[tt] = *reinterpret_cast<const bf16x8*>(xs + x_slot(mr, 2 * tt + hh));
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const int off = tt * 4096 + tr_base + 64 * (f ^ jj);
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WS_LDS(v4s, ps + off));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WS_LDS(v4s, ps + off + 1024));
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, xb, acc[f], 0, 0, 0);
+        lo[tt][f] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WS_LDS(v4s, ps + off));
+        hi[tt][f] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WS_LDS(v4s, ps + off + 1024));
       }
     }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[tt][f], hi[tt][f], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, xb[tt], acc[f], 0, 0, 0);
+      }
   };
 
   // panel j (buffer j % 2): the quantisers prefetch x two panels ahead, quantise
   // panel j and copy panel j + 1 into the other buffer; the down-projection waves
-  // prefetch proj_down two panels ahead, multiply panel j and copy panel j + 1's
-  // proj_down into the other buffer. Three register sets per role, rotated by
-  // name; panels past the split read zeros and store nothing. The role is uniform
-  // per wave, so each role runs its own loop with one barrier per panel (the
-  // same count in both), and only that role's registers are live.
-  const int n_pad = (n + 2) / 3 * 3;
+  // prefetch proj_down two panels ahead, multiply panel j (all of its LDS reads
+  // issued before its matrix instructions) and copy panel j + 1's proj_down into
+  // the other buffer. Three register sets per role, rotated by name; prefetches
+  // past the split read zeros. The role is uniform per wave, so each role runs its
+  // own loop with one barrier per panel (the same count, n + 1, in both), and only
+  // that role's registers are live.
   if (quantiser) {
     auto qstep = [&](const u32x4 (&cur)[5], const u32x4 (&nxt)[5], u32x4 (&ahead)[5], int j) {
       load_x(ahead, j + 2);
@@ -457,10 +465,10 @@ __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
     load_x(X1, 1);
     put_x(X0, 0);
     __syncthreads();
-    for (int j = 0; j < n_pad; j += 3) {
+    for (int j = 0; j < n; j += 3) {
       qstep(X0, X1, X2, j);
-      qstep(X1, X2, X0, j + 1);
-      qstep(X2, X0, X1, j + 2);
+      if (j + 1 < n) qstep(X1, X2, X0, j + 1);
+      if (j + 2 < n) qstep(X2, X0, X1, j + 2);
     }
     return;
   }
@@ -475,35 +483,69 @@ __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
   load_pd(P1, 1);
   put_pd(P0, 0);
   __syncthreads();
-  for (int j = 0; j < n_pad; j += 3) {
+  for (int j = 0; j < n; j += 3) {
     lstep(P1, P2, j);
-    lstep(P2, P0, j + 1);
-    lstep(P0, P1, j + 2);
+    if (j + 1 < n) lstep(P2, P0, j + 1);
+    if (j + 2 < n) lstep(P0, P1, j + 2);
   }
 
   {
-    // lane holds row m0 + lane % 32 and columns r_base + 32 f + 8 G + 4 (lane / 32) + e
-    const int m = m0 + (lane & 31);
-    const int hh = lane >> 5;
-    const uint32_t l_bytes = (uint32_t)M * R * 2;
-    const uint32_t p_bytes = a.partial != nullptr ? (uint32_t)gridDim.y * M * R * 4 : 0u;
-    const auto rl2 = make_rsrc(a.lora_act, l_bytes);
-    const auto rp = make_rsrc(a.partial, p_bytes);
+    // The accumulators go out through this wave's 16 KB of LDS (free after the last
+    // barrier), so that every store instruction writes whole rows. Lane holds row
+    // m0 + lane % 32 and columns r_base + 32 f + 8 G + 4 (lane / 32) + e; the staging area
+    // holds 32 rows of 128 fp32 columns, 16-byte slot s of row m at slot s ^ m (bank
+    // conflict free both ways).
+    float* st = reinterpret_cast<float*>(smem + qw * 16384);
+    const int ml = lane & 31, hh = lane >> 5;
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int G = 0; G < 4; ++G) {
-        const int r = a.r_base + 32 * f + 8 * G + 4 * hh;
-        const bool ok = m < M && r < R;
-        if (a.partial == nullptr) {
-          const u32x2 o = {pack_bf16x2(acc[f][4 * G], acc[f][4 * G + 1]), pack_bf16x2(acc[f][4 * G + 2], acc[f][4 * G + 3])};
-          __builtin_amdgcn_raw_buffer_store_b64(o, rl2, ok ? ((uint32_t)m * R + r) * 2 : l_bytes, 0, 0);
-        } else {
-          const f32x4 o = {acc[f][4 * G], acc[f][4 * G + 1], acc[f][4 * G + 2], acc[f][4 * G + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rp,
-                                                 ok ? (((uint32_t)ks * M + m) * R + r) * 4 : p_bytes, 0, 0);
-        }
+        const int s = 8 * f + 2 * G + hh;
+        *reinterpret_cast<f32x4*>(st + ml * 128 + ((s ^ ml) << 2)) =
+            f32x4{acc[f][4 * G], acc[f][4 * G + 1], acc[f][4 * G + 2], acc[f][4 * G + 3]};
       }
+    if (a.partial != nullptr) {
+      // fp32 partials: one instruction writes rows 2 i, 2 i + 1 (lane: 4 columns)
+      const uint32_t p_bytes = (uint32_t)gridDim.y * M * R * 4;
+      const auto rp = make_rsrc(a.partial, p_bytes);
+      const int c = lane & 31;
+      f32x4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = 2 * i + hh;
+        v[i] = *reinterpret_cast<const f32x4*>(st + rl * 128 + ((c ^ rl) << 2));
+      }
+      const int r = a.r_base + 4 * c;
+      const uint32_t base = (((uint32_t)ks * M + m0 + hh) * R + r) * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = m0 + 2 * i + hh < M && r < R;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[i]), rp,
+                                               ok ? base + (uint32_t)(2 * i * R * 4) : p_bytes, 0, 0);
+      }
+    } else {
+      // bf16 lora_act: one instruction writes rows 4 i .. 4 i + 3 (lane: 8 columns)
+      const uint32_t l_bytes = (uint32_t)M * R * 2;
+      const auto rl2 = make_rsrc(a.lora_act, l_bytes);
+      const int c8 = lane & 15;
+      u32x4 o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rl = 4 * i + (lane >> 4);
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + rl * 128 + (((2 * c8) ^ rl) << 2));
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + rl * 128 + (((2 * c8 + 1) ^ rl) << 2));
+        o[i] = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
+                     pack_bf16x2(v1[2], v1[3])};
+      }
+      const int r = a.r_base + 8 * c8;
+      const uint32_t base = ((uint32_t)(m0 + (lane >> 4)) * R + r) * 2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = m0 + 4 * i + (lane >> 4) < M && r < R;
+        __builtin_amdgcn_raw_buffer_store_b128(o[i], rl2, ok ? base + (uint32_t)(4 * i * R * 2) : l_bytes, 0, 0);
+      }
+    }
   }
 }
 
