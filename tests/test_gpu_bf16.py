@@ -100,3 +100,19 @@ def test_bf16_linear_empty(gpu_lib):
     w = torch.zeros((32, 64), dtype=torch.bfloat16, device="cuda")
     y = gpu_lib.linear_bf16(x, w)
     assert y.shape == (0, 32)
+
+
+def test_bf16_linear_rounding_bit_exact(gpu_lib):
+    """x and W of small dyadic values and biases of 256, 1024, -512 or 0: every fp32
+    partial sum is exact and many results sit on bf16 rounding ties, so the output must
+    equal the oracle's round-to-nearest-even of its float64 value bit for bit."""
+    rng = np.random.default_rng(4200)
+    M, K, N = 70, 208, 90
+    d = dict(M=M, K=K, N=N,
+             x=F.f64_to_bf16(rng.choice([0.0, 0.5, -1.0, 1.5, 2.0, -0.25], size=(M, K))),
+             W=F.f64_to_bf16(rng.choice([0.0, 1.0, -0.5, 0.75, -2.0], size=(N, K))),
+             bias=F.f64_to_bf16(rng.choice([256.0, 1024.0, -512.0, 0.0], size=N)))
+    y64, yb = S.linear_bf16(d["x"], d["W"], d["bias"])
+    ties = np.sum(np.abs(y64 / ulp_bf16(y64) % 1 - 0.5) < 1e-12)
+    assert ties > 50, ties
+    assert np.array_equal(run(gpu_lib, d), yb)

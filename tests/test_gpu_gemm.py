@@ -18,7 +18,7 @@ import torch
 import workloads
 from oracle import formats as F
 from oracle import svdq as S
-from tests.gpu_util import dev_bf16, dev_u8, host_bits, make_layer, within_ulps
+from tests.gpu_util import dev_bf16, dev_u8, host_bits, make_layer, ulp_bf16, within_ulps
 
 pytestmark = pytest.mark.gpu
 
@@ -154,3 +154,43 @@ def test_gemm_packed_full_ffn_shape_sampled_rows(gpu_lib):
     got = host_bits(y)[rows]
     assert S.normwise_rel_err(F.bf16_to_f64(got), y64) <= TOL
     assert within_ulps(got, y64, 1).mean() >= 0.999
+
+
+@pytest.mark.parametrize("R", [0, 16])
+@pytest.mark.parametrize("mode", ["canonical", "packed_weight", "packed_both"])
+def test_gemm_output_rounding_bit_exact(gpu_lib, R, mode):
+    """Operands chosen so that every fp32 quantity before the final bf16 cast is exact:
+    unit block scales, wcscales = wtscale = 1, a residual of small dyadic bf16 values, and
+    biases of 256, 1024, -512 or 0, so that y lands on many bf16 rounding ties (256 + an
+    odd integer, 1024 + 4 mod 8, ...). The only rounding left is the cast, so the output
+    must equal the oracle's round-to-nearest-even of its float64 value bit for bit."""
+    rng = np.random.default_rng(4100 + R)
+    M, K, N = 70, 64, 100
+    qact = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    qweight = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    one = F.e4m3_encode(np.array([1.0]))[0]
+    ascales = np.full((K // 16, M), one, dtype=np.uint8)
+    wscales = np.full((K // 16, N), one, dtype=np.uint8)
+    ones_n = F.f64_to_bf16(np.ones(N))
+    bias = F.f64_to_bf16(rng.choice([256.0, 1024.0, -512.0, 0.0], size=N))
+    lora = F.f64_to_bf16(rng.choice([0.0, 1.0, -1.0, 0.5, 2.0], size=(M, R))) if R else None
+    proj_up = F.f64_to_bf16(rng.choice([0.0, 1.0, -0.5, 2.0], size=(N, R))) if R else None
+    from bit_w4a4_quantized_quantize_amd import ops
+    layer = ops.SVDQLinearWeights(
+        N=N, K=K, weight=dev_u8(qweight), wscales=dev_u8(wscales), wcscales=dev_bf16(ones_n),
+        wtscale=dev_bf16(F.f64_to_bf16(np.ones(1))), smooth=dev_bf16(F.f64_to_bf16(np.ones(K))),
+        proj_down=dev_bf16(F.f64_to_bf16(np.zeros((K, R)))) if R else None,
+        proj_up=dev_bf16(proj_up) if R else None, bias=dev_bf16(bias))
+    if mode != "canonical":
+        layer = layer.packed()
+    if mode == "packed_both":      # the packed-activation kernel of the whole layer
+        from oracle import repack as P
+        y = gpu_lib.gemm_w4a4(dev_u8(P.repack(qact, ascales)), None, dev_bf16(lora) if R else None, layer, M=M)
+    else:
+        y = gpu_lib.gemm_w4a4(dev_u8(qact), dev_u8(ascales), dev_bf16(lora) if R else None, layer)
+    torch.cuda.synchronize()
+    y64 = S.gemm_w4a4(qact, ascales, F.bf16_to_f64(lora) if R else None, qweight, wscales, ones_n,
+                      F.f64_to_bf16(np.ones(1)), proj_up, bias)
+    ties = np.sum(np.abs(y64 / ulp_bf16(y64) % 1 - 0.5) < 1e-12)
+    assert ties > 50, ties          # the case really exercises ties
+    assert np.array_equal(host_bits(y), F.f64_to_bf16(y64))
