@@ -78,8 +78,8 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
-    // the other half of this 16-block sits in the neighbouring lane
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    // the other half of this 16-block sits in the neighbouring lane (a DPP lane swap)
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, false)));
 
     const uint32_t sc = block_scale_code(amax);
     const float sd = e4m3_to_f32(sc, 0);
