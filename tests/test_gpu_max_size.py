@@ -1,0 +1,68 @@
+"""GPU parity at the largest activation the library accepts: x of M = 279620 rows by
+K = 3840 (M K 2 bytes = 2^31 - 2048, just under the 2 GiB limit of the 32-bit buffer
+offsets; M is not a multiple of the 128-row blocks). The rows farthest into the buffers
+are where an offset overflow would show, so the sampled rows include the last ones.
+
+x is drawn on the device by torch's seeded generator (an input, not a result of these
+kernels); the sampled rows are copied back and the oracle evaluates them:
+- codes and scales of the canonical quantisation, bit for bit;
+- the whole layer (packed weights, R = 128, bias), normwise error <= 5e-3 and every
+  element within the arithmetic bound of the layer (as in test_gpu_linear.py).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import formats as F
+from oracle import svdq as S
+from tests.gpu_util import host_bits, host_u8, make_layer, ulp_bf16
+
+pytestmark = pytest.mark.gpu
+
+M_MAX, K, N, R = 279620, 3840, 200, 128
+
+
+def test_layer_at_the_largest_activation(gpu_lib):
+    assert M_MAX * K * 2 < 2 ** 31 <= (M_MAX + 1) * K * 2
+    d, layer = make_layer(dict(M=8, K=K, N=N, R=R, kind="dit", seed=77))   # weights, smooth, proj
+    layer = layer.packed()
+    g = torch.Generator(device="cuda").manual_seed(78)
+    x = torch.randn(M_MAX, K, dtype=torch.bfloat16, device="cuda", generator=g)
+    rows = np.concatenate([[0, 1, 127, 128], np.sort(np.random.default_rng(79).choice(M_MAX - 8, 24, replace=False)),
+                           np.arange(M_MAX - 6, M_MAX)])
+    x_rows = host_bits(x[torch.from_numpy(rows).cuda()])
+
+    qact, ascales, _ = gpu_lib.quantize_act(x, layer.smooth)
+    torch.cuda.synchronize()
+    q_ref, s_ref = S.quantize_act(x_rows, d["smooth"])
+    assert np.array_equal(host_u8(qact[torch.from_numpy(rows).cuda()]), q_ref)
+    assert np.array_equal(host_u8(ascales[:, torch.from_numpy(rows).cuda()]), s_ref)
+    del qact, ascales
+
+    y = gpu_lib.linear_w4a4(x, layer)
+    torch.cuda.synchronize()
+    got_bits = host_bits(y[torch.from_numpy(rows).cuda()])
+    y64, _, _, _ = S.linear_w4a4(x_rows, d["smooth"], d["qweight"], d["wscales"], d["wcscales"], d["wtscale"],
+                                 d["proj_down"], d["proj_up"], d["bias"])
+    got = F.bf16_to_f64(got_bits)
+    assert S.normwise_rel_err(got, y64) <= 5e-3
+    alpha = np.abs(F.bf16_to_f64(d["wtscale"])[0] * F.bf16_to_f64(d["wcscales"]))
+    main_abs = np.abs(S.dequant(q_ref, s_ref)) @ np.abs(S.dequant(d["qweight"], d["wscales"])).T * alpha
+    pu_abs = np.abs(F.bf16_to_f64(d["proj_up"])).T
+    lr_abs = np.abs(S.lowrank_down(x_rows, d["proj_down"])) @ pu_abs
+    lr_acc = (np.abs(F.bf16_to_f64(x_rows)) @ np.abs(F.bf16_to_f64(d["proj_down"]))) @ pu_abs
+    bound = (ulp_bf16(y64) + (K / 16 + 2) * 2.0 ** -24 * main_abs + 2.0 ** -8 * lr_abs
+             + (K + R + 2) * 2.0 ** -24 * lr_acc)
+    bad = np.argwhere(np.abs(got - y64) > bound)
+    assert bad.size == 0, f"{len(bad)} elements beyond the arithmetic bound, first {bad[:3].tolist()}"
+
+
+def test_one_row_more_is_rejected(gpu_lib):
+    """M + 1 rows put x past 2 GiB: the call is refused before any launch."""
+    from bit_w4a4_quantized_quantize_amd import _lib
+    x = torch.empty((M_MAX + 1) * K, dtype=torch.bfloat16, device="cuda")
+    d, layer = make_layer(dict(M=8, K=K, N=N, R=R, kind="dit", seed=77))
+    with pytest.raises(_lib.SvdqError):
+        gpu_lib.quantize_act(x.view(M_MAX + 1, K), layer.smooth)
