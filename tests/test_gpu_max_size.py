@@ -1,4 +1,4 @@
-"""GPU parity at the largest activation the library accepts: x of M = 279620 rows by
+"""GPU parity at the largest operands the library accepts. x of M = 279620 rows by
 K = 3840 (M K 2 bytes = 2^31 - 2048, just under the 2 GiB limit of the 32-bit buffer
 offsets; M is not a multiple of the 128-row blocks). The rows farthest into the buffers
 are where an offset overflow would show, so the sampled rows include the last ones.
@@ -66,3 +66,55 @@ def test_one_row_more_is_rejected(gpu_lib):
     d, layer = make_layer(dict(M=8, K=K, N=N, R=R, kind="dit", seed=77))
     with pytest.raises(_lib.SvdqError):
         gpu_lib.quantize_act(x.view(M_MAX + 1, K), layer.smooth)
+
+
+def test_gemm_at_the_largest_weight(gpu_lib):
+    """The largest N whose packed weight stays under 2 GiB at K = 10240 (N = 372,000 or so):
+    random codes and valid block scales drawn on the device, repacked by the library, then
+    the scaled GEMM + rank-16 residual + bias from the oracle's quantised activations, in both
+    activation layouts. Sampled columns include the last ones (the largest weight offsets)."""
+    from bit_w4a4_quantized_quantize_amd import _lib, ops
+    from oracle import repack as P
+    from tests.gpu_util import dev_bf16, dev_u8
+    L = _lib.lib()
+    Kw, Rw, Mw = 10240, 16, 64
+    lo, hi = 1, 1 << 22
+    while lo < hi:                       # largest N with a packed weight under 2 GiB
+        mid = (lo + hi + 1) // 2
+        lo, hi = (mid, hi) if L.svdq_repack_weight_bytes(mid, Kw) < 2 ** 31 else (lo, mid - 1)
+    Nw = lo
+    assert L.svdq_repack_weight_bytes(Nw + 1, Kw) >= 2 ** 31
+    g = torch.Generator(device="cuda").manual_seed(80)
+    qweight = torch.randint(0, 256, (Nw, Kw // 2), dtype=torch.uint8, device="cuda", generator=g)
+    wscales = torch.randint(0x28, 0x40, (Kw // 16, Nw), dtype=torch.uint8, device="cuda", generator=g)
+    rng = np.random.default_rng(81)
+    wcs_bits = F.f64_to_bf16(rng.uniform(0.5, 1.5, Nw) * 2.0 ** -6)
+    bias_bits = F.f64_to_bf16(rng.normal(0, 0.01, Nw))
+    pu_bits = F.f64_to_bf16(rng.normal(0, 0.02, (Nw, Rw)))
+    wt_bits = F.f64_to_bf16(np.ones(1))
+    layer = ops.SVDQLinearWeights(N=Nw, K=Kw, weight=qweight, wscales=wscales, wcscales=dev_bf16(wcs_bits),
+                                  wtscale=dev_bf16(wt_bits), smooth=dev_bf16(F.f64_to_bf16(np.ones(Kw))),
+                                  proj_down=dev_bf16(F.f64_to_bf16(np.zeros((Kw, Rw)))), proj_up=dev_bf16(pu_bits),
+                                  bias=dev_bf16(bias_bits))
+    cols = np.concatenate([[0, 1, 31, 32], np.sort(rng.choice(Nw - 8, 24, replace=False)), np.arange(Nw - 6, Nw)])
+    cidx = torch.from_numpy(cols).cuda()
+    qw_cols, ws_cols = host_u8(qweight[cidx]), host_u8(wscales[:, cidx])
+    packed = layer.packed()
+    del layer, qweight, wscales
+    d = workloads.make_linear(Mw, Kw, 8, Rw, kind="dit", seed=82, with_bias=False)
+    qact, ascales = S.quantize_act(d["x"], d["smooth"])
+    lora_bits = F.f64_to_bf16(rng.normal(0, 0.5, (Mw, Rw)))
+    y64 = S.gemm_w4a4(qact, ascales, F.bf16_to_f64(lora_bits), qw_cols, ws_cols, wcs_bits[cols], wt_bits,
+                      pu_bits[cols], bias_bits[cols])
+    for act in ("canonical", "packed"):
+        if act == "canonical":
+            y = gpu_lib.gemm_w4a4(dev_u8(qact), dev_u8(ascales), dev_bf16(lora_bits), packed)
+        else:
+            y = gpu_lib.gemm_w4a4(dev_u8(P.repack(qact, ascales)), None, dev_bf16(lora_bits), packed, M=Mw)
+        torch.cuda.synchronize()
+        got_bits = host_bits(y[:, cidx])
+        got = F.bf16_to_f64(got_bits)
+        assert S.normwise_rel_err(got, y64) <= 5e-3, act
+        frac = float(np.mean(np.abs(got - y64) <= ulp_bf16(y64) + 1e-30))
+        assert frac >= 0.999, (act, frac)
+        del y
