@@ -278,7 +278,9 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
 // row k at piece p ^ 4 (k % 4)) and read by the transposing ds_read_tr16_b64.
 // Both operands are double-buffered per panel, one barrier per panel; the
 // quantisers prefetch x two panels ahead, so their VALU work overlaps the
-// down-projection's matrix instructions on the same SIMD.
+// down-projection's matrix instructions on the same SIMD. The accumulators leave
+// through LDS so that every store writes whole rows of lora_act or of the fp32
+// partial sums.
 constexpr int kWsRows = 128;
 constexpr int kWsX = 16384;                  // x of one panel: 4 waves x 32 rows x 128 bytes
 constexpr int kWsStage = kWsX + 64 * 256;    // + proj_down of one panel (64 k x 128 r bf16)
