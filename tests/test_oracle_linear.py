@@ -221,3 +221,159 @@ def test_linear_swiglu_equals_gate_times_up_of_the_plain_layer():
     gate, up = y64[:, :24], y64[:, 24:]
     assert np.array_equal(h64, gate / (1.0 + np.exp(-gate)) * up)
     assert np.array_equal(h, F.f64_to_bf16(h64))
+
+
+# ---------------------------------------------------------------------------
+# gemm_w4a4: the layer from pre-quantised activations and a given lora_act
+# ---------------------------------------------------------------------------
+#
+# Pins of oracle.svdq.gemm_w4a4 (model card "nunchaku-z-image-turbo-svdq",
+# section "What's stored on disk", runtime formula without the quant step):
+#  * an exact-rational brute force of the formula, element by element, with the
+#    E2M1 grid and the e4m3fn closed form written out here;
+#  * bit-for-bit equality with the pinned whole layer when lora_act is the
+#    layer's own x @ proj_down (the two evaluate the same float64 products);
+#  * qweight = 0 gives lora_act @ proj_up^T + bias (torch float64 matmul).
+# Planted mistakes (the low-rank term dropped or scaled by the weight scales,
+# the bias dropped, wcscales applied per row) must fail the brute force.
+
+_GRID = [0, Fraction(1, 2), 1, Fraction(3, 2), 2, 3, 4, 6]
+
+
+def _e2m1_q(c):
+    return -_GRID[c & 7] if c & 8 else _GRID[c & 7]
+
+
+def _e4m3_q(b):
+    e, f = (b >> 3) & 15, b & 7
+    return Fraction(f, 512) if e == 0 else (1 + Fraction(f, 8)) * Fraction(2) ** (e - 7)
+
+
+def _bf16_q(bits):
+    """Exact value of a bf16 bit pattern (finite) as a Fraction."""
+    return Fraction(float(F.bf16_to_f64(np.array([bits], dtype=np.uint16))[0]))
+
+
+def _gemm_brute(qact, ascales, lora, qweight, wscales, wc_bits, wt_bits, pu_bits, bias_bits, m, n):
+    K = 2 * qact.shape[1]
+    main = Fraction(0)
+    for k in range(K):
+        ab, wb = int(qact[m, k // 2]), int(qweight[n, k // 2])
+        a = _e2m1_q(ab & 15 if k % 2 == 0 else ab >> 4) * _e4m3_q(int(ascales[k // 16, m]))
+        w = _e2m1_q(wb & 15 if k % 2 == 0 else wb >> 4) * _e4m3_q(int(wscales[k // 16, n]))
+        main += a * w
+    y = main * _bf16_q(int(wt_bits[0])) * _bf16_q(int(wc_bits[n]))
+    if lora is not None:
+        for r in range(lora.shape[1]):
+            y += Fraction(float(lora[m, r])) * _bf16_q(int(pu_bits[n, r]))
+    if bias_bits is not None:
+        y += _bf16_q(int(bias_bits[n]))
+    return y
+
+
+def _gemm_case(seed=11, **over):
+    d = _tiny(seed=seed, **over)
+    d["wtscale"] = F.f64_to_bf16(np.array([0.625]))   # any global alpha: the inputs are arbitrary here
+    qact, ascales = S.quantize_act(d["x"], d["smooth"])
+    lora = S.lowrank_down(d["x"], d["proj_down"]) if d["R"] > 0 else None
+    return d, qact, ascales, lora
+
+
+def _gemm_pin_error(gemm_fn, d, qact, ascales, lora, points):
+    """Largest |gemm_fn - brute force| / scale over the sampled points, where scale is
+    the sum of the magnitudes of the formula's terms (so float64 rounding is ~1e-16)."""
+    y = gemm_fn(qact, ascales, lora, d["qweight"], d["wscales"], d["wcscales"], d["wtscale"],
+                d["proj_up"], d["bias"])
+    worst = 0.0
+    for m, n in points:
+        exact = _gemm_brute(qact, ascales, lora, d["qweight"], d["wscales"], d["wcscales"], d["wtscale"],
+                            d["proj_up"], d["bias"], m, n)
+        mag = abs(float(exact)) + 1e-3
+        worst = max(worst, abs(float(Fraction(float(y[m, n])) - exact)) / mag)
+    return worst
+
+
+_POINTS = [(0, 0), (5, 17), (63, 127), (31, 64), (10, 99), (47, 3)]
+
+
+def test_gemm_w4a4_rational_brute_force():
+    case = _gemm_case()
+    assert _gemm_pin_error(S.gemm_w4a4, *case, _POINTS) < 1e-13
+
+
+def test_gemm_w4a4_rational_brute_force_dit_rows():
+    """DiT-shaped inputs (outlier channels, normal-range weight scales, R = 32)."""
+    d = workloads.make_linear(M=8, K=256, N=24, R=32, kind="dit", seed=1003)
+    d["qweight"], d["wscales"] = S.quantize_weight(d["W"], d["wcscales"], d["wtscale"])
+    qact, ascales = S.quantize_act(d["x"], d["smooth"])
+    lora = S.lowrank_down(d["x"], d["proj_down"])
+    pts = [(0, 0), (7, 23), (3, 11), (5, 2)]
+    assert _gemm_pin_error(S.gemm_w4a4, d, qact, ascales, lora, pts) < 1e-13
+
+
+def test_gemm_w4a4_equals_whole_layer_bitwise():
+    for d in (_tiny(seed=12),
+              workloads.make_linear(M=32, K=512, N=48, R=32, kind="dit", seed=1003)):
+        if "qweight" not in d:
+            d["qweight"], d["wscales"] = S.quantize_weight(d["W"], d["wcscales"], d["wtscale"])
+        y64, _, qact, ascales = S.linear_w4a4(d["x"], d["smooth"], d["qweight"], d["wscales"], d["wcscales"],
+                                              d["wtscale"], d["proj_down"], d["proj_up"], d["bias"])
+        lora = S.lowrank_down(d["x"], d["proj_down"])
+        y = S.gemm_w4a4(qact, ascales, lora, d["qweight"], d["wscales"], d["wcscales"], d["wtscale"],
+                        d["proj_up"], d["bias"])
+        assert np.array_equal(y, y64)
+
+
+def test_gemm_w4a4_zero_weight_is_lowrank_plus_bias():
+    d, qact, ascales, lora = _gemm_case(seed=13)
+    y = S.gemm_w4a4(qact, ascales, lora, np.zeros_like(d["qweight"]), d["wscales"], d["wcscales"],
+                    d["wtscale"], d["proj_up"], d["bias"])
+    ref = torch.from_numpy(lora) @ torch.from_numpy(F.bf16_to_f64(d["proj_up"])).T + \
+        torch.from_numpy(F.bf16_to_f64(d["bias"]))
+    assert np.allclose(y, ref.numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_gemm_w4a4_r0_and_no_bias():
+    d, qact, ascales, _ = _gemm_case(seed=14, R=0)
+    d["bias"] = None
+    y = S.gemm_w4a4(qact, ascales, None, d["qweight"], d["wscales"], d["wcscales"], d["wtscale"],
+                    None, None)
+    A = S.dequant(qact, ascales)
+    W = S.dequant(d["qweight"], d["wscales"])
+    alpha = F.bf16_to_f64(d["wtscale"])[0] * F.bf16_to_f64(d["wcscales"])
+    assert np.allclose(y, (A @ W.T) * alpha[None, :], rtol=1e-13, atol=0)
+    assert _gemm_pin_error(S.gemm_w4a4, d, qact, ascales, None, _POINTS) < 1e-13
+
+
+def _mut_drop_lowrank(qact, ascales, lora, *rest):
+    return S.gemm_w4a4(qact, ascales, None, *rest)
+
+
+def _mut_scale_lowrank(qact, ascales, lora, qweight, wscales, wc, wt, pu, bias):
+    main = S.main_term(qact, ascales, qweight, wscales)
+    lr = np.asarray(lora) @ F.bf16_to_f64(pu).T
+    return S.epilogue(main + lr, wc, wt, None, bias)
+
+
+def _mut_drop_bias(qact, ascales, lora, qweight, wscales, wc, wt, pu, bias):
+    return S.gemm_w4a4(qact, ascales, lora, qweight, wscales, wc, wt, pu, None)
+
+
+def _mut_row_scales(qact, ascales, lora, qweight, wscales, wc, wt, pu, bias):
+    # wcscales applied along the wrong axis (rows instead of output channels)
+    main = S.main_term(qact, ascales, qweight, wscales)
+    M = main.shape[0]
+    wcm = F.bf16_to_f64(wc)[:M]
+    y = main * F.bf16_to_f64(wt)[0] * wcm[:, None]
+    return y + np.asarray(lora) @ F.bf16_to_f64(pu).T + F.bf16_to_f64(bias)[None, :]
+
+
+def _mut_drop_wtscale(qact, ascales, lora, qweight, wscales, wc, wt, pu, bias):
+    return S.gemm_w4a4(qact, ascales, lora, qweight, wscales, wc, F.f64_to_bf16(np.array([1.0])), pu, bias)
+
+
+@pytest.mark.parametrize("mutant", [_mut_drop_lowrank, _mut_scale_lowrank, _mut_drop_bias, _mut_row_scales,
+                                    _mut_drop_wtscale])
+def test_gemm_pin_catches_planted_mistakes(mutant):
+    case = _gemm_case()
+    assert _gemm_pin_error(mutant, *case, _POINTS) > 1e-6
