@@ -77,6 +77,41 @@ PEAK_FP4_MFMA_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak
 MX_VARIANTS = {"ffn_w1_1024_mxfp4": "ffn_w1_1024", "qkv_1024_mxfp4": "qkv_1024", "ffn_w2_1024_mxfp4": "ffn_w2_1024"}
 
 
+# roofline calibration of this device (no layer): sustained f16 MFMA and device copy
+CALIBS = {"calib": "sustained v_mfma_f32_32x32x16_f16 (8 waves per CU, the GEMM's occupancy and accumulator "
+                   "footprint) on exact NVFP4 values, random f16 bits and zeros, with the shader clock read by "
+                   "the kernel; streaming device copy of 1 GiB (HBM) and 64 MiB (cache resident)"}
+
+
+def run_calib(args):
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    res = calibration(dev, stream)
+    for k, v in res.items():
+        print(f"[bench] {k}: {v}", file=sys.stderr, flush=True)
+    m = res["mfma_f16_32x32x16"]
+    result = {
+        "metric": "MI355X roofline calibration: sustained f16 MFMA TFLOP/s on exact NVFP4 operand values, 1 GPU",
+        "value": m["nvfp4_values"]["TFLOPs"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": 1,
+        "warmup": 0,
+        "ms_per_step": m["nvfp4_values"]["ms_per_launch"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": CALIBS["calib"]},
+        "published_peaks": {"f16_mfma_TFLOPs": PEAK_F16_MFMA_TFLOPS, "hbm_GBps": PEAK_HBM_GBS},
+        "calibration": res,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def workload_cfg(name):
     import workloads
     ref, desc = WORKLOADS[name]
@@ -87,7 +122,8 @@ def workload_cfg(name):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--workload",
-                   choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS) + sorted(SWEEPS) + sorted(PREPS) + sorted(MX_VARIANTS),
+                   choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS) + sorted(SWEEPS) + sorted(PREPS) + sorted(MX_VARIANTS)
+                   + sorted(CALIBS),
                    default=DEFAULT_WORKLOAD,
                    help="layer shape (the default is the headline workload; the rest are for comparison)")
     p.add_argument("--gpus", type=int, default=1)
@@ -102,6 +138,9 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="sweep: time eager launches only")
     p.add_argument("--copy-calibration", action="store_true",
                    help="finish with a plain 512 MiB device copy (to calibrate HBM byte counters)")
+    p.add_argument("--condition-ms", type=float, default=30.0,
+                   help="minimum untimed device work before timing; conditioning also waits until "
+                        "consecutive ~2 ms windows agree within 2%%")
     return p.parse_args()
 
 
@@ -180,12 +219,66 @@ def make_sets(cfg, n_sets, layout, dev):
     return d, sets
 
 
-def time_loop(fn, n_sets, iters, warmup, stream):
-    """Average ms per call of fn(set_index) on `stream`, HIP events around the loop."""
+def condition(fn, n_sets, stream, min_ms=30.0, window_ms=2.0, tol=0.02, max_ms=3000.0):
+    """Run fn(set_index) untimed until at least min_ms of device work has run and two
+    consecutive windows of about window_ms agree within tol: under sustained matrix work the
+    chip settles its clock over some milliseconds, so a fixed number of warm-up calls
+    conditions it differently for different call lengths. The device never idles between
+    windows (the host waits for a window only after queueing the next one); the last
+    window is still running when this returns. Returns (conditioning_ms, calls, window
+    times in ms per call)."""
     import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    a, b = ev(), ev()
+    a.record(stream)
+    fn(0)
+    b.record(stream)
+    b.synchronize()
+    est = max(a.elapsed_time(b), 1e-3)
+    per = max(1, int(round(window_ms / est)))
+    calls = 1
+    total = est
+
+    def enqueue():
+        nonlocal calls
+        s, e = ev(), ev()
+        s.record(stream)
+        for _ in range(per):
+            fn(calls % n_sets)
+            calls += 1
+        e.record(stream)
+        return s, e
+
+    times = []
+    pending = enqueue()
+    while True:
+        nxt = enqueue()
+        pending[1].synchronize()
+        t = pending[0].elapsed_time(pending[1]) / per
+        times.append(t)
+        total += t * per
+        pending = nxt
+        settled = len(times) >= 2 and abs(times[-1] - times[-2]) <= tol * times[-2]
+        if (total >= min_ms and settled) or total >= max_ms:
+            break
+    total += times[-1] * per    # the window still in flight
+    return total, calls, times
+
+
+def timed(fn, n_sets, iters, stream, warmup=0, min_ms=30.0):
+    """Average ms per call of fn(set_index) over `iters` calls on `stream`: conditioning by
+    time, `warmup` more untimed calls, a host synchronisation, about 1 ms of untimed calls
+    queued ahead of the start event (so the timed calls start on a busy device), then HIP
+    events around exactly `iters` calls. Returns (ms per call, info)."""
+    import torch
+    cond_ms, cond_calls, windows = condition(fn, n_sets, stream, min_ms=min_ms)
     for i in range(warmup):
         fn(i % n_sets)
     torch.cuda.synchronize()
+    per_call = windows[-1]
+    prime = max(1, int(round(1.0 / max(per_call, 1e-3))))
+    for i in range(prime):
+        fn(i % n_sets)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -193,7 +286,103 @@ def time_loop(fn, n_sets, iters, warmup, stream):
         fn(i % n_sets)
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / iters
+    info = {"conditioning_ms": round(cond_ms + prime * per_call, 2), "conditioning_calls": cond_calls + prime,
+            "conditioning_windows_us": [round(t * 1e3, 1) for t in windows[-4:]]}
+    return start.elapsed_time(end) / iters, info
+
+
+def time_loop(fn, n_sets, iters, warmup, stream):
+    """Average ms per call of fn(set_index) on `stream` (conditioned by time; see timed)."""
+    return timed(fn, n_sets, iters, stream, warmup=warmup, min_ms=10.0)[0]
+
+
+# ---- roofline calibration (measurement helpers in the library) ----
+
+def calib_tables(dev):
+    """Operand tables for the sustained-MFMA kernel: f16 values with random bits (sign,
+    exponents 2^-4..2^3, all 10 mantissa bits), exact NVFP4 values (E2M1 code times an
+    e4m3 block scale, as the GEMM multiplies them), and zeros."""
+    import torch
+    from bit_w4a4_quantized_quantize_amd import _lib
+    n = _lib.lib().svdq_calib_table_bytes() // 2
+    g = torch.Generator(device="cpu").manual_seed(2024)
+    sign = torch.randint(0, 2, (n,), generator=g) * 2 - 1
+    expo = torch.randint(-4, 4, (n,), generator=g).double()
+    mant = 1.0 + torch.randint(0, 1024, (n,), generator=g).double() / 1024.0
+    rnd = (sign * mant * torch.pow(2.0, expo)).to(torch.float16)
+    grid = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=torch.float64)
+    code = torch.randint(0, 16, (n,), generator=g)
+    e2m1 = torch.where(code >= 8, -grid[code % 8], grid[code % 8])
+    # e4m3 scales of a typical block: exponent 2^-3..2^2, any 3-bit mantissa
+    sc = (1.0 + torch.randint(0, 8, (n // 16,), generator=g).double() / 8.0) * \
+        torch.pow(2.0, torch.randint(-3, 3, (n // 16,), generator=g).double())
+    nv = (e2m1 * sc.repeat_interleave(16)).to(torch.float16)
+    return {"random_f16": rnd.to(dev), "nvfp4_values": nv.to(dev), "zeros": torch.zeros(n, dtype=torch.float16,
+                                                                                         device=dev)}
+
+
+def calib_mfma(table, dev, stream, target_ms=20.0, workgroups=256):
+    """Sustained f16 MFMA rate on `table`, conditioned by time; returns TFLOP/s and the
+    median shader clock (GHz) from the kernel's own counters."""
+    import torch
+    from bit_w4a4_quantized_quantize_amd import _lib
+    L = _lib.lib()
+    out = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(workgroups * 4, dtype=torch.int64, device=dev)
+    per_iter = L.svdq_calib_flop_per_iteration(workgroups)
+
+    def launch(iters):
+        _lib.check("svdq_calib_mfma", L.svdq_calib_mfma(table.data_ptr(), table.numel() * 2, iters, workgroups,
+                                                        out.data_ptr(), out.numel() * 4, clocks.data_ptr(),
+                                                        clocks.numel() * 8, stream.cuda_stream))
+
+    iters = max(1, int(2.0 * 1.6e15 * 1e-3 / per_iter))     # about 2 ms per launch
+    ms, info = timed(lambda i: launch(iters), 1, max(1, int(target_ms / 2.0)), stream, min_ms=30.0)
+    tflops = iters * per_iter / (ms * 1e-3) / 1e12
+    launch(iters)
+    torch.cuda.synchronize()
+    khz = ctypes_int()
+    _lib.check("svdq_calib_wall_clock_khz", L.svdq_calib_wall_clock_khz(khz))
+    c = clocks.view(workgroups, 4).cpu().double()
+    ghz = ((c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2]) * khz.value * 1e3 / 1e9).median().item()
+    return {"TFLOPs": round(tflops, 1), "shader_clock_GHz": round(ghz, 3), "ms_per_launch": round(ms, 4),
+            "flop_per_launch": iters * per_iter, "workgroups": workgroups, "wall_clock_kHz": khz.value}
+
+
+def ctypes_int():
+    import ctypes
+    return ctypes.c_int(0)
+
+
+def calib_copy(dev, stream, nbytes, reps=10):
+    """Device-copy rate (bytes read + written per second) of a streaming copy kernel."""
+    import torch
+    from bit_w4a4_quantized_quantize_amd import _lib
+    L = _lib.lib()
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.random_(0, 256)
+    dst = torch.empty_like(src)
+
+    def f(i):
+        _lib.check("svdq_calib_copy", L.svdq_calib_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream.cuda_stream))
+
+    ms, _ = timed(f, 1, reps, stream, min_ms=10.0)
+    del src, dst
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1), round(ms * 1e3, 2)
+
+
+def calibration(dev, stream, quick=False):
+    """Sustained f16 MFMA rates and device-copy rates on this device."""
+    tables = calib_tables(dev)
+    res = {"mfma_f16_32x32x16": {}}
+    for name in (("nvfp4_values", "random_f16") if quick else ("nvfp4_values", "random_f16", "zeros")):
+        res["mfma_f16_32x32x16"][name] = calib_mfma(tables[name], dev, stream)
+    gbs, us = calib_copy(dev, stream, 1 << 30)
+    res["copy_1GiB"] = {"GBps": gbs, "us": us}
+    if not quick:
+        gbs, us = calib_copy(dev, stream, 64 << 20, reps=50)
+        res["copy_64MiB_cache_resident"] = {"GBps": gbs, "us": us}
+    return res
 
 
 def cpu_baseline(d, cfg, repeats=2):
@@ -279,22 +468,12 @@ def run_ffn_block(args):
         ops.linear_w4a4_gated(a["x"], a["layer"], h=hs[i], workspace=a["ws"])
         ops.linear_w4a4(hs[i], b["layer"], y=b["y"], workspace=b["ws"])
 
-    for i in range(args.warmup):
-        step(i % n_sets)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(i % n_sets)
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step, cond = timed(step, n_sets, args.steps, stream, warmup=args.warmup, min_ms=args.condition_ms)
     wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
     tflops = flops_block / (ms_per_step * 1e-3) / 1e12
     print(f"[bench] FFN block: {ms_per_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s "
-          f"(wall {wall * 1e6 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
+          f"(conditioned {cond['conditioning_ms']:.1f} ms; wall {wall:.2f} s)", file=sys.stderr, flush=True)
 
     # per-kernel: the gated GEMM alone (packed activations, as inside the block)
     for i in range(n_sets):
@@ -522,22 +701,12 @@ def run_sweep(args):
         else:
             forward(i % n_fwd)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step, cond = timed(step, n_fwd, args.steps, stream, warmup=args.warmup, min_ms=args.condition_ms)
     wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
     tflops = flops_fwd / (ms_per_step * 1e-3) / 1e12
     print(f"[bench] sweep ({'graph' if graphs else 'eager'}): {ms_per_step:.2f} ms per forward, {tflops:.1f} TFLOP/s "
-          f"(wall {wall * 1e3 / args.steps:.2f} ms)", file=sys.stderr, flush=True)
+          f"(wall {wall:.2f} s)", file=sys.stderr, flush=True)
 
     # split: the bf16 layers alone and the W4A4 layers alone (eager), and eager whole forwards
     def timed(fn, n):
@@ -778,17 +947,7 @@ def run_mx(args):
         st = sets[i]
         ops.linear_mxfp4(st["x"], st["layer"], st["mx_w"][0], st["mx_w"][1], y=st["y"], workspace=st["ws_mx"])
 
-    for i in range(args.warmup):
-        step(i % n_sets)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(i % n_sets)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, cond = timed(step, n_sets, args.steps, stream, warmup=args.warmup, min_ms=args.condition_ms)
     tflops = flops_linear / (ms * 1e-3) / 1e12
     kw = max(1, args.warmup // 2)
     for st in sets:
@@ -867,6 +1026,11 @@ def run_mx(args):
 
 def main():
     args = parse()
+    if args.workload in CALIBS:
+        if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+            print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
+            sys.exit(2)
+        return run_calib(args)
     if args.workload in MX_VARIANTS:
         if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
             print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
@@ -918,22 +1082,17 @@ def main():
         ops.linear_w4a4(s["x"], s["layer"], y=s["y"], workspace=s["ws"])
 
     # ---- headline: exactly K steps, synchronised on both sides ----
-    for i in range(args.warmup):
-        step(i % n_sets)
-    torch.cuda.synchronize()
+    # The chip is conditioned by time first (its clock settles over some milliseconds
+    # of matrix work), then the W warm-up steps run, then the host synchronises; about
+    # 1 ms of untimed steps is queued ahead of the start event so the timed steps begin
+    # on a busy device rather than after the host's launch latency.
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(i % n_sets)
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step, cond = timed(step, n_sets, args.steps, stream, warmup=args.warmup, min_ms=args.condition_ms)
     wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
     tflops = flops_linear / (ms_per_step * 1e-3) / 1e12
     print(f"[bench] linear: {ms_per_step * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s "
-          f"(wall {wall * 1e6 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
+          f"(conditioned {cond['conditioning_ms']:.1f} ms over {cond['conditioning_calls']} calls; "
+          f"last windows {cond['conditioning_windows_us']} us/step; wall {wall:.2f} s)", file=sys.stderr, flush=True)
 
     # ---- per-kernel timings, same stream and rotation, the kernels the step runs ----
     packed = args.layout == "packed"
@@ -968,9 +1127,17 @@ def main():
     qd_ms = time_loop(quant_down, n_sets, args.kernel_iters, kw, stream)
     gemm_tflops = flops_gemm / (gemm_ms * 1e-3) / 1e12
     quant_bytes_a1 = M * K * 2 + K * 2 + M * K // 2 + (K // 16) * M
+    quant_bytes_fused = quant_bytes_a1 + 2 * K * R + 2 * M * R
     quant_gbs = quant_bytes_a1 / (quant_ms * 1e-3) / 1e9
     print(f"[bench] gemm kernel {gemm_ms * 1e3:.1f} us ({gemm_tflops:.1f} TFLOP/s), quant {quant_ms * 1e3:.2f} us "
           f"({quant_gbs:.0f} GB/s), quant+down {qd_ms * 1e3:.2f} us", file=sys.stderr, flush=True)
+
+    # practical ceilings on this device, measured now: sustained f16 MFMA on exact NVFP4
+    # operand values and on random f16 bits, and a streaming device copy
+    calib = calibration(dev, stream, quick=True)
+    practical = calib["mfma_f16_32x32x16"]["nvfp4_values"]["TFLOPs"]
+    copy_gbs = calib["copy_1GiB"]["GBps"]
+    print(f"[bench] calibration: {calib}", file=sys.stderr, flush=True)
 
     # the committed counters were taken on the packed-path GEMM at the headline workload
     traffic = read_traffic() if packed and args.workload == DEFAULT_WORKLOAD else None
@@ -1009,21 +1176,35 @@ def main():
             "traffic": traffic,
             "flop_per_launch": flops_gemm,
             "avg_launch_us": round(gemm_ms * 1e3, 2),
+            "practical_peak": practical,
+            "frac_of_practical": round(gemm_tflops / practical, 4),
+            "practical_peak_note": "sustained v_mfma_f32_32x32x16_f16 at the GEMM's occupancy on exact NVFP4 "
+                                   "operand values, measured in this run (the chip power-limits its clock "
+                                   "under sustained matrix work)",
         },
         "quant_kernel": {
             "avg_launch_us": round(quant_ms * 1e3, 3),
             "hbm_bytes_per_launch": quant_bytes_a1,
             "achieved_GBps": round(quant_gbs, 1),
             "frac_of_hbm_peak": round(quant_gbs / PEAK_HBM_GBS, 4),
+            "practical_copy_GBps": copy_gbs,
+            "frac_of_practical_copy": round(quant_gbs / copy_gbs, 4),
             "kernel": "quant_act_kernel (activation quantisation alone, canonical output)",
             "fused_with_down_projection_us": round(qd_ms * 1e3, 3),
+            "fused_hbm_bytes_per_launch": quant_bytes_fused,
+            "fused_achieved_GBps": round(quant_bytes_fused / (qd_ms * 1e-3) / 1e9, 1),
         },
+        "conditioning": cond,
+        "calibration": calib,
     }
     if args.copy_calibration:
+        # a plain 512 MiB streaming copy, to calibrate the profiler's HBM byte counters
+        L = ops._lib.lib()
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            ops._lib.check("svdq_calib_copy", L.svdq_calib_copy(src.data_ptr(), dst.data_ptr(), src.numel(),
+                                                                stream.cuda_stream))
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu_baseline:

@@ -20,6 +20,7 @@ SIGNATURES = {
     "svdq_abi_version": (_int, []),
     "svdq_status_string": (ctypes.c_char_p, [_int]),
     "svdq_last_error": (ctypes.c_char_p, []),
+    "svdq_debug_mode": (_int, []),
     "svdq_quantize_act_workspace_bytes": (_size, [_i64, _i64, _i64]),
     "svdq_packed_act_bytes": (_size, [_i64, _i64]),
     "svdq_quantize_act": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64, _int,
@@ -57,6 +58,11 @@ SIGNATURES = {
     "svdq_linear_mxfp4": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, _size,
                                  _c_void_p]),
+    "svdq_calib_table_bytes": (_size, []),
+    "svdq_calib_flop_per_iteration": (_i64, [_i64]),
+    "svdq_calib_mfma": (_int, [_c_void_p, _size, _i64, _i64, _c_void_p, _size, _c_void_p, _size, _c_void_p]),
+    "svdq_calib_copy": (_int, [_c_void_p, _c_void_p, _size, _c_void_p]),
+    "svdq_calib_wall_clock_khz": (_int, [ctypes.POINTER(_int)]),
 }
 
 STATUS = {

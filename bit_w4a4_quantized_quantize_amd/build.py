@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libsvdq.so")
 
 SOURCES = ["api.hip", "quant_act.hip", "quant_lora.hip", "gemm_w4a4.hip", "gemm_lds.hip", "gemm_bf16.hip",
-           "repack.hip", "prep.hip", "gemm_mx.hip"]
+           "repack.hip", "prep.hip", "gemm_mx.hip", "calib.hip"]
 HEADERS = ["common.h", "kernels.h"]
 
 

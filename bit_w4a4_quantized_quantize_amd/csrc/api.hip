@@ -2,6 +2,8 @@
 // the host, workspace layout, and the launch sequence of each entry point.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <string>
 
@@ -24,6 +26,37 @@ int fail(int code, const char* fmt, ...) {
 
 int ok() {
   g_last_error.clear();
+  return SVDQ_OK;
+}
+
+// Debug mode: SVDQ_DEBUG set to 1, true, yes or on (any case), read once per
+// process. Every entry point then synchronises its stream after each launch
+// (unless the stream is being captured into a graph) and reports any error the
+// kernels raised as SVDQ_ERR_HIP, naming the launch.
+bool parse_debug_flag(const char* v) {
+  if (v == nullptr) return false;
+  char b[8] = {0};
+  for (int i = 0; i < 7 && v[i]; ++i) b[i] = (char)((v[i] >= 'A' && v[i] <= 'Z') ? v[i] - 'A' + 'a' : v[i]);
+  if (strlen(v) > 7) return false;
+  return !strcmp(b, "1") || !strcmp(b, "true") || !strcmp(b, "yes") || !strcmp(b, "on");
+}
+
+bool debug_mode() {
+  static const bool on = parse_debug_flag(getenv("SVDQ_DEBUG"));
+  return on;
+}
+
+// After a launch (or an entry point's launch sequence): a launch error becomes
+// SVDQ_ERR_HIP; in debug mode the stream is synchronised and checked too.
+int launched(hipError_t e, const char* what, hipStream_t s) {
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  if (debug_mode()) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(s, &cs);
+    if (e == hipSuccess && cs == hipStreamCaptureStatusNone) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "%s (checked after the launch): %s", what, hipGetErrorString(e));
+  }
   return SVDQ_OK;
 }
 
@@ -139,7 +172,7 @@ int run_quantize(const void* x, const void* smooth, int64_t M, int64_t K, const 
                                 static_cast<uint8_t*>(ascales), static_cast<uint16_t*>(lora_act),
                                 static_cast<float*>(scratch), M, K, R, packed_out, s);
   }
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "quantisation launch: %s", hipGetErrorString(e));
+  if (int st = launched(e, "quantisation", s)) return st;
   return ok();
 }
 
@@ -180,6 +213,8 @@ const char* svdq_status_string(int status) {
 }
 
 const char* svdq_last_error(void) { return g_last_error.c_str(); }
+
+int svdq_debug_mode(void) { return debug_mode() ? 1 : 0; }
 
 size_t svdq_quantize_act_workspace_bytes(int64_t M, int64_t K, int64_t R) {
   if (M <= 0 || K <= 0 || R <= 0) return 0;
@@ -272,7 +307,7 @@ int svdq_repack_weight(const void* qweight, const void* wscales, int64_t N, int6
                                      static_cast<const uint8_t*>(wscales),
                                      static_cast<uint8_t*>(packed), N, K,
                                      static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "repack launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "repack", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -295,7 +330,7 @@ int svdq_unpack_weight(const void* packed, size_t packed_bytes, int64_t N, int64
                                      static_cast<uint8_t*>(qweight_out),
                                      static_cast<uint8_t*>(wscales_out), N, K,
                                      static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "unpack launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "unpack", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -384,7 +419,7 @@ int svdq_gemm_w4a4(const void* qact, const void* ascales, int act_layout, const 
   a.packed = weight_layout == SVDQ_WEIGHT_PACKED;
   hipError_t e = act_packed ? svdq::launch_gemm_lds(a, static_cast<hipStream_t>(stream))
                             : svdq::launch_gemm_w4a4(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -455,7 +490,7 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   a.M = M; a.N = N; a.K = K; a.R = R;
   a.packed = packed;
   hipError_t e = packed ? svdq::launch_gemm_lds(a, s) : svdq::launch_gemm_w4a4(a, s);
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -511,7 +546,7 @@ int svdq_gemm_w4a4_gated(const void* qact, const void* lora_act, const void* wei
   if ((st = check_alias(in, 7, out, 1))) return st;
   const svdq::GemmArgs a = gated_args(qact, lora_act, weight, wcscales, wtscale, proj_up, bias, M, F, K, R, h);
   hipError_t e = svdq::launch_gemm_lds(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -568,7 +603,7 @@ int svdq_linear_w4a4_gated(const void* x, const void* smooth, const void* weight
   if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, nullptr, lora, scratch, true, s))) return st;
   const svdq::GemmArgs a = gated_args(qact, lora, weight, wcscales, wtscale, proj_up, bias, M, F, K, R, h);
   hipError_t e = svdq::launch_gemm_lds(a, s);
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -600,7 +635,7 @@ int svdq_linear_bf16(const void* x, const void* weight, const void* bias, int64_
   a.N = N;
   a.K = K;
   hipError_t e = svdq::launch_gemm_bf16(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "bf16 gemm launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "bf16 gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -672,16 +707,17 @@ int svdq_prepare_weight(const void* weight, const void* smooth, const void* omeg
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipError_t e = hipSuccess;
-  if (R > 0)
+  if (R > 0) {
     e = svdq::launch_prepare_lowrank(static_cast<const uint16_t*>(weight), static_cast<const uint16_t*>(smooth),
                                      static_cast<const float*>(omega), N, K, R, iters,
                                      static_cast<uint16_t*>(proj_down), static_cast<uint16_t*>(proj_up), ws, s);
-  if (e == hipSuccess)
-    e = svdq::launch_prepare_residual(static_cast<const uint16_t*>(weight), static_cast<const uint16_t*>(smooth),
+    if (int st_ = launched(e, "rank-R split", s)) return st_;
+  }
+  e = svdq::launch_prepare_residual(static_cast<const uint16_t*>(weight), static_cast<const uint16_t*>(smooth),
                                       static_cast<const uint16_t*>(proj_down), static_cast<const uint16_t*>(proj_up),
                                       N, K, R, static_cast<uint8_t*>(qweight), static_cast<uint8_t*>(wscales),
                                       static_cast<uint16_t*>(wcscales), static_cast<uint16_t*>(wtscale), ws, s);
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "preparation launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "preparation", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -699,7 +735,7 @@ int svdq_prepare_residual(const void* weight, const void* smooth, const void* pr
       static_cast<const uint16_t*>(proj_down), static_cast<const uint16_t*>(proj_up), N, K, R,
       static_cast<uint8_t*>(qweight), static_cast<uint8_t*>(wscales), static_cast<uint16_t*>(wcscales),
       static_cast<uint16_t*>(wtscale), static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "preparation launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "preparation", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -738,7 +774,7 @@ int svdq_reround_weight_mxfp4(const void* qweight, const void* wscales, int64_t 
   hipError_t e = svdq::launch_reround_mx(static_cast<const uint8_t*>(qweight), static_cast<const uint8_t*>(wscales),
                                          static_cast<uint8_t*>(mx_codes), static_cast<uint8_t*>(mx_scales), N, K,
                                          static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "re-round launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "re-round", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -757,7 +793,7 @@ int svdq_quantize_act_mxfp4(const void* x, const void* smooth, int64_t M, int64_
   hipError_t e = svdq::launch_quant_act_mx(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
                                            static_cast<uint8_t*>(mx_codes), static_cast<uint8_t*>(mx_scales), M, K,
                                            static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "MX quantisation launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "MX quantisation", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -837,7 +873,7 @@ int svdq_gemm_mxfp4(const void* act_codes, const void* act_scales, const void* l
   const svdq::MxGemmArgs a = mx_args(act_codes, act_scales, lora_act, w_codes, w_scales, wcscales, wtscale, proj_up,
                                      bias, M, N, K, R, y);
   hipError_t e = svdq::launch_gemm_mx(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "MX gemm launch: %s", hipGetErrorString(e));
+  if (int st_ = launched(e, "MX gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 
@@ -897,16 +933,77 @@ int svdq_linear_mxfp4(const void* x, const void* smooth, const void* w_codes, co
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipError_t e = svdq::launch_quant_act_mx(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
                                            ws + w.codes, ws + w.scales, M, K, s);
+  if (int st_ = launched(e, "MX quantisation", s)) return st_;
   uint16_t* lora = reinterpret_cast<uint16_t*>(ws + w.lora);
-  if (e == hipSuccess && R > 0)
+  if (R > 0) {
     e = svdq::launch_lowrank_down(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(proj_down), lora,
                                   reinterpret_cast<float*>(ws + w.partial), M, K, R, s);
-  if (e == hipSuccess) {
-    const svdq::MxGemmArgs a = mx_args(ws + w.codes, ws + w.scales, lora, w_codes, w_scales, wcscales, wtscale,
-                                       proj_up, bias, M, N, K, R, y);
-    e = svdq::launch_gemm_mx(a, s);
+    if (int st_ = launched(e, "down-projection", s)) return st_;
   }
-  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "MX layer launch: %s", hipGetErrorString(e));
+  const svdq::MxGemmArgs a = mx_args(ws + w.codes, ws + w.scales, lora, w_codes, w_scales, wcscales, wtscale,
+                                     proj_up, bias, M, N, K, R, y);
+  e = svdq::launch_gemm_mx(a, s);
+  if (int st_ = launched(e, "MX gemm", s)) return st_;
+  return ok();
+}
+
+// ---- measurement helpers (not part of the layer) ----
+
+size_t svdq_calib_table_bytes(void) { return svdq::calib_table_bytes(); }
+
+int64_t svdq_calib_flop_per_iteration(int64_t workgroups) {
+  if (workgroups <= 0) return 0;
+  return workgroups * svdq::calib_waves_per_workgroup() * svdq::calib_flop_per_wave_iteration();
+}
+
+int svdq_calib_mfma(const void* table, size_t table_bytes, int64_t iters, int64_t workgroups, void* out,
+                    size_t out_bytes, void* clocks, size_t clocks_bytes, void* stream) {
+  if (iters < 1 || workgroups < 1 || workgroups > (int64_t(1) << 20))
+    return fail(SVDQ_ERR_SHAPE, "iters = %lld and workgroups = %lld must be positive (workgroups <= 2^20)",
+                (long long)iters, (long long)workgroups);
+  int st;
+  {
+    const char* names[] = {"table", "out", "clocks"};
+    const void* ptrs[] = {table, out, clocks};
+    if ((st = check_ptrs(names, ptrs, 3))) return st;
+  }
+  if (table_bytes < svdq::calib_table_bytes())
+    return fail(SVDQ_ERR_WORKSPACE, "table has %zu bytes, %zu needed", table_bytes, svdq::calib_table_bytes());
+  const size_t need_out = (size_t)workgroups * 64 * svdq::calib_waves_per_workgroup() * 4;
+  const size_t need_clk = (size_t)workgroups * 4 * 8;
+  if (out_bytes < need_out || clocks_bytes < need_clk)
+    return fail(SVDQ_ERR_WORKSPACE, "out has %zu bytes (%zu needed), clocks %zu (%zu needed)", out_bytes, need_out,
+                clocks_bytes, need_clk);
+  const Range in[] = {range("table", table, svdq::calib_table_bytes())};
+  const Range outs[] = {range("out", out, need_out), range("clocks", clocks, need_clk)};
+  if ((st = check_alias(in, 1, outs, 2))) return st;
+  hipError_t e = svdq::launch_calib_mfma(table, iters, workgroups, static_cast<float*>(out),
+                                         static_cast<uint64_t*>(clocks), static_cast<hipStream_t>(stream));
+  if (int st_ = launched(e, "calibration", static_cast<hipStream_t>(stream))) return st_;
+  return ok();
+}
+
+int svdq_calib_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes % 16 != 0) return fail(SVDQ_ERR_SHAPE, "bytes = %zu is not a multiple of 16", bytes);
+  if (bytes == 0) return ok();
+  int st;
+  const char* names[] = {"src", "dst"};
+  const void* ptrs[] = {src, dst};
+  if ((st = check_ptrs(names, ptrs, 2))) return st;
+  const Range in[] = {range("src", src, bytes)};
+  const Range outs[] = {range("dst", dst, bytes)};
+  if ((st = check_alias(in, 1, outs, 1))) return st;
+  hipError_t e = svdq::launch_calib_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+  if (int st_ = launched(e, "copy", static_cast<hipStream_t>(stream))) return st_;
+  return ok();
+}
+
+int svdq_calib_wall_clock_khz(int* khz) {
+  if (khz == nullptr) return fail(SVDQ_ERR_NULL, "khz is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "wall clock rate: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -1,0 +1,113 @@
+// Measurement helpers, not part of the layer: the sustained rate of the matrix
+// instruction the NVFP4 GEMM runs (v_mfma_f32_32x32x16_f16) on operands the
+// caller chooses, with the shader clock sampled in the kernel, and a plain
+// streaming device copy. They calibrate the roofline figures the benchmark
+// reports next to the published peaks: the chip power-limits its clock under
+// sustained matrix work, and by how much depends on how many operand bits
+// toggle, so the operand table decides what "sustained" means.
+#include "common.h"
+#include "kernels.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int kCalibWaves = 8;     // two waves per SIMD, as in the GEMM
+constexpr int kCalibFrags = 8;     // operand fragments per lane
+constexpr int kCalibTables = 64;   // distinct per-wave operand sets in the table
+
+// Each wave holds the GEMM's accumulator footprint (2 x 5 tiles of 32 x 32,
+// 160 registers) and eight f16 operand fragments. One iteration issues 20
+// independent-accumulator matrix instructions whose operand pairs all differ
+// from the previous instruction's, so the operand bits keep toggling. Wave 0,
+// lane 0 of every workgroup records the core-clock and the constant-rate
+// counters at its start and end.
+__global__ __launch_bounds__(64 * kCalibWaves) void calib_mfma_kernel(const f16x8* __restrict__ table,
+                                                                      int64_t iters, float* __restrict__ out,
+                                                                      uint64_t* __restrict__ clocks) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int set = (int)((blockIdx.x * kCalibWaves + wave) % kCalibTables);
+  f16x8 f[kCalibFrags];
+#pragma unroll
+  for (int i = 0; i < kCalibFrags; ++i) f[i] = table[(set * kCalibFrags + i) * 64 + lane];
+  f32x16 acc[10];
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+
+  const bool timer = threadIdx.x == 0;
+  uint64_t c0 = 0, w0 = 0;
+  if (timer) {
+    c0 = (uint64_t)clock64();
+    w0 = (uint64_t)wall_clock64();
+  }
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 5; ++j)
+        acc[5 * i + j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[i], f[2 + j], acc[5 * i + j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 5; ++j)
+        acc[5 * i + j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[7 - i], f[j], acc[5 * i + j], 0, 0, 0);
+  }
+  if (timer) {
+    const uint64_t c1 = (uint64_t)clock64();
+    const uint64_t w1 = (uint64_t)wall_clock64();
+    uint64_t* c = clocks + 4 * blockIdx.x;
+    c[0] = c0;
+    c[1] = c1;
+    c[2] = w0;
+    c[3] = w1;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[t][r];
+  out[(size_t)blockIdx.x * 64 * kCalibWaves + threadIdx.x] = s;
+}
+
+// Grid-stride copy of 16-byte units, four in flight per thread.
+__global__ __launch_bounds__(256) void calib_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                         int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    dst[i] = a;
+    dst[i + stride] = b;
+    dst[i + 2 * stride] = c;
+    dst[i + 3 * stride] = d;
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+size_t calib_table_bytes() { return (size_t)kCalibTables * kCalibFrags * 64 * sizeof(f16x8); }
+int calib_waves_per_workgroup() { return kCalibWaves; }
+int64_t calib_flop_per_wave_iteration() { return 20 * 2 * 32 * 32 * 16; }
+
+hipError_t launch_calib_mfma(const void* table, int64_t iters, int64_t workgroups, float* out, uint64_t* clocks,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(calib_mfma_kernel, dim3((unsigned)workgroups), dim3(64 * kCalibWaves), 0, stream,
+                     static_cast<const f16x8*>(table), iters, out, clocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  const int64_t n = (int64_t)(bytes / 16);
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + 1023) / 1024;
+  const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(calib_copy_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const u32x4*>(src),
+                     static_cast<u32x4*>(dst), n);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

@@ -121,4 +121,16 @@ hipError_t launch_repack(const uint8_t* qweight, const uint8_t* wscales, uint8_t
 hipError_t launch_unpack(const uint8_t* packed, uint8_t* qweight, uint8_t* wscales,
                          int64_t N, int64_t K, hipStream_t stream);
 
+// Measurement helpers (not part of the layer): sustained f16 matrix-instruction
+// rate on a caller-filled operand table of calib_table_bytes() bytes, with the
+// core-clock and constant-rate counters of each workgroup's start and end in
+// clocks [workgroups][4] (c0, c1, w0, w1); out receives 512 floats per
+// workgroup. And a plain device copy of `bytes` (a multiple of 16).
+size_t calib_table_bytes();
+int calib_waves_per_workgroup();
+int64_t calib_flop_per_wave_iteration();
+hipError_t launch_calib_mfma(const void* table, int64_t iters, int64_t workgroups, float* out, uint64_t* clocks,
+                             hipStream_t stream);
+hipError_t launch_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
 }  // namespace svdq

@@ -94,6 +94,12 @@ int svdq_abi_version(void);
 const char* svdq_status_string(int status);
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char* svdq_last_error(void);
+/* Debug mode: 1 when the environment variable SVDQ_DEBUG was 1, true, yes or on
+ * (any case) when the library first read it (once per process), else 0. In debug
+ * mode every entry point synchronises its stream after each kernel launch (not
+ * while the stream is being captured into a graph) and returns SVDQ_ERR_HIP,
+ * naming the launch, if the device reported an error. */
+int svdq_debug_mode(void);
 
 /*
  * Activation quantisation quant(x * smooth), and the down-projection of the
@@ -304,6 +310,34 @@ int svdq_linear_mxfp4(const void* x, const void* smooth, const void* w_codes, co
                       const void* wcscales, const void* wtscale, const void* proj_down, const void* proj_up,
                       const void* bias, int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement helpers. Not part of the layer and not from the pages: they
+ * calibrate the roofline figures reported beside AMD's published MI355X peaks.
+ *
+ * svdq_calib_mfma: `workgroups` workgroups of 8 waves (two per SIMD, the
+ *   GEMM's occupancy), each wave holding the GEMM's 2 x 5 accumulator tiles
+ *   and running `iters` iterations of 20 v_mfma_f32_32x32x16_f16 on operand
+ *   fragments read once from `table` (svdq_calib_table_bytes() bytes of f16
+ *   values the caller chooses: the power the chip draws, and so its clock,
+ *   depends on how many operand bits toggle). Work per launch:
+ *   iters * svdq_calib_flop_per_iteration(workgroups) flop.
+ *   out: >= workgroups * 512 floats (sums that keep the results live);
+ *   clocks: >= workgroups * 4 uint64, per workgroup the core-clock counter at
+ *   its start and end, then the constant-rate counter at its start and end
+ *   (rate in kHz from svdq_calib_wall_clock_khz).
+ * svdq_calib_copy: dst = src, `bytes` (a multiple of 16) by a streaming
+ *   kernel; src and dst must not overlap. The device-copy rate is the
+ *   practical HBM ceiling, and its byte counters calibrate the profiler's.
+ * svdq_calib_wall_clock_khz: the constant counter's rate on the current
+ *   device (a property query; nothing is enqueued).
+ */
+size_t svdq_calib_table_bytes(void);
+int64_t svdq_calib_flop_per_iteration(int64_t workgroups);
+int svdq_calib_mfma(const void* table, size_t table_bytes, int64_t iters, int64_t workgroups, void* out,
+                    size_t out_bytes, void* clocks, size_t clocks_bytes, void* stream);
+int svdq_calib_copy(const void* src, void* dst, size_t bytes, void* stream);
+int svdq_calib_wall_clock_khz(int* khz);
 
 #ifdef __cplusplus
 }

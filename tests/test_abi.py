@@ -307,3 +307,20 @@ def test_mx_rejections_and_sizes():
                              64, 64, 256, 24, fake(9), None) == 3
     assert L.svdq_linear_mxfp4(fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), fake(7), fake(8), None,
                                64, 64, 256, 16, fake(9), fake(10), 0, None) == 5
+
+
+@pytest.mark.parametrize("value,on", [(None, 0), ("1", 1), ("true", 1), ("ON", 1), ("Yes", 1), ("0", 0),
+                                      ("", 0), ("no", 0), ("off", 0), ("2", 0), ("1 ", 0), ("truetrue", 0)])
+def test_debug_flag_parsing(value, on):
+    """SVDQ_DEBUG is read once per process, so each value runs in a fresh interpreter."""
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("SVDQ_DEBUG", None)
+    if value is not None:
+        env["SVDQ_DEBUG"] = value
+    code = ("import sys; sys.path.insert(0, %r); from bit_w4a4_quantized_quantize_amd import _lib; "
+            "print(_lib.lib().svdq_debug_mode())" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert int(out.stdout.strip()) == on

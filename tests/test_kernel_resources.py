@@ -15,7 +15,7 @@ HIPCC = "/opt/rocm/bin/hipcc"
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 @pytest.mark.parametrize("src", ["gemm_lds.hip", "gemm_bf16.hip", "gemm_w4a4.hip", "gemm_mx.hip", "quant_lora.hip",
-                                 "quant_act.hip", "repack.hip", "prep.hip"])
+                                 "quant_act.hip", "repack.hip", "prep.hip", "calib.hip"])
 def test_no_scratch_no_spills(src, tmp_path):
     path = os.path.join(build.CSRC, src)
     cmd = [HIPCC, *build.COMMON_FLAGS, "-I", build.INCLUDE, "-I", build.CSRC, "--cuda-device-only", "-c", path,
