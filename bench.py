@@ -83,6 +83,95 @@ CALIBS = {"calib": "sustained v_mfma_f32_32x32x16_f16 (8 waves per CU, the GEMM'
                    "the kernel; streaming device copy of 1 GiB (HBM) and 64 MiB (cache resident)"}
 
 
+# the oracle's own timing on the host cores (no GPU): the configurations of the pages'
+# workloads, quantisation and the rest of the layer timed apart
+ORACLE_TIMES = {"oracle_times": "the CPU oracle (NumPy float64 / int64) per layer call: median of 3 at the "
+                                "tiny config, the 1024^2 QKV and FFN w1 layers; one run per 2048px layer; the "
+                                "mixed-precision forward extrapolated from per-layer rates"}
+
+
+def blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        return [{k: i.get(k) for k in ("internal_api", "num_threads", "version")} for i in info]
+    except Exception:
+        return []
+
+
+def run_oracle_times(args):
+    import numpy as np
+
+    import workloads
+    from oracle import svdq as S
+
+    cfgs = [("tiny", dict(workloads.TINY), 3), ("qkv_1024", dict(workloads.QKV_1024), 3),
+            ("ffn_w1_1024", dict(workloads.FFN_W1_1024), 3)]
+    cfgs += [(f"{k}_2048", dict(v), 1) for k, v in workloads.LAYERS_2048.items()]
+    rows = {}
+    for name, cfg, reps in cfgs:
+        d = workloads.make_linear(**cfg)
+        qw, ws = S.quantize_weight(d["W"], d["wcscales"], d["wtscale"])   # load time, not timed
+        M, K, N, R = cfg["M"], cfg["K"], cfg["N"], cfg["R"]
+        tq, tr = [], []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            qact, asc = S.quantize_act(d["x"], d["smooth"])
+            t1 = time.perf_counter()
+            main = S.main_term(qact, asc, qw, ws)
+            lr = S.lowrank(d["x"], d["proj_down"], d["proj_up"])
+            S.epilogue(main, d["wcscales"], d["wtscale"], lr, d["bias"])
+            t2 = time.perf_counter()
+            tq.append(t1 - t0)
+            tr.append(t2 - t1)
+            del qact, asc, main, lr
+        q, r = float(np.median(tq)), float(np.median(tr))
+        flops = 2 * M * N * K + 2 * M * R * (K + N)
+        qbytes = M * K * 2 + K * 2 + M * K // 2 + (K // 16) * M
+        rows[name] = {"M": M, "K": K, "N": N, "R": R, "runs": reps, "quant_s": round(q, 4), "rest_s": round(r, 4),
+                      "layer_s": round(q + r, 4), "TFLOPs": round(flops / (q + r) / 1e12, 4),
+                      "quant_GBps": round(qbytes / q / 1e9, 3)}
+        print(f"[oracle] {name}: {rows[name]}", file=sys.stderr, flush=True)
+        del d, qw, ws
+    # one bf16 layer (the out projection at 1024^2), then the mixed-precision forward
+    # (90 bf16 + 60 W4A4 linears at M=4096) extrapolated from the measured per-flop rates
+    db = workloads.make_bf16_linear(4096, 3840, 3840, kind="dit", seed=5001)
+    t0 = time.perf_counter()
+    S.linear_bf16(db["x"], db["W"], db["bias"])
+    t_bf = time.perf_counter() - t0
+    rate_bf = 2 * 4096 * 3840 * 3840 / t_bf
+    rows["out_1024_bf16"] = {"M": 4096, "K": 3840, "N": 3840, "runs": 1, "layer_s": round(t_bf, 4),
+                             "TFLOPs": round(rate_bf / 1e12, 4)}
+    print(f"[oracle] out_1024_bf16: {rows['out_1024_bf16']}", file=sys.stderr, flush=True)
+    t_fwd = 0.0
+    for L in workloads.sweep_layers():
+        if L["precision"] == "bf16":
+            t_fwd += 2 * 4096 * L["K"] * L["N"] / rate_bf
+        else:
+            rate = rows["ffn_w1_1024" if L["K"] == 3840 else "w2_2048"]["TFLOPs"] * 1e12
+            t_fwd += (2 * 4096 * L["K"] * L["N"] + 2 * 4096 * 128 * (L["K"] + L["N"])) / rate
+    cores = len(os.sched_getaffinity(0))
+    result = {
+        "metric": "CPU oracle seconds per SVDQuant W4A4 linear call at M=4096,K=3840,N=10240 (host cores)",
+        "value": rows["ffn_w1_1024"]["layer_s"],
+        "unit": "s",
+        "n_gpus": 0,
+        "steps": 3,
+        "warmup": 0,
+        "ms_per_step": rows["ffn_w1_1024"]["layer_s"] * 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": ORACLE_TIMES["oracle_times"], "cores": cores,
+                   "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"), "blas": blas_info()},
+        "layers": rows,
+        "mixed_precision_forward_s_extrapolated": round(t_fwd, 1),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def run_calib(args):
     import torch
     dev = torch.device("cuda:0")
@@ -123,7 +212,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--workload",
                    choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS) + sorted(SWEEPS) + sorted(PREPS) + sorted(MX_VARIANTS)
-                   + sorted(CALIBS),
+                   + sorted(CALIBS) + sorted(ORACLE_TIMES),
                    default=DEFAULT_WORKLOAD,
                    help="layer shape (the default is the headline workload; the rest are for comparison)")
     p.add_argument("--gpus", type=int, default=1)
@@ -1026,6 +1115,8 @@ def run_mx(args):
 
 def main():
     args = parse()
+    if args.workload in ORACLE_TIMES:
+        return run_oracle_times(args)
     if args.workload in CALIBS:
         if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
             print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
