@@ -35,6 +35,10 @@ SIGNATURES = {
     "svdq_linear_w4a4": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _int,
                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "svdq_noalloc_scratch_bytes": (_size, []),
+    "svdq_linear_w4a4_noalloc": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _int,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                        _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
     "svdq_gemm_w4a4_gated": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
     "svdq_linear_gated_workspace_bytes": (_size, [_i64, _i64, _i64, _i64]),

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -945,6 +947,75 @@ int svdq_linear_mxfp4(const void* x, const void* smooth, const void* w_codes, co
   e = svdq::launch_gemm_mx(a, s);
   if (int st_ = launched(e, "MX gemm", s)) return st_;
   return ok();
+}
+
+}  // extern "C"
+
+// ---- the layer without allocation: workspace in a static device array ----
+//
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops, harnesses that forbid it): svdq_linear_w4a4_noalloc runs the same
+// launches as svdq_linear_w4a4 with its workspace in `scratch`, a file-scope
+// device array every GPU the library runs on holds until the process ends. In
+// host code `scratch` only names the symbol; its device address on the current
+// device comes from hipGetSymbolAddress, taken once per device on the first
+// call there and kept. Nothing in the workspace needs initialising (each call
+// writes everything it later reads), so no clearing step is needed; calls
+// that overlap on one GPU share the array and race.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SVDQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SVDQ_ERR_UNSUPPORTED, "device ordinal %d is beyond the %d this library tracks", dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(SVDQ_ERR_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SVDQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t svdq_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+int svdq_linear_w4a4_noalloc(const void* x, const void* smooth, const void* weight, const void* wscales,
+                             int weight_layout, const void* wcscales, const void* wtscale, const void* proj_down,
+                             const void* proj_up, const void* bias, int64_t M, int64_t N, int64_t K, int64_t R,
+                             void* y, void* stream) {
+  int st = check_mk(M, K, R);
+  if (st) return st;
+  if ((st = check_nk(N, K))) return st;
+  if (M == 0 || N == 0) return ok();
+  const size_t need = linear_ws(M, K, R).total;
+  if (need > kNoallocScratchBytes)
+    return fail(SVDQ_ERR_WORKSPACE,
+                "M=%lld K=%lld R=%lld needs %zu bytes of workspace; the static scratch holds %zu "
+                "(use svdq_linear_w4a4 with a caller workspace)",
+                (long long)M, (long long)K, (long long)R, need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws))) return st;
+  return svdq_linear_w4a4(x, smooth, weight, wscales, weight_layout, wcscales, wtscale, proj_down, proj_up, bias,
+                          M, N, K, R, y, ws, kNoallocScratchBytes, stream);
 }
 
 // ---- measurement helpers (not part of the layer) ----

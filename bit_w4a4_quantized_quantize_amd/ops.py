@@ -297,6 +297,30 @@ def linear_w4a4(x, w: SVDQLinearWeights, y=None, workspace=None):
     return y
 
 
+def linear_w4a4_noalloc(x, w: SVDQLinearWeights, y):
+    """The whole layer with the library's static device scratch as workspace (no
+    allocation by the library; y [M, N] bf16 must be given). Raises SvdqError
+    (SVDQ_ERR_WORKSPACE) when the problem needs more than noalloc_scratch_bytes()."""
+    dev = _check_layer(w)
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"x has K={K}, the layer K={w.K}")
+    _need(y, "y", torch.bfloat16, shape=(M, w.N))
+    _devices(**_layer_tensors(w), x=x, y=y)
+    L = _lib.lib()
+    _lib.check("svdq_linear_w4a4_noalloc", L.svdq_linear_w4a4_noalloc(
+        _p(x), _p(w.smooth), _p(_bytes(w.weight)),
+        _p(_bytes(w.wscales)) if w.wscales is not None else None, w.layout,
+        _p(w.wcscales), _p(w.wtscale), _p(w.proj_down) if w.R > 0 else None,
+        _p(w.proj_up) if w.R > 0 else None, _p(w.bias), M, w.N, K, w.R, _p(y), _stream(dev)))
+    return y
+
+
+def noalloc_scratch_bytes():
+    return int(_lib.lib().svdq_noalloc_scratch_bytes())
+
+
 def _check_gated(w: SVDQLinearWeights):
     if w.layout != WEIGHT_PACKED:
         raise ValueError("the gated layer needs the packed weight layout (use .packed())")

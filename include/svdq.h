@@ -191,6 +191,25 @@ int svdq_linear_w4a4(const void* x, const void* smooth,
                      void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The whole layer without allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid allocation. Same arguments and results as svdq_linear_w4a4 (bit for
+ * bit: the same kernels run), minus the workspace: the library keeps it in a
+ * static device array of svdq_noalloc_scratch_bytes() bytes (64 MiB), which
+ * every GPU the library runs on holds until the process ends. A problem whose
+ * svdq_linear_workspace_bytes(M, N, K, R) exceeds that returns
+ * SVDQ_ERR_WORKSPACE before anything is enqueued. Calls that overlap on one
+ * GPU (different streams or host threads) share the array and race; serialise
+ * them. No hipMalloc, hipFree or other allocating call is made.
+ */
+size_t svdq_noalloc_scratch_bytes(void);
+int svdq_linear_w4a4_noalloc(const void* x, const void* smooth,
+                             const void* weight, const void* wscales, int weight_layout,
+                             const void* wcscales, const void* wtscale,
+                             const void* proj_down, const void* proj_up, const void* bias,
+                             int64_t M, int64_t N, int64_t K, int64_t R, void* y, void* stream);
+
+/*
  * FFN neighbour (gated): the DiT feed-forward layers w1 and w3 (blog page
  * "Z-Image NVFP4 ...", layer table and its key insight: FFN w1, w2, w3 are the
  * NVFP4 layers) run as ONE SVDQuant layer with 2F output channels that share x,

@@ -324,3 +324,22 @@ def test_debug_flag_parsing(value, on):
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
     assert int(out.stdout.strip()) == on
+
+
+@no_gpu_only
+def test_noalloc_size_limit_and_empty():
+    """The no-allocation entry point refuses a problem whose workspace exceeds its static
+    scratch, on the host, before any pointer is used; empty problems succeed."""
+    L = _lib.lib()
+    cap = L.svdq_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    M, K, N, R = 16896, 10240, 3840, 128
+    assert L.svdq_linear_workspace_bytes(M, N, K, R) > cap
+    st = L.svdq_linear_w4a4_noalloc(fake(1), fake(2), fake(3), None, 1, fake(4), fake(5), fake(6), fake(7), None,
+                                    M, N, K, R, fake(8), None)
+    assert st == 5
+    assert b"static scratch" in L.svdq_last_error()
+    assert L.svdq_linear_w4a4_noalloc(None, None, None, None, 1, None, None, None, None, None, 0, N, K, R, None,
+                                      None) == 0
+    assert L.svdq_linear_w4a4_noalloc(None, None, None, None, 1, None, None, None, None, None, 64, N, 100, R, None,
+                                      None) == 2   # K not a multiple of 16
