@@ -190,6 +190,71 @@ def linear_w4a4(x_bits, smooth_bits, qweight, wscales, wcscales_bits, wtscale_bi
 
 
 # ---------------------------------------------------------------------------
+# Static (calibrated) activation scale
+# ---------------------------------------------------------------------------
+#
+# The blog page's section on the Comfy-Org Z-Image Turbo NVFP4 checkpoint says it
+# uses calibrated static activation scales; the pages give no rule. Reading
+# (NVFP4's two-level form): a per-tensor global scale g is fixed offline from
+# calibration activations, g = bf16(max |x * smooth| / (6 * 448)) (1 when that
+# maximum is 0), and the per-16 e4m3 block scales are still computed per call,
+# relative to g:
+#     s = e4m3(amax / (6 g)) (nearest even, saturating at 448),
+#     codes = E2M1 nearest even of |v| / (dec(s) * g) (saturating at 6, sign kept).
+# The layer's main term then carries a factor g: A_eff = E2M1 * dec(s) * g, so
+# y = main * g * wtscale * wcscales + lowrank + bias. With g = 1 this is the
+# dynamic rule above. g is a bf16 value (8 significant bits).
+
+
+def _quantize_blocks_static(v, g):
+    """Per 16-block of float64 rows v [rows, K] with the global scale g (float64):
+    (codes [rows, K] 0..15, scale bytes [rows, K/16])."""
+    rows, K = v.shape
+    assert K % BLOCK == 0 and g > 0
+    vb = v.reshape(rows, K // BLOCK, BLOCK)
+    amax = np.abs(vb).max(axis=2)
+    sc = F.e4m3_encode(amax / (6.0 * g))
+    d = F.e4m3_decode(sc) * g              # exact: a 4-bit times an 8-bit significand
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.abs(vb) / d[:, :, None]
+    t = np.where(d[:, :, None] > 0, t, 0.0)
+    mag = F.e2m1_encode_mag(t)
+    sign = np.where(np.signbit(vb), 8, 0).astype(np.uint8)
+    return (mag | sign).reshape(rows, K), sc
+
+
+def calibrate_gscale(x_bits, smooth_bits):
+    """The static global activation scale from calibration activations x [M, K] (bf16
+    bits): bf16(max |x * smooth| / (6 * 448)), or bf16(1) when the maximum is 0.
+    Returns a uint16 array of shape (1,)."""
+    v = F.bf16_to_f64(x_bits) * F.bf16_to_f64(smooth_bits)[None, :]
+    amax = float(np.abs(v).max()) if v.size else 0.0
+    g = amax / 2688.0 if amax > 0 else 1.0
+    return F.f64_to_bf16(np.array([g]))
+
+
+def quantize_act_static(x_bits, smooth_bits, gscale_bits):
+    """quant(x * smooth) relative to the static global scale g (bf16 bits, shape (1,)):
+    qact [M, K/2] uint8 (low nibble = even k), ascales [K/16, M] uint8."""
+    g = float(F.bf16_to_f64(gscale_bits).reshape(-1)[0])
+    v = F.bf16_to_f64(x_bits) * F.bf16_to_f64(smooth_bits)[None, :]
+    codes, sc = _quantize_blocks_static(v, g)
+    return F.pack_nibbles(codes), np.ascontiguousarray(sc.T)
+
+
+def linear_w4a4_static(x_bits, smooth_bits, gscale_bits, qweight, wscales, wcscales_bits, wtscale_bits,
+                       proj_down_bits, proj_up_bits, bias_bits):
+    """The layer with static activation scales. Returns (y64, y bf16 bits, qact, ascales)."""
+    g = float(F.bf16_to_f64(gscale_bits).reshape(-1)[0])
+    qact, ascales = quantize_act_static(x_bits, smooth_bits, gscale_bits)
+    main = main_term(qact, ascales, qweight, wscales) * g
+    R = 0 if proj_down_bits is None else np.shape(proj_down_bits)[1]
+    lr = lowrank(x_bits, proj_down_bits, proj_up_bits) if R > 0 else None
+    y64 = epilogue(main, wcscales_bits, wtscale_bits, lr, bias_bits)
+    return y64, F.f64_to_bf16(y64), qact, ascales
+
+
+# ---------------------------------------------------------------------------
 # FFN neighbour: gated combination of the w1 / w3 outputs
 # ---------------------------------------------------------------------------
 #
