@@ -77,6 +77,89 @@ PEAK_FP4_MFMA_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak
 MX_VARIANTS = {"ffn_w1_1024_mxfp4": "ffn_w1_1024", "qkv_1024_mxfp4": "qkv_1024", "ffn_w2_1024_mxfp4": "ffn_w2_1024"}
 
 
+# the static (calibrated) activation-scale variant of a layer shape, beside the dynamic layer
+STATIC_VARIANTS = {"ffn_w1_1024_static": "ffn_w1_1024", "ffn_w2_1024_static": "ffn_w2_1024",
+                   "qkv_1024_static": "qkv_1024"}
+
+
+def run_static(args):
+    """Static activation scales: g calibrated by the library on a separate seeded batch of the
+    same distribution; the layer timed like the headline; accuracy of the static and the dynamic
+    layer against the unquantised float64 product on sampled rows."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from bit_w4a4_quantized_quantize_amd import ops
+    from oracle import formats as Fm
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    cfg, desc = workload_cfg(STATIC_VARIANTS[args.workload])
+    M, K, N, R = cfg["M"], cfg["K"], cfg["N"], cfg["R"]
+    n_sets = 1 if args.warm else args.sets
+    print(f"[bench] static activation scales: building {n_sets} sets for M={M} K={K} N={N} R={R}",
+          file=sys.stderr, flush=True)
+    d, sets = make_sets(cfg, n_sets, "packed", dev)
+    cal = workloads.make_linear(**dict(cfg, seed=cfg["seed"] + 1000))
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    g = ops.calibrate_act_gscale(bf(cal["x"]), sets[0]["layer"].smooth)
+    torch.cuda.synchronize()
+    g_val = float(g.float().item())
+    flops = 2 * M * N * K + 2 * M * R * (K + N)
+
+    def step(i):
+        st = sets[i]
+        ops.linear_w4a4_static(st["x"], st["layer"], g, y=st["y"], workspace=st["ws"])
+
+    ms, cond = timed(step, n_sets, args.steps, stream, warmup=args.warmup, min_ms=args.condition_ms)
+    tflops = flops / (ms * 1e-3) / 1e12
+    dyn_ms = time_loop(lambda i: ops.linear_w4a4(sets[i]["x"], sets[i]["layer"], y=sets[i]["y"],
+                                                 workspace=sets[i]["ws"]), n_sets, args.kernel_iters, 1, stream)
+    st = sets[0]
+    y_s = ops.linear_w4a4_static(st["x"], st["layer"], g)
+    y_d = ops.linear_w4a4(st["x"], st["layer"])
+    qa, sa, _ = ops.quantize_act_static(st["x"], st["layer"].smooth, g)
+    torch.cuda.synchronize()
+    sat = float((sa == 0x7E).float().mean().item())
+    dist = float(torch.linalg.vector_norm(y_s.float() - y_d.float()) / torch.linalg.vector_norm(y_d.float()))
+    # accuracy against the unquantised layer (x * smooth) W^T + (x proj_down) proj_up^T + bias on sampled rows
+    rows = np.sort(np.random.default_rng(7).choice(M, size=min(256, M), replace=False))
+    x64 = Fm.bf16_to_f64(d["x"][rows])
+    ref = (x64 * Fm.bf16_to_f64(d["smooth"])[None, :]) @ np.asarray(d["W"], np.float64).T
+    ref = ref + (x64 @ Fm.bf16_to_f64(d["proj_down"])) @ Fm.bf16_to_f64(d["proj_up"]).T + Fm.bf16_to_f64(d["bias"])
+    rsel = torch.from_numpy(rows).to(dev)
+
+    def err(y):
+        yy = y.index_select(0, rsel).float().cpu().double().numpy()
+        return float(np.linalg.norm(yy - ref) / np.linalg.norm(ref))
+
+    e_s, e_d = err(y_s), err(y_d)
+    print(f"[bench] static layer {ms * 1e3:.1f} us ({tflops:.1f} TFLOP/s), dynamic {dyn_ms * 1e3:.1f} us; g = {g_val:.6g}; "
+          f"saturated block scales {sat:.2e}; static vs dynamic {dist:.4f}; error vs unquantised: static {e_s:.4f}, "
+          f"dynamic {e_d:.4f}", file=sys.stderr, flush=True)
+    result = {
+        "metric": f"SVDQuant W4A4 linear with static (calibrated) activation scales, TFLOP/s at M={M},K={K},N={N}, 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{desc}: static global activation scale calibrated on another seeded batch "
+                               f"(seed {cfg['seed'] + 1000}), per-16 e4m3 block scales relative to it; "
+                               f"M={M} K={K} N={N} R={R}",
+                   "cache": "warm" if args.warm else f"cold (rotating {n_sets} sets)"},
+        "act_gscale": g_val, "saturated_block_scale_fraction": sat,
+        "dynamic_layer_us": round(dyn_ms * 1e3, 2),
+        "normwise_static_vs_dynamic": round(dist, 5),
+        "error_vs_unquantised": {"static": round(e_s, 5), "dynamic": round(e_d, 5), "rows": len(rows)},
+        "conditioning": cond,
+    }
+    print(json.dumps(result), flush=True)
+
+
 # roofline calibration of this device (no layer): sustained f16 MFMA and device copy
 CALIBS = {"calib": "sustained v_mfma_f32_32x32x16_f16 (8 waves per CU, the GEMM's occupancy and accumulator "
                    "footprint) on exact NVFP4 values, random f16 bits and zeros, with the shader clock read by "
@@ -212,7 +295,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--workload",
                    choices=sorted(WORKLOADS) + sorted(FFN_BLOCKS) + sorted(SWEEPS) + sorted(PREPS) + sorted(MX_VARIANTS)
-                   + sorted(CALIBS) + sorted(ORACLE_TIMES),
+                   + sorted(CALIBS) + sorted(ORACLE_TIMES) + sorted(STATIC_VARIANTS),
                    default=DEFAULT_WORKLOAD,
                    help="layer shape (the default is the headline workload; the rest are for comparison)")
     p.add_argument("--gpus", type=int, default=1)
@@ -1117,6 +1200,11 @@ def main():
     args = parse()
     if args.workload in ORACLE_TIMES:
         return run_oracle_times(args)
+    if args.workload in STATIC_VARIANTS:
+        if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+            print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)
+            sys.exit(2)
+        return run_static(args)
     if args.workload in CALIBS:
         if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
             print("bench.py: --gpus must be 1 (single-GPU build)", file=sys.stderr)

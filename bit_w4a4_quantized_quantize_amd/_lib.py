@@ -35,6 +35,14 @@ SIGNATURES = {
     "svdq_linear_w4a4": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _int,
                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "svdq_calibrate_workspace_bytes": (_size, [_i64, _i64]),
+    "svdq_calibrate_act_gscale": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _size,
+                                         _c_void_p]),
+    "svdq_quantize_act_static": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64, _int,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "svdq_linear_w4a4_static": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _int,
+                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                       _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, _size, _c_void_p]),
     "svdq_noalloc_scratch_bytes": (_size, []),
     "svdq_linear_w4a4_noalloc": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _int,
                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,

@@ -163,16 +163,17 @@ LinearWs linear_ws(int64_t M, int64_t K, int64_t R) {
 // enqueue a1 (+ a2): pointers already validated
 int run_quantize(const void* x, const void* smooth, int64_t M, int64_t K, const void* proj_down,
                  int64_t R, void* qact, void* ascales, void* lora_act, void* scratch, bool packed_out,
-                 hipStream_t s) {
+                 hipStream_t s, const void* gscale = nullptr) {
   hipError_t e;
+  const uint16_t* gs = static_cast<const uint16_t*>(gscale);
   if (R == 0 && !packed_out) {
     e = svdq::launch_quant_act(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
-                               static_cast<uint8_t*>(qact), static_cast<uint8_t*>(ascales), M, K, s);
+                               static_cast<uint8_t*>(qact), static_cast<uint8_t*>(ascales), M, K, s, gs);
   } else {
     e = svdq::launch_quant_lora(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
                                 static_cast<const uint16_t*>(proj_down), static_cast<uint8_t*>(qact),
                                 static_cast<uint8_t*>(ascales), static_cast<uint16_t*>(lora_act),
-                                static_cast<float*>(scratch), M, K, R, packed_out, s);
+                                static_cast<float*>(scratch), M, K, R, packed_out, s, gs);
   }
   if (int st = launched(e, "quantisation", s)) return st;
   return ok();
@@ -228,10 +229,29 @@ size_t svdq_packed_act_bytes(int64_t M, int64_t K) {
   return svdq::packed_weight_bytes(M, K);
 }
 
+static int quantize_act_impl(const void* x, const void* smooth, const void* gscale, int64_t M, int64_t K,
+                             const void* proj_down, int64_t R, int act_layout, void* qact, void* ascales,
+                             void* lora_act, void* workspace, size_t workspace_bytes, void* stream);
+
 int svdq_quantize_act(const void* x, const void* smooth, int64_t M, int64_t K,
                       const void* proj_down, int64_t R, int act_layout, void* qact,
                       void* ascales, void* lora_act, void* workspace, size_t workspace_bytes,
                       void* stream) {
+  return quantize_act_impl(x, smooth, nullptr, M, K, proj_down, R, act_layout, qact, ascales, lora_act, workspace,
+                           workspace_bytes, stream);
+}
+
+int svdq_quantize_act_static(const void* x, const void* smooth, const void* act_gscale, int64_t M, int64_t K,
+                             const void* proj_down, int64_t R, int act_layout, void* qact, void* ascales,
+                             void* lora_act, void* workspace, size_t workspace_bytes, void* stream) {
+  if (act_gscale == nullptr) return fail(SVDQ_ERR_NULL, "act_gscale is NULL");
+  return quantize_act_impl(x, smooth, act_gscale, M, K, proj_down, R, act_layout, qact, ascales, lora_act,
+                           workspace, workspace_bytes, stream);
+}
+
+static int quantize_act_impl(const void* x, const void* smooth, const void* gscale, int64_t M, int64_t K,
+                             const void* proj_down, int64_t R, int act_layout, void* qact, void* ascales,
+                             void* lora_act, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_mk(M, K, R);
   if (st) return st;
   if ((st = check_rsrc_sizes(M, K, R))) return st;
@@ -264,16 +284,18 @@ int svdq_quantize_act(const void* x, const void* smooth, int64_t M, int64_t K,
     const void* ptrs[] = {workspace};
     if ((st = check_ptrs(names, ptrs, 1))) return st;
   }
+  if (gscale != nullptr && !aligned16(gscale)) return fail(SVDQ_ERR_ALIGN, "act_gscale is not 16-byte aligned");
   const size_t qbytes = packed ? svdq::packed_weight_bytes(M, K) : (size_t)M * (K / 2);
   const Range in[] = {range("x", x, (size_t)M * K * 2), range("smooth", smooth, (size_t)K * 2),
-                      range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2)};
+                      range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2),
+                      range("act_gscale", gscale, 2)};
   const Range out[] = {range("qact", qact, qbytes),
                        range("ascales", packed ? nullptr : ascales, (size_t)(K / 16) * M),
                        range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
                        range("workspace", ws_need > 0 ? workspace : nullptr, ws_need)};
-  if ((st = check_alias(in, 3, out, 4))) return st;
+  if ((st = check_alias(in, 4, out, 4))) return st;
   return run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora_act,
-                      ws_need > 0 ? workspace : nullptr, packed, static_cast<hipStream_t>(stream));
+                      ws_need > 0 ? workspace : nullptr, packed, static_cast<hipStream_t>(stream), gscale);
 }
 
 size_t svdq_repack_weight_bytes(int64_t N, int64_t K) {
@@ -431,11 +453,33 @@ size_t svdq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t R) {
   return linear_ws(M, K, R).total;
 }
 
+static int linear_impl(const void* x, const void* smooth, const void* gscale, const void* weight,
+                       const void* wscales, int weight_layout, const void* wcscales, const void* wtscale,
+                       const void* proj_down, const void* proj_up, const void* bias, int64_t M, int64_t N,
+                       int64_t K, int64_t R, void* y, void* workspace, size_t workspace_bytes, void* stream);
+
 int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, const void* wscales,
                      int weight_layout, const void* wcscales, const void* wtscale,
                      const void* proj_down, const void* proj_up, const void* bias, int64_t M,
                      int64_t N, int64_t K, int64_t R, void* y, void* workspace,
                      size_t workspace_bytes, void* stream) {
+  return linear_impl(x, smooth, nullptr, weight, wscales, weight_layout, wcscales, wtscale, proj_down, proj_up,
+                     bias, M, N, K, R, y, workspace, workspace_bytes, stream);
+}
+
+int svdq_linear_w4a4_static(const void* x, const void* smooth, const void* act_gscale, const void* weight,
+                            const void* wscales, int weight_layout, const void* wcscales, const void* wtscale,
+                            const void* proj_down, const void* proj_up, const void* bias, int64_t M, int64_t N,
+                            int64_t K, int64_t R, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (act_gscale == nullptr) return fail(SVDQ_ERR_NULL, "act_gscale is NULL");
+  return linear_impl(x, smooth, act_gscale, weight, wscales, weight_layout, wcscales, wtscale, proj_down, proj_up,
+                     bias, M, N, K, R, y, workspace, workspace_bytes, stream);
+}
+
+static int linear_impl(const void* x, const void* smooth, const void* gscale, const void* weight,
+                       const void* wscales, int weight_layout, const void* wcscales, const void* wtscale,
+                       const void* proj_down, const void* proj_up, const void* bias, int64_t M, int64_t N,
+                       int64_t K, int64_t R, void* y, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_mk(M, K, R);
   if (st) return st;
   if ((st = check_rsrc_sizes(M, K, R))) return st;
@@ -466,9 +510,10 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
                       range("wtscale", wtscale, 2),
                       range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2),
                       range("proj_up", R > 0 ? proj_up : nullptr, (size_t)N * R * 2),
-                      range("bias", bias, (size_t)N * 2)};
+                      range("bias", bias, (size_t)N * 2), range("act_gscale", gscale, 2)};
   const Range out[] = {range("y", y, (size_t)M * N * 2), range("workspace", workspace, ws.total)};
-  if ((st = check_alias(in, 9, out, 2))) return st;
+  if ((st = check_alias(in, 10, out, 2))) return st;
+  if (gscale != nullptr && !aligned16(gscale)) return fail(SVDQ_ERR_ALIGN, "act_gscale is not 16-byte aligned");
 
   char* w = static_cast<char*>(workspace);
   const bool packed = weight_layout == SVDQ_WEIGHT_PACKED;
@@ -477,7 +522,7 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   void* lora = R > 0 ? (void*)(w + ws.lora) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   void* scratch = ws.total > ws.partial ? (void*)(w + ws.partial) : nullptr;
-  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora, scratch, packed, s))) return st;
+  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora, scratch, packed, s, gscale))) return st;
   svdq::GemmArgs a{};
   a.qact = static_cast<const uint8_t*>(qact);
   a.ascales = static_cast<const uint8_t*>(ascales);
@@ -491,6 +536,7 @@ int svdq_linear_w4a4(const void* x, const void* smooth, const void* weight, cons
   a.y = static_cast<uint16_t*>(y);
   a.M = M; a.N = N; a.K = K; a.R = R;
   a.packed = packed;
+  a.act_gscale = static_cast<const uint16_t*>(gscale);
   hipError_t e = packed ? svdq::launch_gemm_lds(a, s) : svdq::launch_gemm_w4a4(a, s);
   if (int st_ = launched(e, "gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
@@ -946,6 +992,34 @@ int svdq_linear_mxfp4(const void* x, const void* smooth, const void* w_codes, co
                                      proj_up, bias, M, N, K, R, y);
   e = svdq::launch_gemm_mx(a, s);
   if (int st_ = launched(e, "MX gemm", s)) return st_;
+  return ok();
+}
+
+size_t svdq_calibrate_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % 16 != 0) return 0;
+  return svdq::calibrate_workspace_bytes(M, K);
+}
+
+int svdq_calibrate_act_gscale(const void* x, const void* smooth, int64_t M, int64_t K, void* act_gscale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_mk(M, K, 0);
+  if (st) return st;
+  if (M == 0) return fail(SVDQ_ERR_SHAPE, "calibration needs at least one row");
+  if ((int64_t)M * K * 2 >= (int64_t(1) << 31))
+    return fail(SVDQ_ERR_UNSUPPORTED, "calibration batch above 2 GiB (M=%lld K=%lld)", (long long)M, (long long)K);
+  const char* names[] = {"x", "smooth", "act_gscale", "workspace"};
+  const void* ptrs[] = {x, smooth, act_gscale, workspace};
+  if ((st = check_ptrs(names, ptrs, 4))) return st;
+  const size_t need = svdq::calibrate_workspace_bytes(M, K);
+  if (workspace_bytes < need)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const Range in[] = {range("x", x, (size_t)M * K * 2), range("smooth", smooth, (size_t)K * 2)};
+  const Range out[] = {range("act_gscale", act_gscale, 2), range("workspace", workspace, need)};
+  if ((st = check_alias(in, 2, out, 2))) return st;
+  hipError_t e = svdq::launch_calibrate(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth), M, K,
+                                        static_cast<uint16_t*>(act_gscale), static_cast<float*>(workspace),
+                                        static_cast<hipStream_t>(stream));
+  if (int st_ = launched(e, "calibration", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }
 

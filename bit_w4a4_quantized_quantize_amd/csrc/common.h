@@ -67,9 +67,9 @@ __device__ __forceinline__ uint32_t block_scale_code(float amax) {
   return f32_to_e4m3_sat(amax * (1.0f / 6.0f));
 }
 
-// 1 / s_d for a decoded nonzero e4m3 scale (a normal fp32 in [2^-9, 448]):
-// hardware reciprocal plus one Newton step, within about 1 unit in the last
-// place, which the 21-bit rounding of the quotients (below) tolerates.
+// 1 / s for a positive normal fp32 s (a decoded nonzero e4m3 scale, possibly times a
+// global scale): hardware reciprocal plus one Newton step, within about 1 unit in
+// the last place, which the 21-bit rounding of the quotients (below) tolerates.
 __device__ __forceinline__ float scale_reciprocal(float sd) {
   const float r = __builtin_amdgcn_rcpf(sd);
   return __builtin_fmaf(__builtin_fmaf(-sd, r, 1.0f), r, r);
@@ -83,6 +83,34 @@ __device__ __forceinline__ float scale_reciprocal(float sd) {
 __device__ __forceinline__ float snap21(float q) {
   return __uint_as_float((__float_as_uint(q) + 4u) & ~7u);
 }
+
+// Per-block scale rule, dynamic or relative to a static global activation scale g
+// (a bf16 value: at most 8 significant bits, positive and normal).
+//  dynamic: s = e4m3(max|v| * RN(1/6)), divisor dec(s);
+//  static:  s = e4m3(round21(max|v| * r)) with r within about 1 unit of 1/(6 g),
+//           divisor dec(s) * g (exact: 4 + 8 significant bits).
+// Static exactness: max|v| (16 significant bits) against an e4m3 midpoint times
+// 6 g (5 + 10 bits) is either equal or at least 2^-17 (relative) apart, so the
+// product within 2 units of the quotient, rounded to 21 significant bits, lands
+// exactly on a tie and on the right side otherwise; the code quotient v / (dec(s)
+// g) keeps the same separation (3 + 12 bits against 16), as in the dynamic case.
+template <bool STATIC>
+struct BlockScale {
+  float g = 1.0f, r6g = 0.0f;
+  __device__ __forceinline__ void init(const uint16_t* gscale) {
+    if (STATIC) {
+      g = bf16lo_to_f32(gscale[0]);
+      r6g = scale_reciprocal(6.0f * g);
+    }
+  }
+  __device__ __forceinline__ uint32_t code(float amax) const {
+    return STATIC ? f32_to_e4m3_sat(snap21(amax * r6g)) : block_scale_code(amax);
+  }
+  __device__ __forceinline__ float divisor(uint32_t sc) const {
+    const float sd = e4m3_to_f32(sc, 0);
+    return STATIC ? sd * g : sd;
+  }
+};
 
 // Dequantise one dword of 8 E2M1 codes (low nibble first = lower k) times the
 // block scale `s` (an exactly representable f16) into 8 f16 values, exactly.

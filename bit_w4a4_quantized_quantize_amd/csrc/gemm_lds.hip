@@ -28,7 +28,8 @@
 // multiple of 8; the padding workgroups exit at once.
 //
 // Epilogue: wcscales and bias load while the last panel multiplies;
-// accumulators * wtscale * wcscales[n]; then lora_act @ proj_up^T as
+// accumulators * wtscale * wcscales[n] (times the static global activation
+// scale when the activations were quantised relative to one); then lora_act @ proj_up^T as
 // ceil(R/64) further panels of the same two-stage pipeline (bf16 matrix
 // instructions; each residual panel is copied into its stage by direct
 // global-to-LDS loads while the panel before it multiplies); then bias, then
@@ -213,6 +214,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
     }
   }
   const uint32_t wt_raw = a.wtscale[0];
+  const uint32_t gs_raw = a.act_gscale != nullptr ? (uint32_t)a.act_gscale[0] : 0x3F80u;   // bf16 1.0
 
   // The residual lora_act @ proj_up^T runs as ceil(R/64) more panels of the
   // same pipeline: residual panel p (R steps 4p .. 4p+3) is copied by direct
@@ -253,7 +255,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   }
 
   // ---- epilogue ----
-  const float wt = bf16lo_to_f32(wt_raw);
+  // a static global activation scale (bf16, like wtscale) multiplies in exactly
+  const float wt = bf16lo_to_f32(wt_raw) * bf16lo_to_f32(gs_raw);
   float alpha[TN], bias_v[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {

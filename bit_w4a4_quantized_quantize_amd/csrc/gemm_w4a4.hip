@@ -210,7 +210,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a4_kernel(GemmArgs a) {
   }
 
   // ---- epilogue: * wtscale * wcscales[n], + lora_act @ proj_up^T, + bias ----
-  const float wt = bf16lo_to_f32(a.wtscale[0]);
+  // a static global activation scale (bf16, like wtscale) multiplies in exactly
+  const float wt = bf16lo_to_f32(a.wtscale[0]) * (a.act_gscale != nullptr ? bf16lo_to_f32(a.act_gscale[0]) : 1.0f);
   int ncol[TN];
   float alpha[TN], bias_v[TN];
 #pragma unroll

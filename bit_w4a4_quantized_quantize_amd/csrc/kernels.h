@@ -25,8 +25,11 @@ inline hipError_t set_lds_limit_once(const void* kernel, int bytes, std::atomic<
 
 // a1: quant(x * smooth) -> qact [M, K/2], ascales [K/16, M] (canonical layout;
 // the work is laid out for HBM streaming).
+// gscale: NULL (dynamic scales) or the static global activation scale, bf16 [1] on
+// the device (block scales relative to it; see common.h, BlockScale).
 hipError_t launch_quant_act(const uint16_t* x, const uint16_t* smooth, uint8_t* qact,
-                            uint8_t* ascales, int64_t M, int64_t K, hipStream_t stream);
+                            uint8_t* ascales, int64_t M, int64_t K, hipStream_t stream,
+                            const uint16_t* gscale = nullptr);
 
 // a1 + a2 fused: one pass over x gives quant(x * smooth) and
 // lora_act [M, R] = bf16(x @ proj_down) (R may be 0). Output codes/scales in the
@@ -37,7 +40,15 @@ hipError_t launch_quant_act(const uint16_t* x, const uint16_t* smooth, uint8_t* 
 size_t quant_lora_workspace_bytes(int64_t M, int64_t K, int64_t R);
 hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down,
                              uint8_t* qact, uint8_t* ascales, uint16_t* lora_act, float* partial,
-                             int64_t M, int64_t K, int64_t R, bool packed_out, hipStream_t stream);
+                             int64_t M, int64_t K, int64_t R, bool packed_out, hipStream_t stream,
+                             const uint16_t* gscale = nullptr);
+
+// Calibration of the static global activation scale: gscale [1] bf16 =
+// bf16(max |x * smooth| / (6 * 448)), or 1 when that maximum is 0. workspace:
+// calibrate_workspace_bytes(M, K) bytes of per-workgroup maxima.
+size_t calibrate_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_calibrate(const uint16_t* x, const uint16_t* smooth, int64_t M, int64_t K, uint16_t* gscale,
+                            float* workspace, hipStream_t stream);
 
 // a4 + a5: scaled GEMM, low-rank up-projection and epilogue.
 struct GemmArgs {
@@ -54,6 +65,7 @@ struct GemmArgs {
   int64_t M, N, K, R;
   int packed;
   int64_t gated_f;          // 0, or F: N = 2F and y = silu(y[:, :F]) * y[:, F:] is [M, F]
+  const uint16_t* act_gscale = nullptr;  // static global activation scale bf16 [1], or NULL (= 1)
 };
 // canonical activations (LDS-staged), canonical or packed weights
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);

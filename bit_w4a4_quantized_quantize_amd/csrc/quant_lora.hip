@@ -70,14 +70,17 @@ struct QLArgs {
   int M, K, R;
   int r_base;          // first of the (up to kRChunk) lora_act columns this launch computes
   int split_steps;     // 32-wide K steps per split (blockIdx.y selects the split)
+  const uint16_t* gscale;  // static global activation scale bf16 [1] (STATIC kernels only)
 };
 
 // QUANT: write the codes and scales; LORA: compute lora_act columns
 // r_base .. r_base + kRChunk - 1. A rank above kRChunk takes further launches
 // with QUANT = false.
-template <int RT, bool PACKED, bool QUANT, bool LORA>
+template <int RT, bool PACKED, bool QUANT, bool LORA, bool STATIC = false>
 __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
   constexpr int ROWS = 16 * RT * kWaves;
+  BlockScale<STATIC> bs;
+  if (QUANT) bs.init(a.gscale);
   // B fragments of one step: [stage][fragment i][lane] x 16 bytes
   __shared__ __attribute__((aligned(16))) uint8_t s_frag[LORA ? 2 * 8 * 1024 : 16];
 
@@ -174,8 +177,8 @@ __global__ __launch_bounds__(64 * kWaves) void quant_lora_kernel(QLArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
         amax = fmaxf(amax, __shfl_xor(amax, 16));   // other half of the block
-        const uint32_t sc = block_scale_code(amax);
-        const float sd = e4m3_to_f32(sc, 0);
+        const uint32_t sc = bs.code(amax);
+        const float sd = bs.divisor(sc);
         const float inv = sd > 0.0f ? scale_reciprocal(sd) : 0.0f;
         uint32_t packed = 0u;
         packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, snap21(v[0] * inv), snap21(v[1] * inv), 1.0f, 0);
@@ -288,7 +291,7 @@ constexpr int kWsStage = kWsX + 64 * 256;    // + proj_down of one panel (64 k x
 typedef short v4s __attribute__((ext_vector_type(4)));
 #define WS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-template <bool PACKED>
+template <bool PACKED, bool STATIC = false>
 __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kWsStage];
 
@@ -369,6 +372,8 @@ __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
     for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(base + (256 * u + 64 * qw + lane) * 16) = P[u];
   };
 
+  BlockScale<STATIC> bs;
+  if (quantiser) bs.init(a.gscale);
   // quantise panel j from X (all four rows of the lane), store codes and scales
   auto quantise = [&](const u32x4 (&X)[5], int j) {
     const int p = p_begin + j;
@@ -396,8 +401,8 @@ __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
       // the other half of the block sits in lane ^ 1 (a DPP lane swap, no LDS round trip)
       amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, false)));
-      const uint32_t sc = block_scale_code(amax);
-      const float sd = e4m3_to_f32(sc, 0);
+      const uint32_t sc = bs.code(amax);
+      const float sd = bs.divisor(sc);
       const float inv = sd > 0.0f ? scale_reciprocal(sd) : 0.0f;
       uint32_t pk = 0u;
       pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(v[0] * inv), snap21(v[1] * inv), 1.0f, 0);
@@ -619,8 +624,10 @@ size_t quant_lora_workspace_bytes(int64_t M, int64_t K, int64_t R) {
 
 hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down,
                              uint8_t* qact, uint8_t* ascales, uint16_t* lora_act, float* partial,
-                             int64_t M, int64_t K, int64_t R, bool packed_out, hipStream_t stream) {
-  QLArgs a{x, smooth, proj_down, qact, ascales, lora_act, nullptr, (int)M, (int)K, (int)R, 0, 0};
+                             int64_t M, int64_t K, int64_t R, bool packed_out, hipStream_t stream,
+                             const uint16_t* gscale) {
+  QLArgs a{x, smooth, proj_down, qact, ascales, lora_act, nullptr, (int)M, (int)K, (int)R, 0, 0, gscale};
+  const bool st = gscale != nullptr;
   const int ks = k_splits(M, K, R, packed_out);
   const int steps = packed_out ? (int)(2 * ((K + 63) / 64)) : (int)((K + 31) / 32);
   a.split_steps = (steps + ks - 1) / ks;
@@ -633,8 +640,24 @@ hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const ui
       const int64_t KP = (K + 63) / 64;
       w.split_steps = (int)((KP + ks - 1) / ks);
       const dim3 wgrid((unsigned)((M + kWsRows - 1) / kWsRows), (unsigned)ks);
-      if (packed_out) hipLaunchKernelGGL((quant_lora_ws_kernel<true>), wgrid, dim3(512), 0, stream, w);
-      else hipLaunchKernelGGL((quant_lora_ws_kernel<false>), wgrid, dim3(512), 0, stream, w);
+      if (packed_out) {
+        if (st) hipLaunchKernelGGL((quant_lora_ws_kernel<true, true>), wgrid, dim3(512), 0, stream, w);
+        else hipLaunchKernelGGL((quant_lora_ws_kernel<true>), wgrid, dim3(512), 0, stream, w);
+      } else {
+        if (st) hipLaunchKernelGGL((quant_lora_ws_kernel<false, true>), wgrid, dim3(512), 0, stream, w);
+        else hipLaunchKernelGGL((quant_lora_ws_kernel<false>), wgrid, dim3(512), 0, stream, w);
+      }
+      return;
+    }
+    if (quant && st) {
+      // quantisation alone with a static scale (R = 0; the canonical layout without a
+      // down-projection goes to quant_act_kernel instead)
+      if (packed_out)
+        hipLaunchKernelGGL((quant_lora_kernel<kRowTiles, true, true, false, true>), grid, dim3(64 * kWaves), 0,
+                           stream, a);
+      else
+        hipLaunchKernelGGL((quant_lora_kernel<kRowTiles, false, true, false, true>), grid, dim3(64 * kWaves), 0,
+                           stream, a);
       return;
     }
 #define SVDQ_QL(RT, P, Q, L) hipLaunchKernelGGL((quant_lora_kernel<RT, P, Q, L>), grid, dim3(64 * kWaves), 0, stream, a)
@@ -666,7 +689,7 @@ hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const ui
 hipError_t launch_lowrank_down(const uint16_t* x, const uint16_t* proj_down, uint16_t* lora_act, float* partial,
                                int64_t M, int64_t K, int64_t R, hipStream_t stream) {
   if (R <= 0) return hipSuccess;
-  QLArgs a{x, nullptr, proj_down, nullptr, nullptr, lora_act, nullptr, (int)M, (int)K, (int)R, 0, 0};
+  QLArgs a{x, nullptr, proj_down, nullptr, nullptr, lora_act, nullptr, (int)M, (int)K, (int)R, 0, 0, nullptr};
   const int ks = k_splits(M, K, R, false);
   const int steps = (int)((K + 31) / 32);
   a.split_steps = (steps + ks - 1) / ks;

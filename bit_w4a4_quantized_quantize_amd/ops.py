@@ -86,6 +86,40 @@ def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=No
     workspace: optional uint8 device tensor of at least
     quantize_act_workspace_bytes(M, K, R) bytes (allocated here when None).
     """
+    return _quantize_act(x, smooth, None, proj_down, qact, ascales, lora_act, packed, workspace)
+
+
+def quantize_act_static(x, smooth, act_gscale, proj_down=None, qact=None, ascales=None, lora_act=None,
+                        packed=False, workspace=None):
+    """As quantize_act, with the block scales relative to the static global activation
+    scale act_gscale (bf16 [1] device tensor, e.g. from calibrate_act_gscale)."""
+    _need(act_gscale, "act_gscale", torch.bfloat16, shape=(1,))
+    return _quantize_act(x, smooth, act_gscale, proj_down, qact, ascales, lora_act, packed, workspace)
+
+
+def calibrate_act_gscale(x, smooth, act_gscale=None, workspace=None):
+    """Static global activation scale from a calibration batch x [M, K] (bf16):
+    bf16(max |x * smooth| / (6 * 448)), or 1 when that maximum is 0. Returns bf16 [1]."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    _k_ok(K)
+    _need(smooth, "smooth", torch.bfloat16, shape=(K,))
+    dev = x.device
+    if act_gscale is None:
+        act_gscale = torch.empty(1, dtype=torch.bfloat16, device=dev)
+    _need(act_gscale, "act_gscale", torch.bfloat16, shape=(1,))
+    L = _lib.lib()
+    nbytes = L.svdq_calibrate_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, min_numel=nbytes)
+    _devices(x=x, smooth=smooth, act_gscale=act_gscale, workspace=workspace)
+    _lib.check("svdq_calibrate_act_gscale", L.svdq_calibrate_act_gscale(
+        _p(x), _p(smooth), M, K, _p(act_gscale), _p(workspace), workspace.numel(), _stream(dev)))
+    return act_gscale
+
+
+def _quantize_act(x, smooth, act_gscale, proj_down, qact, ascales, lora_act, packed, workspace):
     _need(x, "x", torch.bfloat16, 2)
     M, K = x.shape
     _k_ok(K)
@@ -121,12 +155,16 @@ def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=No
     ws_bytes = 0
     if workspace is not None:
         ws_bytes = _need(workspace, "workspace", torch.uint8, 1, min_numel=ws_need).numel()
-    _devices(x=x, smooth=smooth, proj_down=proj_down, qact=qact, ascales=ascales, lora_act=lora_act,
-             workspace=workspace)
-    _lib.check("svdq_quantize_act", L.svdq_quantize_act(
-        _p(x), _p(smooth), M, K, _p(proj_down), R, ACT_PACKED if packed else ACT_CANONICAL,
-        _p(qact), _p(_bytes(ascales)) if ascales is not None else None, _p(lora_act) if R > 0 else None,
-        _p(workspace), ws_bytes, _stream(dev)))
+    _devices(x=x, smooth=smooth, act_gscale=act_gscale, proj_down=proj_down, qact=qact, ascales=ascales,
+             lora_act=lora_act, workspace=workspace)
+    layout = ACT_PACKED if packed else ACT_CANONICAL
+    rest = (_p(proj_down), R, layout, _p(qact), _p(_bytes(ascales)) if ascales is not None else None,
+            _p(lora_act) if R > 0 else None, _p(workspace), ws_bytes, _stream(dev))
+    if act_gscale is None:
+        _lib.check("svdq_quantize_act", L.svdq_quantize_act(_p(x), _p(smooth), M, K, *rest))
+    else:
+        _lib.check("svdq_quantize_act_static", L.svdq_quantize_act_static(_p(x), _p(smooth), _p(act_gscale), M, K,
+                                                                          *rest))
     return qact, ascales, (lora_act if R > 0 else None)
 
 
@@ -273,6 +311,16 @@ def linear_workspace_bytes(M, N, K, R):
 
 def linear_w4a4(x, w: SVDQLinearWeights, y=None, workspace=None):
     """The whole layer: y [M, N] bf16."""
+    return _linear(x, w, None, y, workspace)
+
+
+def linear_w4a4_static(x, w: SVDQLinearWeights, act_gscale, y=None, workspace=None):
+    """The whole layer with static activation scales relative to act_gscale (bf16 [1])."""
+    _need(act_gscale, "act_gscale", torch.bfloat16, shape=(1,))
+    return _linear(x, w, act_gscale, y, workspace)
+
+
+def _linear(x, w, act_gscale, y, workspace):
     dev = _check_layer(w)
     _need(x, "x", torch.bfloat16, 2)
     M, K = x.shape
@@ -287,13 +335,15 @@ def linear_w4a4(x, w: SVDQLinearWeights, y=None, workspace=None):
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, 1, min_numel=nbytes)
-    _devices(**_layer_tensors(w), x=x, y=y, workspace=workspace)
-    _lib.check("svdq_linear_w4a4", L.svdq_linear_w4a4(
-        _p(x), _p(w.smooth), _p(_bytes(w.weight)),
-        _p(_bytes(w.wscales)) if w.wscales is not None else None, w.layout,
-        _p(w.wcscales), _p(w.wtscale), _p(w.proj_down) if w.R > 0 else None,
-        _p(w.proj_up) if w.R > 0 else None, _p(w.bias), M, w.N, K, w.R,
-        _p(y), _p(workspace), workspace.numel(), _stream(x.device)))
+    _devices(**_layer_tensors(w), x=x, y=y, workspace=workspace, act_gscale=act_gscale)
+    rest = (_p(_bytes(w.weight)), _p(_bytes(w.wscales)) if w.wscales is not None else None, w.layout,
+            _p(w.wcscales), _p(w.wtscale), _p(w.proj_down) if w.R > 0 else None,
+            _p(w.proj_up) if w.R > 0 else None, _p(w.bias), M, w.N, K, w.R,
+            _p(y), _p(workspace), workspace.numel(), _stream(x.device))
+    if act_gscale is None:
+        _lib.check("svdq_linear_w4a4", L.svdq_linear_w4a4(_p(x), _p(w.smooth), *rest))
+    else:
+        _lib.check("svdq_linear_w4a4_static", L.svdq_linear_w4a4_static(_p(x), _p(w.smooth), _p(act_gscale), *rest))
     return y
 
 

@@ -191,6 +191,42 @@ int svdq_linear_w4a4(const void* x, const void* smooth,
                      void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Static (calibrated) activation scales: the NVFP4 datatype-variant row's second
+ * half. The blog page "Z-Image NVFP4 ..." says the Comfy-Org Z-Image Turbo NVFP4
+ * checkpoint uses calibrated static activation scales; the pages give no rule.
+ * Reading (NVFP4's two-level form): a per-tensor global activation scale g, fixed
+ * offline from calibration activations, and per-16 e4m3 block scales still
+ * computed per call relative to it:
+ *   s = e4m3(max|v| / (6 g)) (nearest even, saturating at 448) -> ascales,
+ *   codes = E2M1 nearest even of |v| / (dec(s) * g), sign of v kept,
+ * with v = x * smooth in fp32. The GEMM's main term then carries g:
+ *   y = bf16( scaled_mma(...) * g * wtscale * wcscales[n] + lora_act @ proj_up^T + bias[n] ).
+ * g = 1 gives the dynamic rule exactly. Blocks above 6 * 448 * g saturate.
+ *
+ *   act_gscale: bf16 [1] on the device, a positive normal value in [2^-64, 2^64]
+ *     (outside that the results are unspecified); bf16 precision keeps every
+ *     rounding decision exact in fp32.
+ * svdq_calibrate_act_gscale: act_gscale = bf16(max |x * smooth| / (6 * 448)) over
+ *   a calibration batch x [M, K] (M >= 1), or 1 when that maximum is 0; workspace
+ *   of svdq_calibrate_workspace_bytes(M, K) bytes; x below 2 GiB.
+ * svdq_quantize_act_static, svdq_linear_w4a4_static: as svdq_quantize_act and
+ *   svdq_linear_w4a4 with the block scales relative to *act_gscale (same
+ *   layouts, workspace sizes and errors; act_gscale NULL is SVDQ_ERR_NULL).
+ */
+size_t svdq_calibrate_workspace_bytes(int64_t M, int64_t K);
+int svdq_calibrate_act_gscale(const void* x, const void* smooth, int64_t M, int64_t K, void* act_gscale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int svdq_quantize_act_static(const void* x, const void* smooth, const void* act_gscale, int64_t M, int64_t K,
+                             const void* proj_down, int64_t R, int act_layout, void* qact, void* ascales,
+                             void* lora_act, void* workspace, size_t workspace_bytes, void* stream);
+int svdq_linear_w4a4_static(const void* x, const void* smooth, const void* act_gscale,
+                            const void* weight, const void* wscales, int weight_layout,
+                            const void* wcscales, const void* wtscale,
+                            const void* proj_down, const void* proj_up, const void* bias,
+                            int64_t M, int64_t N, int64_t K, int64_t R,
+                            void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The whole layer without allocation, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, and harnesses that
  * forbid allocation. Same arguments and results as svdq_linear_w4a4 (bit for
