@@ -670,10 +670,42 @@ def run_ffn_block(args):
         h = torch.nn.functional.silu(y[:, :F_out].float()).mul_(y[:, F_out:].float()).to(torch.bfloat16)
         ops.linear_w4a4(h, b["layer"], y=b["y"], workspace=b["ws"])
 
+    # the block with w2's input quantised in the gated epilogue: quantise x (+ down), the gated
+    # GEMM that also writes w2's packed codes, w2's down-projection alone, w2's GEMM
+    q13 = [torch.empty(ops._lib.lib().svdq_packed_act_bytes(M, K), dtype=torch.uint8, device=dev)
+           for _ in range(n_sets)]
+    l13 = [torch.empty((M, R), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    q2 = [torch.empty(ops._lib.lib().svdq_packed_act_bytes(M, F_out), dtype=torch.uint8, device=dev)
+          for _ in range(n_sets)]
+    l2 = [torch.empty((M, R), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    qws = torch.empty(max(1, ops.quantize_act_workspace_bytes(M, K, R), ops.quantize_act_workspace_bytes(M, F_out, R)),
+                      dtype=torch.uint8, device=dev)
+
+    def fused(i):
+        a, b = sets13[i], sets2[i]
+        ops.quantize_act(a["x"], a["layer"].smooth, a["layer"].proj_down, qact=q13[i], lora_act=l13[i], packed=True,
+                         workspace=qws)
+        ops.gemm_w4a4_gated_quant(q13[i], l13[i], a["layer"], M, b["layer"].smooth, h=hs[i], next_qact=q2[i])
+        ops.lowrank_down(hs[i], b["layer"].proj_down, lora_act=l2[i], workspace=qws)
+        ops.gemm_w4a4(q2[i], None, l2[i], b["layer"], y=b["y"], M=M)
+
+    def gated_quant_gemm(i):
+        a, b = sets13[i], sets2[i]
+        ops.gemm_w4a4_gated_quant(q13[i], l13[i], a["layer"], M, b["layer"].smooth, h=hs[i], next_qact=q2[i])
+
+    def w2_down(i):
+        ops.lowrank_down(hs[i], sets2[i]["layer"].proj_down, lora_act=l2[i], workspace=qws)
+
     kw = max(1, args.warmup // 2)
+    fused_ms = time_loop(fused, n_sets, max(10, args.kernel_iters // 4), kw, stream)
+    gq_ms = time_loop(gated_quant_gemm, n_sets, max(10, args.kernel_iters // 4), kw, stream)
+    w2d_ms = time_loop(w2_down, n_sets, args.kernel_iters, kw, stream)
     gated_ms = time_loop(gated_gemm, n_sets, args.kernel_iters, kw, stream)
     w2_ms = time_loop(w2_layer, n_sets, args.kernel_iters, kw, stream)
     unfused_ms = time_loop(unfused, n_sets, max(10, args.kernel_iters // 4), kw, stream)
+    print(f"[bench] block with w2's input quantised in the gated epilogue: {fused_ms * 1e3:.1f} us "
+          f"(that gated GEMM {gq_ms * 1e3:.1f} us, w2 down-projection alone {w2d_ms * 1e3:.1f} us)",
+          file=sys.stderr, flush=True)
     gated_tflops = flops_gated_gemm / (gated_ms * 1e-3) / 1e12
     print(f"[bench] gated GEMM {gated_ms * 1e3:.1f} us ({gated_tflops:.1f} TFLOP/s), w2 layer {w2_ms * 1e3:.1f} us, "
           f"unfused block {unfused_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
@@ -710,6 +742,9 @@ def run_ffn_block(args):
         },
         "w2_layer_us": round(w2_ms * 1e3, 2),
         "unfused_block_us": round(unfused_ms * 1e3, 2),
+        "block_with_quantising_gate_us": round(fused_ms * 1e3, 2),
+        "quantising_gated_gemm_us": round(gq_ms * 1e3, 2),
+        "w2_down_projection_alone_us": round(w2d_ms * 1e3, 2),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the same block", file=sys.stderr, flush=True)

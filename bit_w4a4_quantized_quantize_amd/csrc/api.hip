@@ -598,6 +598,79 @@ int svdq_gemm_w4a4_gated(const void* qact, const void* lora_act, const void* wei
   return ok();
 }
 
+int svdq_gemm_w4a4_gated_quant(const void* qact, const void* lora_act, const void* weight,
+                               const void* wcscales, const void* wtscale, const void* proj_up,
+                               const void* bias, int64_t M, int64_t F, int64_t K, int64_t R, void* h,
+                               const void* next_smooth, void* next_qact, size_t next_qact_bytes, void* stream) {
+  int st = check_mk(M, K, R);
+  if (st) return st;
+  if ((st = check_gated_f(F))) return st;
+  if (F % 64 != 0)
+    return fail(SVDQ_ERR_UNSUPPORTED, "F = %lld: quantising h for the next layer needs F to be a multiple of 64",
+                (long long)F);
+  const int64_t N = 2 * F;
+  if ((st = check_nk(N, K))) return st;
+  if ((st = check_packed_gemm_sizes(M, N, K))) return st;
+  if ((st = check_rsrc_sizes(M, F, 0))) return st;
+  if (M == 0 || F == 0) return ok();
+  if ((st = validate_gemm(qact, nullptr, SVDQ_ACT_PACKED, lora_act, weight, nullptr, SVDQ_WEIGHT_PACKED,
+                          wcscales, wtscale, proj_up, bias, M, N, K, R, h, true)))
+    return st;
+  {
+    const char* names[] = {"next_smooth", "next_qact"};
+    const void* ptrs[] = {next_smooth, next_qact};
+    if ((st = check_ptrs(names, ptrs, 2))) return st;
+  }
+  const size_t q2 = svdq::packed_weight_bytes(M, F);
+  if (next_qact_bytes < q2)
+    return fail(SVDQ_ERR_WORKSPACE, "next_qact has %zu bytes, %zu needed", next_qact_bytes, q2);
+  const Range in[] = {range("qact", qact, svdq::packed_weight_bytes(M, K)),
+                      range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
+                      range("weight", weight, svdq::packed_weight_bytes(N, K)),
+                      range("wcscales", wcscales, (size_t)N * 2),
+                      range("wtscale", wtscale, 2),
+                      range("proj_up", R > 0 ? proj_up : nullptr, (size_t)N * R * 2),
+                      range("bias", bias, (size_t)N * 2),
+                      range("next_smooth", next_smooth, (size_t)F * 2)};
+  const Range out[] = {range("h", h, (size_t)M * F * 2), range("next_qact", next_qact, q2)};
+  if ((st = check_alias(in, 8, out, 2))) return st;
+  svdq::GemmArgs a = gated_args(qact, lora_act, weight, wcscales, wtscale, proj_up, bias, M, F, K, R, h);
+  a.next_smooth = static_cast<const uint16_t*>(next_smooth);
+  a.next_qact = static_cast<uint8_t*>(next_qact);
+  hipError_t e = svdq::launch_gemm_lds(a, static_cast<hipStream_t>(stream));
+  if (int st_ = launched(e, "gemm", static_cast<hipStream_t>(stream))) return st_;
+  return ok();
+}
+
+int svdq_lowrank_down(const void* x, const void* proj_down, int64_t M, int64_t K, int64_t R, void* lora_act,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_mk(M, K, R);
+  if (st) return st;
+  if ((st = check_rsrc_sizes(M, K, R))) return st;
+  if (M == 0 || R == 0) return ok();
+  const char* names[] = {"x", "proj_down", "lora_act"};
+  const void* ptrs[] = {x, proj_down, lora_act};
+  if ((st = check_ptrs(names, ptrs, 3))) return st;
+  const size_t ws_need = quant_ws_bytes(M, K, R);
+  if (ws_need > 0) {
+    if (workspace_bytes < ws_need)
+      return fail(SVDQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws_need);
+    const char* wn[] = {"workspace"};
+    const void* wp[] = {workspace};
+    if ((st = check_ptrs(wn, wp, 1))) return st;
+  }
+  const Range in[] = {range("x", x, (size_t)M * K * 2), range("proj_down", proj_down, (size_t)K * R * 2)};
+  const Range out[] = {range("lora_act", lora_act, (size_t)M * R * 2),
+                       range("workspace", ws_need > 0 ? workspace : nullptr, ws_need)};
+  if ((st = check_alias(in, 2, out, 2))) return st;
+  hipError_t e = svdq::launch_lowrank_down(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(proj_down),
+                                           static_cast<uint16_t*>(lora_act),
+                                           ws_need > 0 ? static_cast<float*>(workspace) : nullptr, M, K, R,
+                                           static_cast<hipStream_t>(stream));
+  if (int st_ = launched(e, "down-projection", static_cast<hipStream_t>(stream))) return st_;
+  return ok();
+}
+
 size_t svdq_linear_gated_workspace_bytes(int64_t M, int64_t F, int64_t K, int64_t R) {
   (void)F;
   if (M <= 0 || K <= 0 || K % 16 != 0 || R < 0) return 0;

@@ -65,10 +65,19 @@ struct LdsCfg {
 // workgroup's two wave columns compute matching column ranges of the two
 // halves (wave_n = 0: channels c, wave_n = 1: channels F + c), and the output
 // is h[:, c] = silu(y[:, c]) * y[:, F + c], [M, F] bf16.
-template <int WM, int WN, int TM, int TN, bool GATED>
+//
+// Q2 (gated only): the writer waves also quantise h for the next layer, w2,
+// whose input h is: per row and 16-block of h's columns, v = h * next_smooth
+// with the activation rule of the quantiser kernels, codes and e4m3 scales
+// into next_qact in the packed activation layout (rows = tokens, K = F). A
+// 16-block is two 8-column pieces held by an even lane and the next one in the
+// store loop below, so the block maximum takes one lane swap; an output tile
+// holds whole blocks (its width is a multiple of 32 columns).
+template <int WM, int WN, int TM, int TN, bool GATED, bool Q2 = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   using C = LdsCfg<WM, WN, TM, TN>;
   static_assert(!GATED || WN == 2, "the gated epilogue pairs the two wave columns");
+  static_assert(!Q2 || (GATED && (32 * (32 * TN / 8)) % 64 == 0), "Q2: whole 16-blocks in lane pairs");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -304,6 +313,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   uint16_t* stage_out = reinterpret_cast<uint16_t*>(smem + kXBytes + (GATED ? wave_m : wave) * (32 * kCols * 2));
   f32x16* xchg = reinterpret_cast<f32x16*>(smem) + wave_m * TN * 64;
   const bool vec_ok = (FO % 8) == 0;
+  // Q2: w2's packed activation buffer ([M, F], K = F a multiple of 64) and smooth
+  const uint32_t q2_code_bytes = Q2 ? (uint32_t)(FO / 64) * MP * 1024 : 0u;
+  const __amdgpu_buffer_rsrc_t rq2 = make_rsrc(a.next_qact, Q2 ? q2_code_bytes + (uint32_t)(FO / 64) * MP * 128 : 0u);
+  const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(a.next_smooth, Q2 ? (uint32_t)FO * 2 : 0u);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     if (GATED) {
@@ -341,14 +354,48 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
           const int row = idx / kPieces, piece = idx % kPieces;
           const int m = m_w + 32 * i + row;
           const int n = n_w + 8 * piece;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + row * kCols + 8 * piece);
           if (m < M && n < FO) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(stage_out + row * kCols + 8 * piece);
             uint16_t* dst = a.y + (size_t)m * FO + n;
             if (vec_ok && n + 8 <= FO) {
               *reinterpret_cast<u32x4*>(dst) = v;
             } else {
               for (int e = 0; e < 8 && n + e < FO; ++e) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
             }
+          }
+          if (Q2) {
+            // this lane's 8 columns are half of the 16-block n & ~15; every lane of the
+            // wave is here (whole pieces per iteration), so the lane swap is complete
+            const bool n_in = n < FO;
+            const u32x4 smv = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs2, n_in ? (uint32_t)n * 2 : 0x80000000u, 0, 0));
+            float q[8];
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              q[2 * e] = bf16lo_to_f32(v[e]) * bf16lo_to_f32(smv[e]);
+              q[2 * e + 1] = bf16hi_to_f32(v[e]) * bf16hi_to_f32(smv[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(q[e]));
+            amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, false)));
+            const uint32_t sc = block_scale_code(amax);
+            const float sd = e4m3_to_f32(sc, 0);
+            const float inv = sd > 0.0f ? scale_reciprocal(sd) : 0.0f;
+            uint32_t pk = 0u;
+            pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(q[0] * inv), snap21(q[1] * inv), 1.0f, 0);
+            pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(q[2] * inv), snap21(q[3] * inv), 1.0f, 1);
+            pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(q[4] * inv), snap21(q[5] * inv), 1.0f, 2);
+            pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(q[6] * inv), snap21(q[7] * inv), 1.0f, 3);
+            // packed activation layout of [M, F]: chunk (n / 64, m / 32), dword (hh * 32 + c) * 4 + t
+            const int mq = m >> 5, c = m & 31, pp = n >> 6, t = (n >> 4) & 3, hh = (n >> 3) & 1;
+            const bool ok = n_in && mq < MP;
+            const uint32_t chunk = (uint32_t)pp * MP + mq;
+            __builtin_amdgcn_raw_buffer_store_b32(pk, rq2, ok ? chunk * 1024 + ((hh * 32 + c) * 4 + t) * 4 : 0x80000000u,
+                                                  0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rq2,
+                                                 ok && hh == 0 ? q2_code_bytes + chunk * 128 + c * 4 + t : 0x80000000u,
+                                                 0, 0);
           }
         }
       }
@@ -357,18 +404,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   }
 }
 
-template <int WM, int WN, int TM, int TN, bool GATED>
+template <int WM, int WN, int TM, int TN, bool GATED, bool Q2 = false>
 hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
   using C = LdsCfg<WM, WN, TM, TN>;
   const int64_t col_tiles = GATED ? ((a.gated_f + 31) / 32 + TN - 1) / TN : (a.N + C::BN - 1) / C::BN;
   const int64_t tiles = col_tiles * ((a.M + C::BM - 1) / C::BM);
   const unsigned lds = 2 * C::kStageBytes;
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN, GATED>),
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN, GATED, Q2>),
                                     (int)lds, lds_set);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((gemm_lds_kernel<WM, WN, TM, TN, GATED>), grid, dim3(C::kThreads), lds, stream, a);
+  hipLaunchKernelGGL((gemm_lds_kernel<WM, WN, TM, TN, GATED, Q2>), grid, dim3(C::kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -390,8 +437,10 @@ hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream) {
   const double cost320 = (double)((tiles320 + 255) / 256);
   const double cost256 = 0.82 * (double)((tiles256 + 255) / 256);
   if (gated) {
-    if (cost256 < cost320) return launch_lds_cfg<4, 2, 2, 4, true>(a, stream);
-    return launch_lds_cfg<4, 2, 2, 5, true>(a, stream);
+    const bool q2 = a.next_qact != nullptr;
+    if (cost256 < cost320)
+      return q2 ? launch_lds_cfg<4, 2, 2, 4, true, true>(a, stream) : launch_lds_cfg<4, 2, 2, 4, true>(a, stream);
+    return q2 ? launch_lds_cfg<4, 2, 2, 5, true, true>(a, stream) : launch_lds_cfg<4, 2, 2, 5, true>(a, stream);
   }
   if (cost256 < cost320) return launch_lds_cfg<4, 2, 2, 4, false>(a, stream);
   return launch_lds_cfg<4, 2, 2, 5, false>(a, stream);

@@ -66,6 +66,10 @@ struct GemmArgs {
   int packed;
   int64_t gated_f;          // 0, or F: N = 2F and y = silu(y[:, :F]) * y[:, F:] is [M, F]
   const uint16_t* act_gscale = nullptr;  // static global activation scale bf16 [1], or NULL (= 1)
+  // gated only: also quantise h for the next layer (w2), whose smooth is next_smooth [F],
+  // into next_qact, the packed activation layout of [M, F] (F % 64 == 0), or NULL
+  const uint16_t* next_smooth = nullptr;
+  uint8_t* next_qact = nullptr;
 };
 // canonical activations (LDS-staged), canonical or packed weights
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);

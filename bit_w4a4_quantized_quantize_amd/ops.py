@@ -400,6 +400,57 @@ def gemm_w4a4_gated(qact, lora_act, w: SVDQLinearWeights, M, h=None):
     return h
 
 
+def gemm_w4a4_gated_quant(qact, lora_act, w: SVDQLinearWeights, M, next_smooth, h=None, next_qact=None):
+    """Gated FFN step from packed activations that also quantises h for the next layer
+    (w2) with w2's smooth factor: returns (h [M, F] bf16, next_qact packed uint8 buffer of
+    the [M, F] activation, as quantize_act(h, next_smooth, packed=True) would give)."""
+    F_out = _check_gated(w)
+    dev = w.weight.device
+    L = _lib.lib()
+    _need(qact, "qact (packed)", torch.uint8, 1, min_numel=L.svdq_packed_act_bytes(M, w.K))
+    if w.R > 0:
+        _need(lora_act, "lora_act", torch.bfloat16, shape=(M, w.R))
+    _need(next_smooth, "next_smooth", torch.bfloat16, shape=(F_out,))
+    if h is None:
+        h = torch.empty((M, F_out), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, shape=(M, F_out))
+    nbytes = L.svdq_packed_act_bytes(M, F_out)
+    if next_qact is None:
+        next_qact = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _need(next_qact, "next_qact", torch.uint8, 1, min_numel=nbytes)
+    _devices(**_layer_tensors(w), qact=qact, lora_act=lora_act, h=h, next_smooth=next_smooth, next_qact=next_qact)
+    _lib.check("svdq_gemm_w4a4_gated_quant", L.svdq_gemm_w4a4_gated_quant(
+        _p(qact), _p(lora_act) if w.R > 0 else None, _p(_bytes(w.weight)), _p(w.wcscales), _p(w.wtscale),
+        _p(w.proj_up) if w.R > 0 else None, _p(w.bias), M, F_out, w.K, w.R, _p(h), _p(next_smooth),
+        _p(next_qact), next_qact.numel(), _stream(dev)))
+    return h, next_qact
+
+
+def lowrank_down(x, proj_down, lora_act=None, workspace=None):
+    """lora_act [M, R] = bf16(x @ proj_down) alone (x [M, K], proj_down [K, R], bf16)."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    _k_ok(K)
+    _need(proj_down, "proj_down", torch.bfloat16, 2)
+    R = proj_down.shape[1]
+    _need(proj_down, "proj_down", torch.bfloat16, shape=(K, R))
+    dev = x.device
+    if lora_act is None:
+        lora_act = torch.empty((M, R), dtype=torch.bfloat16, device=dev)
+    _need(lora_act, "lora_act", torch.bfloat16, shape=(M, R))
+    need = quantize_act_workspace_bytes(M, K, R)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0
+    if workspace is not None:
+        ws_bytes = _need(workspace, "workspace", torch.uint8, 1, min_numel=need).numel()
+    _devices(x=x, proj_down=proj_down, lora_act=lora_act, workspace=workspace)
+    L = _lib.lib()
+    _lib.check("svdq_lowrank_down", L.svdq_lowrank_down(_p(x), _p(proj_down), M, K, R, _p(lora_act),
+                                                         _p(workspace), ws_bytes, _stream(dev)))
+    return lora_act
+
+
 def linear_w4a4_gated(x, w: SVDQLinearWeights, h=None, workspace=None):
     """The whole gated step from x: h [M, F] bf16 (w is the 2F-channel w1/w3 layer)."""
     F_out = _check_gated(w)

@@ -275,6 +275,30 @@ int svdq_linear_w4a4_gated(const void* x, const void* smooth, const void* weight
                            int64_t R, void* h, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The gated step that also prepares w2's input (the rest of the FFN neighbour
+ * fusion): as svdq_gemm_w4a4_gated, and the epilogue additionally quantises the
+ * bf16 h it writes with w2's smooth factor, by the activation rule of the file
+ * header, into next_qact: the packed activation layout of an [M, F] activation
+ * (SVDQ_ACT_PACKED, svdq_packed_act_bytes(M, F) bytes), ready for
+ * svdq_gemm_w4a4 with w2's packed weight. Each output tile of the gated GEMM
+ * holds whole 16-blocks of h's rows, so this is local to the tile; w2's
+ * down-projection h @ proj_down2 needs whole rows of h and is left to
+ * svdq_lowrank_down. F must be a multiple of 64 (SVDQ_ERR_UNSUPPORTED).
+ *   next_smooth [F] bf16 (w2's smooth_factor); next_qact must not overlap any input or h.
+ * The codes and scales equal svdq_quantize_act(h, next_smooth) bit for bit.
+ *
+ * svdq_lowrank_down: lora_act [M, R] = bf16(x @ proj_down) alone (fp32
+ * accumulation), x [M, K] bf16, proj_down [K, R] bf16, with a workspace of
+ * svdq_quantize_act_workspace_bytes(M, K, R) bytes (fp32 K-split partial sums).
+ */
+int svdq_gemm_w4a4_gated_quant(const void* qact, const void* lora_act, const void* weight,
+                               const void* wcscales, const void* wtscale, const void* proj_up,
+                               const void* bias, int64_t M, int64_t F, int64_t K, int64_t R, void* h,
+                               const void* next_smooth, void* next_qact, size_t next_qact_bytes, void* stream);
+int svdq_lowrank_down(const void* x, const void* proj_down, int64_t M, int64_t K, int64_t R, void* lora_act,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Linears kept in bf16. A mixed-precision NVFP4 model leaves some linears
  * unquantised (blog page "Z-Image NVFP4 ...", variant table: the "Ultra"
  * variant keeps attention qkv/out and every linear of blocks 0-4 and 25-29 in
