@@ -1,15 +1,19 @@
 """The library's launches under HIP graph capture (torch.cuda.graph): a captured
 forward of one bf16 linear and one packed W4A4 linear is replayed several times,
 with eager work and synchronisations in between, and every replay must equal the
-eager results bit for bit. The entry points make no allocation and no attribute
-call while capturing once the kernels have run eagerly."""
+eager results bit for bit; the replayed outputs are also checked against the
+oracle (the bf16 layer's per-element bound and the W4A4 layer's 5e-3 gate). The
+entry points make no allocation and no attribute call while capturing once the
+kernels have run eagerly."""
 
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from tests.gpu_util import dev_bf16, make_layer
+from oracle import formats as F
+from oracle import svdq as S
+from tests.gpu_util import dev_bf16, host_bits, make_layer, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -52,5 +56,12 @@ def test_graph_replays_match_eager(gpu_lib):
         torch.cuda.synchronize()
         assert torch.equal(y_bf.view(torch.int16), ref_bf.view(torch.int16)), f"bf16 output, replay {rep}"
         assert torch.equal(y_q.view(torch.int16), ref_q.view(torch.int16)), f"W4A4 output, replay {rep}"
-    # the eager result is still the oracle-checked one
-    assert np.isfinite(ref_bf.float().cpu().numpy()).all()
+    # the replayed outputs against the oracle
+    y64_bf, _ = S.linear_bf16(d_bf["x"], d_bf["W"], d_bf["bias"])
+    got_bf = F.bf16_to_f64(host_bits(y_bf))
+    xa, wa = np.abs(F.bf16_to_f64(d_bf["x"])), np.abs(F.bf16_to_f64(d_bf["W"]))
+    bound = ulp_bf16(y64_bf) + 2 * (256 + 2) * 2.0 ** -24 * (xa @ wa.T + np.abs(F.bf16_to_f64(d_bf["bias"])))
+    assert np.all(np.abs(got_bf - y64_bf) <= bound), "bf16 replay beyond the oracle bound"
+    y64_q, _, _, _ = S.linear_w4a4(d_q["x"], d_q["smooth"], d_q["qweight"], d_q["wscales"], d_q["wcscales"],
+                                   d_q["wtscale"], d_q["proj_down"], d_q["proj_up"], d_q["bias"])
+    assert S.normwise_rel_err(F.bf16_to_f64(host_bits(y_q)), y64_q) <= 5e-3
