@@ -441,7 +441,22 @@ def timed(fn, n_sets, iters, stream, warmup=0, min_ms=30.0):
     """Average ms per call of fn(set_index) over `iters` calls on `stream`: conditioning by
     time, `warmup` more untimed calls, a host synchronisation, about 1 ms of untimed calls
     queued ahead of the start event (so the timed calls start on a busy device), then HIP
-    events around exactly `iters` calls. Returns (ms per call, info)."""
+    events around exactly `iters` calls. Python's cyclic garbage collector is run once
+    beforehand and kept off until the end (as timeit does): a full collection in the middle
+    of the timed calls stops the host for tens of milliseconds, and the device then idles.
+    Returns (ms per call, info)."""
+    import gc
+    gc_on = gc.isenabled()
+    gc.collect()
+    gc.disable()
+    try:
+        return _timed(fn, n_sets, iters, stream, warmup, min_ms)
+    finally:
+        if gc_on:
+            gc.enable()
+
+
+def _timed(fn, n_sets, iters, stream, warmup, min_ms):
     import torch
     cond_ms, cond_calls, windows = condition(fn, n_sets, stream, min_ms=min_ms)
     for i in range(warmup):
