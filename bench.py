@@ -771,12 +771,14 @@ def run_ffn_block(args):
     print(json.dumps(result), flush=True)
 
 
-def sweep_build(dev, n_fwd):
+def sweep_build(dev, n_fwd, keep_prequant=False):
     """Weights of the sweep's 150 linears and fresh activations for n_fwd forwards, drawn on
     the device (torch's generator, seeded per layer / per (forward, layer)) with the
     distributions of the seeded host recipe: x ~ N(0,1) with 1% outlier channels x20 (fixed
     per layer), W ~ N(0, 0.02), proj ~ N(0, 0.02), bias ~ N(0, 0.01); the NVFP4 weights come
-    from the library's own quantiser as in make_sets."""
+    from the library's own quantiser as in make_sets. With keep_prequant, each W4A4 entry
+    also keeps "Wp", the bf16 weight W / (wtscale * wcscales) before quantisation (so that a
+    check can quantise it independently)."""
     import torch
 
     import workloads
@@ -806,6 +808,8 @@ def sweep_build(dev, n_fwd):
             Wp = (W / (wt.float() * wc.float())[:, None]).to(bf)
             del W
             qw, ws, _ = ops.quantize_act(Wp, torch.ones(K, dtype=bf, device=dev))
+            if keep_prequant:
+                e["Wp"] = Wp
             del Wp
             pd = (torch.randn(K, R, generator=g, device=dev) * 0.02).to(bf)
             pu = (torch.randn(N, R, generator=g, device=dev) * 0.02).to(bf)
