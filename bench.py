@@ -935,23 +935,13 @@ def run_sweep(args):
           f"(wall {wall:.2f} s)", file=sys.stderr, flush=True)
 
     # split: the bf16 layers alone and the W4A4 layers alone (eager), and eager whole forwards
-    def timed(fn, n):
-        for i in range(min(n, n_fwd)):
-            fn(i)
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(n):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
+    def split_timed(fn, n):
+        return timed(fn, n_fwd, n, stream, min_ms=10.0)[0]
 
     n_part = max(2, min(args.steps, n_fwd))
-    bf_ms = timed(lambda i: forward(i % n_fwd, ("bf16",)), n_part)
-    q_ms = timed(lambda i: forward(i % n_fwd, ("w4a4",)), n_part)
-    eager_ms = timed(lambda i: forward(i % n_fwd), n_part)
+    bf_ms = split_timed(lambda i: forward(i % n_fwd, ("bf16",)), n_part)
+    q_ms = split_timed(lambda i: forward(i % n_fwd, ("w4a4",)), n_part)
+    eager_ms = split_timed(lambda i: forward(i % n_fwd), n_part)
     bf_tflops = flops_bf / (bf_ms * 1e-3) / 1e12
     q_tflops = flops_q / (q_ms * 1e-3) / 1e12
     print(f"[bench] bf16 layers {bf_ms:.2f} ms ({bf_tflops:.1f} TFLOP/s), W4A4 layers {q_ms:.2f} ms "
@@ -974,7 +964,7 @@ def run_sweep(args):
                 ops.quantize_act(acts[f][li], e["layer"].smooth, e["layer"].proj_down, qact=qa, lora_act=lo,
                                  packed=True, workspace=qws)
 
-    quant_ms = timed(lambda i: quant_fwd(i % n_fwd), n_part)
+    quant_ms = split_timed(lambda i: quant_fwd(i % n_fwd), n_part)
     qbytes = sum(2 * M * e["K"] + 2 * e["K"] + 2 * e["K"] * R + M * e["K"] // 2 + M * e["K"] // 16 + 2 * M * R
                  for e in built if e["precision"] == "w4a4")
     quant_gbs = qbytes / (quant_ms * 1e-3) / 1e9
@@ -987,8 +977,8 @@ def run_sweep(args):
         e = next(e for e in built if e["name"] == name and e["precision"] == "bf16")
         li = built.index(e)
         xs = [acts[f][li] for f in range(n_fwd)]
-        ours = timed(lambda i: ops.linear_bf16(xs[i % n_fwd], e["W"], e["b"], y=ys[name]), 20)
-        ref = timed(lambda i: torch.nn.functional.linear(xs[i % n_fwd], e["W"], e["b"]), 20)
+        ours = split_timed(lambda i: ops.linear_bf16(xs[i % n_fwd], e["W"], e["b"], y=ys[name]), 20)
+        ref = split_timed(lambda i: torch.nn.functional.linear(xs[i % n_fwd], e["W"], e["b"]), 20)
         fl = 2 * M * K * N
         shapes[name] = {"K": K, "N": N, "us": round(ours * 1e3, 1), "TFLOPs": round(fl / (ours * 1e-3) / 1e12, 1),
                         "torch_linear_us": round(ref * 1e3, 1)}

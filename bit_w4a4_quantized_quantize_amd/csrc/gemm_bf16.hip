@@ -86,9 +86,18 @@ struct Bf16Cfg {
   static constexpr int kLdsBytes = S * kStageBytes > kOutBytes ? S * kStageBytes : kOutBytes;
 };
 
-template <int WM, int WN, int TM, int TN, int TS, int S>
+// PIPE: the software-pipelined loop (two LDS stages of 64-K panels only). Each 16-K
+// step issues the next step's fragment reads between its own matrix instructions, one
+// read after each of the first TM + TN, into a second register set; the panel barrier
+// sits before the last step, whose instructions then cover the first reads of the next
+// panel. Without the ordering hints the compiler issues each step's reads after the
+// previous step's matrix instructions and waits for them at once, and the matrix pipe
+// idles for about one LDS round trip per step. It needs 2 * (TM + TN) fragment
+// registers, which fits 2 x 4 tiles per wave but not 2 x 5.
+template <int WM, int WN, int TM, int TN, int TS, int S, bool PIPE>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs a) {
   using C = Bf16Cfg<WM, WN, TM, TN, TS, S>;
+  static_assert(!PIPE || (S == 2 && TS == 4), "pipelined loop: two stages of 64-K panels");
   static_assert(S >= 2 && (S - 2) * C::kPerWave * C::kCopies < 64, "stage count");
   static_assert(TS == 2 || TS == 4, "panel depth");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -218,6 +227,62 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs a)
 #pragma unroll
   for (int t = 0; t < TS; ++t) frag_off[t] = l32 * C::kPanelK * 2 + (((2 * t + h) ^ C::swz(l32)) * 16);
 
+  if constexpr (PIPE) {
+    bf16x8 fr[2][TM + TN];
+    auto read_set = [&](bf16x8 (&dst)[TM + TN], const uint8_t* st, int t) {
+      const int off = frag_off[t];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        dst[i] = *reinterpret_cast<const bf16x8*>(st + (wave_m * TM + i) * C::kChunkBytes + off);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        dst[TM + j] = *reinterpret_cast<const bf16x8*>(st + (C::kChunksA + wave_n * TN + j) * C::kChunkBytes + off);
+    };
+    // one 16-K step: the matrix instructions of `cur`, with the reads of step `t` of
+    // stage `st` into `nxt` (when rd) placed one after each of the first TM + TN of them
+    auto step = [&](const bf16x8 (&cur)[TM + TN], bf16x8 (&nxt)[TM + TN], const uint8_t* st, int t, bool rd) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (rd) read_set(nxt, st, t);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[i], cur[TM + j], acc[i][j], 0, 0, 0);
+      if (rd) {
+#pragma unroll
+        for (int q = 0; q < TM + TN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    load_panel(0);
+    wait_panel(0);
+    wait_lds_writes();
+    barrier_no_fence();
+    if (KP > 1) load_panel(1);
+    read_set(fr[0], stage_at(0), 0);
+    for (int kp = 0; kp + 1 < KP; ++kp) {
+      const uint8_t* cur = stage_at(kp);
+      step(fr[0], fr[1], cur, 1, true);
+      step(fr[1], fr[0], cur, 2, true);
+      step(fr[0], fr[1], cur, 3, true);
+      // every wave has read this stage to the end (lgkmcnt) and panel kp+1 has landed:
+      // publish it, then refill this stage with panel kp+2 while the last step multiplies
+      wait_panel(kp + 1);
+      wait_lds_writes();
+      barrier_no_fence();
+      if (kp + 2 < KP) load_panel(kp + 2);
+      step(fr[1], fr[0], stage_at(kp + 1), 0, true);
+    }
+    const uint8_t* last = stage_at(KP - 1);
+    step(fr[0], fr[1], last, 1, true);
+    step(fr[1], fr[0], last, 2, true);
+    step(fr[0], fr[1], last, 3, true);
+    step(fr[1], fr[0], last, 0, false);
+  } else {
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
     if (p < KP) load_panel(p);
@@ -253,6 +318,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs a)
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
     }
+  }
   }
   __syncthreads();   // every wave done with the stages: LDS reused for the output
 
@@ -295,18 +361,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs a)
   }
 }
 
-template <int WM, int WN, int TM, int TN, int TS, int S>
+template <int WM, int WN, int TM, int TN, int TS, int S, bool PIPE>
 hipError_t launch_bf16_cfg(const Bf16GemmArgs& a, hipStream_t stream) {
   using C = Bf16Cfg<WM, WN, TM, TN, TS, S>;
   static_assert(C::kLdsBytes <= 160 * 1024, "LDS budget");
   const int64_t tiles = ((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM);
   const unsigned lds = C::kLdsBytes;
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_bf16_kernel<WM, WN, TM, TN, TS, S>),
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_bf16_kernel<WM, WN, TM, TN, TS, S, PIPE>),
                                     (int)lds, lds_set);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, TM, TN, TS, S>), grid, dim3(C::kThreads), lds, stream, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, TM, TN, TS, S, PIPE>), grid, dim3(C::kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -322,17 +388,18 @@ int64_t gemm_bf16_tiles(int64_t M, int64_t N) {
   return ((M + 255) / 256) * ((N + 255) / 256);
 }
 
-// Tile width 256 or 320 columns by the same round-count estimate as the NVFP4
-// GEMM: one workgroup per CU, ceil(tiles / 256) rounds, a 256-wide tile costing
-// about 82% of a 320-wide one.
+// Tile width 256 or 320 columns by a round-count estimate: one workgroup per CU,
+// ceil(tiles / 256) rounds, a 256-wide tile (pipelined loop) costing about 75% of a
+// 320-wide one (measured at K = 3840: 104.5 us for one round of 256-wide tiles against
+// 287 us for two rounds of 320-wide ones).
 hipError_t launch_gemm_bf16(const Bf16GemmArgs& a, hipStream_t stream) {
   const int64_t row_blocks = (a.M + 255) / 256;
   const int64_t tiles320 = row_blocks * ((a.N + 319) / 320);
   const int64_t tiles256 = row_blocks * ((a.N + 255) / 256);
   const double cost320 = (double)((tiles320 + 255) / 256);
-  const double cost256 = 0.82 * (double)((tiles256 + 255) / 256);
-  if (cost256 < cost320) return launch_bf16_cfg<kWM, kWN, kTM, 4, kTS, kStages>(a, stream);
-  return launch_bf16_cfg<kWM, kWN, kTM, 5, kTS, kStages>(a, stream);
+  const double cost256 = 0.75 * (double)((tiles256 + 255) / 256);
+  if (cost256 < cost320) return launch_bf16_cfg<kWM, kWN, kTM, 4, kTS, kStages, true>(a, stream);
+  return launch_bf16_cfg<kWM, kWN, kTM, 5, kTS, kStages, false>(a, stream);
 }
 
 }  // namespace svdq
