@@ -120,3 +120,40 @@ def test_variant_layer_is_exact_on_lossless_inputs():
     y_nv = S.linear_w4a4(x_bits, ones, qw, ws, wc, one, None, None, None)[0]
     assert np.array_equal(y_mx, y_nv)
     assert np.allclose(y_nv, x @ S.dequant(qw, ws).T, rtol=0, atol=0)
+
+
+def test_quantize_act_mx_applies_smooth():
+    """quantize_act_mx(x, smooth) = MX(x * smooth), checked by the rational brute force on
+    each 32-block with per-channel power-of-two smooth factors (exact products), so a dropped
+    or misplaced smooth changes the scales or the codes."""
+    rng = np.random.default_rng(3)
+    M, K = 6, 96
+    x = F.bf16_to_f64(F.f64_to_bf16(rng.standard_normal((M, K))))
+    sm = np.ldexp(1.0, rng.integers(-3, 4, K))
+    sm[::7] = 8.0
+    x_bits, sm_bits = F.f64_to_bf16(x), F.f64_to_bf16(sm)
+    codes, scales = X.quantize_act_mx(x_bits, sm_bits)
+    v = x * sm
+    for m in range(M):
+        for b in range(K // 32):
+            bc, bs = brute_block(list(v[m, 32 * b: 32 * b + 32]))
+            assert scales[m, b] == bs
+            assert list(codes[m, 32 * b: 32 * b + 32]) == bc
+    c_plain, _ = X.quantize_act_mx(x_bits, F.f64_to_bf16(np.ones(K)))
+    assert not np.array_equal(c_plain, codes)
+
+
+def test_reround_weight_mx_identity_on_representable_weight():
+    """An NVFP4 weight whose 16-block scales are equal powers of two within each 32-block and
+    whose blocks hold a 6 is MX-representable: re-rounding keeps every value, and the MX
+    scale byte is the block's power of two (2^e * 6 has floor log2 = e + 2, minus 2)."""
+    rng = np.random.default_rng(4)
+    N, K = 10, 128
+    cw = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    cw[:, ::32] = 7
+    e = rng.integers(-5, 4, (N, K // 32))
+    ws = F.e4m3_encode(np.ldexp(1.0, np.repeat(e, 2, axis=1))).T.copy()
+    qw = F.pack_nibbles(cw)
+    codes, scales = X.reround_weight_mx(qw, ws)
+    assert np.array_equal(X.mx_dequant(codes, scales), S.dequant(qw, ws))
+    assert np.array_equal(scales.astype(np.int64) - 127, e)
