@@ -189,18 +189,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
     };
   };
 
-  // panels 0 .. KP-2: multiply panel kp, dequantise panel kp+1, load panel kp+2
+  // panels 0 .. KP-2: multiply panel kp, dequantise panel kp+1, load panel kp+2. Panel
+  // kp+1 is complete after step 2 (slices 2 and 3 are dequantised there), so the barrier
+  // sits before step 3, whose fragments are already read and whose matrix instructions
+  // overlap it (1-2% faster than a barrier after the last step).
   for (int kp = 0; kp + 1 < KP; ++kp) {
     const uint8_t* cur = (kp & 1) ? stage1 : stage0;
     uint8_t* nxt = (kp & 1) ? stage0 : stage1;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      auto mm = mma_step(cur, t);
-      dequant_slice(nxt, t);
+    {
+      auto mm = mma_step(cur, 0);
+      dequant_slice(nxt, 0);
       mm();
     }
-    if (kp + 2 < KP) load_chunks(kp + 2);
-    __syncthreads();
+    {
+      auto mm = mma_step(cur, 1);
+      dequant_slice(nxt, 1);
+      mm();
+    }
+    {
+      auto mm = mma_step(cur, 2);
+      dequant_slice(nxt, 2);
+      dequant_slice(nxt, 3);
+      mm();
+    }
+    {
+      auto mm = mma_step(cur, 3);
+      if (kp + 2 < KP) load_chunks(kp + 2);
+      __syncthreads();
+      mm();
+    }
   }
   // epilogue operands load while the last panel multiplies
   const int m_w = (mp0 + wave_m * TM) * 32;
