@@ -162,8 +162,9 @@ def run_static(args):
 
 # roofline calibration of this device (no layer): sustained f16 MFMA and device copy
 CALIBS = {"calib": "sustained v_mfma_f32_32x32x16_f16 (8 waves per CU, the GEMM's occupancy and accumulator "
-                   "footprint) on exact NVFP4 values, random f16 bits and zeros, with the shader clock read by "
-                   "the kernel; streaming device copy of 1 GiB (HBM) and 64 MiB (cache resident)"}
+                   "footprint) on exact NVFP4 values, random f16 bits and zeros, and the block-scaled "
+                   "v_mfma_scale_f32_32x32x64_f8f6f4 on random fp4 and fp8 operands, with the shader clock read "
+                   "by the kernel; streaming device copy of 1 GiB (HBM) and 64 MiB (cache resident)"}
 
 
 # the oracle's own timing on the host cores (no GPU): the configurations of the pages'
@@ -478,6 +479,50 @@ def _timed(fn, n_sets, iters, stream, warmup, min_ms):
     return start.elapsed_time(end) / iters, info
 
 
+def step_percentiles(fn, n_sets, iters, stream):
+    """p10 / p50 / p90 of the per-call device time of fn(set_index) over `iters` back-to-back
+    calls, from one HIP event recorded between consecutive calls (the calls are all queued
+    before the host waits, so the device runs them back to back). A separate pass after the
+    timed region: the events do not touch the headline figure. Microseconds."""
+    import gc
+
+    import numpy as np
+    import torch
+    gc_on = gc.isenabled()
+    gc.collect()
+    gc.disable()
+    try:
+        for i in range(min(4, iters)):
+            fn(i % n_sets)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        evs[0].record(stream)
+        for i in range(iters):
+            fn(i % n_sets)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+    finally:
+        if gc_on:
+            gc.enable()
+    t = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(iters)])
+    return {"p10": round(float(np.percentile(t, 10)), 2), "p50": round(float(np.percentile(t, 50)), 2),
+            "p90": round(float(np.percentile(t, 90)), 2), "n": iters,
+            "note": "one event between consecutive calls; the events add a few us per call, so these sit "
+                    "slightly above the mean of the event-pair timing"}
+
+
+def device_info(dev):
+    """Compute units and clock as the runtime reports them (the published peaks assume 256 CUs
+    at 2.4 GHz)."""
+    import torch
+    pr = torch.cuda.get_device_properties(dev)
+    info = {"name": pr.name, "compute_units": pr.multi_processor_count,
+            "arch": getattr(pr, "gcnArchName", None)}
+    clk = getattr(pr, "clock_rate", None)
+    if clk:
+        info["max_clock_MHz"] = round(clk / 1000.0, 1)
+    return info
+
+
 def time_loop(fn, n_sets, iters, warmup, stream):
     """Average ms per call of fn(set_index) on `stream` (conditioned by time; see timed)."""
     return timed(fn, n_sets, iters, stream, warmup=warmup, min_ms=10.0)[0]
@@ -504,26 +549,44 @@ def calib_tables(dev):
     sc = (1.0 + torch.randint(0, 8, (n // 16,), generator=g).double() / 8.0) * \
         torch.pow(2.0, torch.randint(-3, 3, (n // 16,), generator=g).double())
     nv = (e2m1 * sc.repeat_interleave(16)).to(torch.float16)
+    # bytes for the block-scaled instruction: any byte is a pair of valid E2M1 codes; for e4m3
+    # the two NaN patterns (S.1111.111) are moved to the largest finite magnitude
+    byts = torch.randint(0, 256, (2 * n,), generator=g, dtype=torch.int64)
+    fp8 = torch.where((byts & 0x7F) == 0x7F, byts - 1, byts)
     return {"random_f16": rnd.to(dev), "nvfp4_values": nv.to(dev), "zeros": torch.zeros(n, dtype=torch.float16,
-                                                                                         device=dev)}
+                                                                                         device=dev),
+            "random_fp4_codes": byts.to(torch.uint8).to(dev), "random_fp8_e4m3": fp8.to(torch.uint8).to(dev)}
 
 
-def calib_mfma(table, dev, stream, target_ms=20.0, workgroups=256):
-    """Sustained f16 MFMA rate on `table`, conditioned by time; returns TFLOP/s and the
-    median shader clock (GHz) from the kernel's own counters."""
+def calib_mfma(table, dev, stream, target_ms=20.0, workgroups=256, fmt=None):
+    """Sustained MFMA rate on `table`, conditioned by time: v_mfma_f32_32x32x16_f16 (fmt None)
+    or the block-scaled v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in format fmt
+    (4 = fp4, 0 = fp8); returns TFLOP/s and the median shader clock (GHz) from the kernel's
+    own counters."""
     import torch
     from bit_w4a4_quantized_quantize_amd import _lib
     L = _lib.lib()
     out = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
     clocks = torch.zeros(workgroups * 4, dtype=torch.int64, device=dev)
-    per_iter = L.svdq_calib_flop_per_iteration(workgroups)
+    nbytes = table.numel() * table.element_size()
+    if fmt is None:
+        per_iter = L.svdq_calib_flop_per_iteration(workgroups)
+    else:
+        per_iter = L.svdq_calib_scaled_flop_per_iteration(workgroups)
 
     def launch(iters):
-        _lib.check("svdq_calib_mfma", L.svdq_calib_mfma(table.data_ptr(), table.numel() * 2, iters, workgroups,
-                                                        out.data_ptr(), out.numel() * 4, clocks.data_ptr(),
-                                                        clocks.numel() * 8, stream.cuda_stream))
+        if fmt is None:
+            _lib.check("svdq_calib_mfma", L.svdq_calib_mfma(table.data_ptr(), nbytes, iters, workgroups,
+                                                            out.data_ptr(), out.numel() * 4, clocks.data_ptr(),
+                                                            clocks.numel() * 8, stream.cuda_stream))
+        else:
+            _lib.check("svdq_calib_mfma_scaled",
+                       L.svdq_calib_mfma_scaled(table.data_ptr(), nbytes, iters, workgroups, fmt, out.data_ptr(),
+                                                out.numel() * 4, clocks.data_ptr(), clocks.numel() * 8,
+                                                stream.cuda_stream))
 
-    iters = max(1, int(2.0 * 1.6e15 * 1e-3 / per_iter))     # about 2 ms per launch
+    rate = 1.6e15 if fmt is None else 6.0e15
+    iters = max(1, int(2.0 * rate * 1e-3 / per_iter))     # about 2 ms per launch
     ms, info = timed(lambda i: launch(iters), 1, max(1, int(target_ms / 2.0)), stream, min_ms=30.0)
     tflops = iters * per_iter / (ms * 1e-3) / 1e12
     launch(iters)
@@ -564,6 +627,10 @@ def calibration(dev, stream, quick=False):
     res = {"mfma_f16_32x32x16": {}}
     for name in (("nvfp4_values", "random_f16") if quick else ("nvfp4_values", "random_f16", "zeros")):
         res["mfma_f16_32x32x16"][name] = calib_mfma(tables[name], dev, stream)
+    if not quick:
+        res["mfma_scaled_32x32x64"] = {
+            "fp4_random_codes": calib_mfma(tables["random_fp4_codes"], dev, stream, fmt=4),
+            "fp8_e4m3_random": calib_mfma(tables["random_fp8_e4m3"], dev, stream, fmt=0)}
     gbs, us = calib_copy(dev, stream, 1 << 30)
     res["copy_1GiB"] = {"GBps": gbs, "us": us}
     if not quick:
@@ -1183,6 +1250,8 @@ def run_mx(args):
     torch.cuda.synchronize()
     dist = float(torch.linalg.vector_norm((st["y"].float() - st["y_nv"].float())) /
                  torch.linalg.vector_norm(st["y_nv"].float()))
+    fp4_cal = calib_mfma(calib_tables(dev)["random_fp4_codes"], dev, stream, fmt=4)
+    print(f"[bench] sustained scaled fp4 MFMA in this run: {fp4_cal}", file=sys.stderr, flush=True)
     print(f"[bench] MXFP4 layer {ms * 1e3:.1f} us ({tflops:.1f} TFLOP/s), its GEMM {gemm_ms * 1e3:.1f} us "
           f"({gemm_tflops:.1f} TFLOP/s); NVFP4 layer {nv_ms * 1e3:.1f} us; normwise distance {dist:.4f}",
           file=sys.stderr, flush=True)
@@ -1214,7 +1283,12 @@ def run_mx(args):
             "traffic": None,
             "flop_per_launch": flops_gemm,
             "avg_launch_us": round(gemm_ms * 1e3, 2),
+            "practical_peak": fp4_cal["TFLOPs"],
+            "frac_of_practical": round(gemm_tflops / fp4_cal["TFLOPs"], 4),
+            "practical_peak_note": "sustained v_mfma_scale_f32_32x32x64_f8f6f4 on random fp4 operands at the "
+                                   "GEMM's occupancy, measured in this run",
         },
+        "calibration_fp4": fp4_cal,
         "nvfp4_layer_us": round(nv_ms * 1e3, 2),
         "speedup_vs_nvfp4": round(nv_ms / ms, 3),
         "normwise_distance_from_nvfp4": round(dist, 5),
@@ -1317,6 +1391,13 @@ def main():
           f"(conditioned {cond['conditioning_ms']:.1f} ms over {cond['conditioning_calls']} calls; "
           f"last windows {cond['conditioning_windows_us']} us/step; wall {wall:.2f} s)", file=sys.stderr, flush=True)
 
+    # the per-step distribution (a separate pass with an event between steps) and the warm-cache
+    # step (one set, the same buffers every call)
+    step_dist = step_percentiles(step, n_sets, args.steps, stream)
+    warm_ms = time_loop(step, 1, args.kernel_iters, max(1, args.warmup // 2), stream)
+    print(f"[bench] per-step p10/p50/p90 {step_dist['p10']}/{step_dist['p50']}/{step_dist['p90']} us; "
+          f"warm (one set) {warm_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
     # ---- per-kernel timings, same stream and rotation, the kernels the step runs ----
     packed = args.layout == "packed"
 
@@ -1346,6 +1427,7 @@ def main():
 
     kw = max(1, args.warmup // 2)
     gemm_ms = time_loop(gemm, n_sets, args.kernel_iters, kw, stream)
+    warm_gemm_ms = time_loop(gemm, 1, args.kernel_iters, kw, stream)
     quant_ms = time_loop(quant, n_sets, args.kernel_iters, kw, stream)
     qd_ms = time_loop(quant_down, n_sets, args.kernel_iters, kw, stream)
     gemm_tflops = flops_gemm / (gemm_ms * 1e-3) / 1e12
@@ -1418,7 +1500,11 @@ def main():
             "fused_achieved_GBps": round(quant_bytes_fused / (qd_ms * 1e-3) / 1e9, 1),
         },
         "conditioning": cond,
+        "step_us": step_dist,
+        "warm_step_us": round(warm_ms * 1e3, 2),
+        "warm_gemm_us": round(warm_gemm_ms * 1e3, 2),
         "calibration": calib,
+        "device": device_info(dev),
     }
     if args.copy_calibration:
         # a plain 512 MiB streaming copy, to calibrate the profiler's HBM byte counters

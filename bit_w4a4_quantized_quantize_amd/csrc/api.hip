@@ -1174,8 +1174,10 @@ int64_t svdq_calib_flop_per_iteration(int64_t workgroups) {
   return workgroups * svdq::calib_waves_per_workgroup() * svdq::calib_flop_per_wave_iteration();
 }
 
-int svdq_calib_mfma(const void* table, size_t table_bytes, int64_t iters, int64_t workgroups, void* out,
-                    size_t out_bytes, void* clocks, size_t clocks_bytes, void* stream) {
+namespace {
+// argument checks shared by the two sustained-rate kernels
+int calib_mfma_checks(const void* table, size_t table_bytes, int64_t iters, int64_t workgroups, void* out,
+                      size_t out_bytes, void* clocks, size_t clocks_bytes) {
   if (iters < 1 || workgroups < 1 || workgroups > (int64_t(1) << 20))
     return fail(SVDQ_ERR_SHAPE, "iters = %lld and workgroups = %lld must be positive (workgroups <= 2^20)",
                 (long long)iters, (long long)workgroups);
@@ -1194,9 +1196,32 @@ int svdq_calib_mfma(const void* table, size_t table_bytes, int64_t iters, int64_
                 clocks_bytes, need_clk);
   const Range in[] = {range("table", table, svdq::calib_table_bytes())};
   const Range outs[] = {range("out", out, need_out), range("clocks", clocks, need_clk)};
-  if ((st = check_alias(in, 1, outs, 2))) return st;
+  return check_alias(in, 1, outs, 2);
+}
+}  // namespace
+
+int svdq_calib_mfma(const void* table, size_t table_bytes, int64_t iters, int64_t workgroups, void* out,
+                    size_t out_bytes, void* clocks, size_t clocks_bytes, void* stream) {
+  if (int st = calib_mfma_checks(table, table_bytes, iters, workgroups, out, out_bytes, clocks, clocks_bytes))
+    return st;
   hipError_t e = svdq::launch_calib_mfma(table, iters, workgroups, static_cast<float*>(out),
                                          static_cast<uint64_t*>(clocks), static_cast<hipStream_t>(stream));
+  if (int st_ = launched(e, "calibration", static_cast<hipStream_t>(stream))) return st_;
+  return ok();
+}
+
+int64_t svdq_calib_scaled_flop_per_iteration(int64_t workgroups) {
+  if (workgroups <= 0) return 0;
+  return workgroups * svdq::calib_waves_per_workgroup() * svdq::calib_scaled_flop_per_wave_iteration();
+}
+
+int svdq_calib_mfma_scaled(const void* table, size_t table_bytes, int64_t iters, int64_t workgroups, int fmt,
+                           void* out, size_t out_bytes, void* clocks, size_t clocks_bytes, void* stream) {
+  if (fmt != 0 && fmt != 4) return fail(SVDQ_ERR_UNSUPPORTED, "fmt = %d (0 = fp8 e4m3 or 4 = fp4 E2M1)", fmt);
+  if (int st = calib_mfma_checks(table, table_bytes, iters, workgroups, out, out_bytes, clocks, clocks_bytes))
+    return st;
+  hipError_t e = svdq::launch_calib_mfma_scaled(table, iters, workgroups, fmt, static_cast<float*>(out),
+                                                static_cast<uint64_t*>(clocks), static_cast<hipStream_t>(stream));
   if (int st_ = launched(e, "calibration", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }

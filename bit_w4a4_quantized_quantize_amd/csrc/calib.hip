@@ -1,6 +1,6 @@
 // Measurement helpers, not part of the layer: the sustained rate of the matrix
-// instruction the NVFP4 GEMM runs (v_mfma_f32_32x32x16_f16) on operands the
-// caller chooses, with the shader clock sampled in the kernel, and a plain
+// instruction the NVFP4 GEMM runs (v_mfma_f32_32x32x16_f16), and of the
+// block-scaled one the MXFP4 variant runs, on operands the caller chooses, with the shader clock sampled in the kernel, and a plain
 // streaming device copy. They calibrate the roofline figures the benchmark
 // reports next to the published peaks: the chip power-limits its clock under
 // sustained matrix work, and by how much depends on how many operand bits
@@ -72,6 +72,73 @@ __global__ __launch_bounds__(64 * kCalibWaves) void calib_mfma_kernel(const f16x
   out[(size_t)blockIdx.x * 64 * kCalibWaves + threadIdx.x] = s;
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// The same measurement for the block-scaled matrix instruction of the MXFP4 variant,
+// v_mfma_scale_f32_32x32x64_f8f6f4, with FMT the operand format of both sides (4 = fp4
+// E2M1: the first 16 bytes of each operand are used; 0 = fp8 e4m3: all 32 bytes) and
+// unit E8M0 scales. Operands are built from the table's bytes: fragment i alone (fp4),
+// or fragments i and i+1 (fp8).
+template <int FMT>
+__global__ __launch_bounds__(64 * kCalibWaves) void calib_mfma_scaled_kernel(const u32x4* __restrict__ table,
+                                                                             int64_t iters, float* __restrict__ out,
+                                                                             uint64_t* __restrict__ clocks) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int set = (int)((blockIdx.x * kCalibWaves + wave) % kCalibTables);
+  u32x4 raw[kCalibFrags];
+#pragma unroll
+  for (int i = 0; i < kCalibFrags; ++i) raw[i] = table[(set * kCalibFrags + i) * 64 + lane];
+  i32x8 f[kCalibFrags];
+#pragma unroll
+  for (int i = 0; i < kCalibFrags; ++i) {
+    const u32x4 a = raw[i];
+    const u32x4 b = FMT == 4 ? zero4() : raw[(i + 1) % kCalibFrags];
+    f[i] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  }
+  f32x16 acc[10];
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+
+  const bool timer = threadIdx.x == 0;
+  uint64_t c0 = 0, w0 = 0;
+  if (timer) {
+    c0 = (uint64_t)clock64();
+    w0 = (uint64_t)wall_clock64();
+  }
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 5; ++j)
+        acc[5 * i + j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[i], f[2 + j], acc[5 * i + j], FMT, FMT, 0,
+                                                                         127, 0, 127);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 5; ++j)
+        acc[5 * i + j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[7 - i], f[j], acc[5 * i + j], FMT, FMT, 0,
+                                                                         127, 0, 127);
+  }
+  if (timer) {
+    const uint64_t c1 = (uint64_t)clock64();
+    const uint64_t w1 = (uint64_t)wall_clock64();
+    uint64_t* c = clocks + 4 * blockIdx.x;
+    c[0] = c0;
+    c[1] = c1;
+    c[2] = w0;
+    c[3] = w1;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[t][r];
+  out[(size_t)blockIdx.x * 64 * kCalibWaves + threadIdx.x] = s;
+}
+
 // Grid-stride copy of 16-byte units, four in flight per thread.
 __global__ __launch_bounds__(256) void calib_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                          int64_t n) {
@@ -92,6 +159,21 @@ __global__ __launch_bounds__(256) void calib_copy_kernel(const u32x4* __restrict
 size_t calib_table_bytes() { return (size_t)kCalibTables * kCalibFrags * 64 * sizeof(f16x8); }
 int calib_waves_per_workgroup() { return kCalibWaves; }
 int64_t calib_flop_per_wave_iteration() { return 20 * 2 * 32 * 32 * 16; }
+int64_t calib_scaled_flop_per_wave_iteration() { return 20 * 2 * 32 * 32 * 64; }
+
+hipError_t launch_calib_mfma_scaled(const void* table, int64_t iters, int64_t workgroups, int fmt, float* out,
+                                    uint64_t* clocks, hipStream_t stream) {
+  const u32x4* t = static_cast<const u32x4*>(table);
+  if (fmt == 4)
+    hipLaunchKernelGGL(calib_mfma_scaled_kernel<4>, dim3((unsigned)workgroups), dim3(64 * kCalibWaves), 0, stream, t,
+                       iters, out, clocks);
+  else if (fmt == 0)
+    hipLaunchKernelGGL(calib_mfma_scaled_kernel<0>, dim3((unsigned)workgroups), dim3(64 * kCalibWaves), 0, stream, t,
+                       iters, out, clocks);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_calib_mfma(const void* table, int64_t iters, int64_t workgroups, float* out, uint64_t* clocks,
                              hipStream_t stream) {

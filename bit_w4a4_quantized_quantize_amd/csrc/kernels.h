@@ -147,6 +147,10 @@ int calib_waves_per_workgroup();
 int64_t calib_flop_per_wave_iteration();
 hipError_t launch_calib_mfma(const void* table, int64_t iters, int64_t workgroups, float* out, uint64_t* clocks,
                              hipStream_t stream);
+// the block-scaled instruction (fmt 4: fp4 E2M1, 0: fp8 e4m3), unit scales, same table
+int64_t calib_scaled_flop_per_wave_iteration();
+hipError_t launch_calib_mfma_scaled(const void* table, int64_t iters, int64_t workgroups, int fmt, float* out,
+                                    uint64_t* clocks, hipStream_t stream);
 hipError_t launch_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 }  // namespace svdq

@@ -405,6 +405,12 @@ int svdq_linear_mxfp4(const void* x, const void* smooth, const void* w_codes, co
  *   clocks: >= workgroups * 4 uint64, per workgroup the core-clock counter at
  *   its start and end, then the constant-rate counter at its start and end
  *   (rate in kHz from svdq_calib_wall_clock_khz).
+ * svdq_calib_mfma_scaled: the same for the block-scaled instruction the MXFP4
+ *   variant runs (v_mfma_scale_f32_32x32x64_f8f6f4), both operands in format
+ *   `fmt` (4 = fp4 E2M1, using the first 16 bytes of each lane's operand; 0 =
+ *   fp8 e4m3, using 32 bytes) and unit E8M0 scales, operands taken from the same
+ *   table's bytes. Work per launch: iters * svdq_calib_scaled_flop_per_iteration(
+ *   workgroups) flop. Another fmt returns SVDQ_ERR_UNSUPPORTED.
  * svdq_calib_copy: dst = src, `bytes` (a multiple of 16) by a streaming
  *   kernel; src and dst must not overlap. The device-copy rate is the
  *   practical HBM ceiling, and its byte counters calibrate the profiler's.
@@ -415,6 +421,9 @@ size_t svdq_calib_table_bytes(void);
 int64_t svdq_calib_flop_per_iteration(int64_t workgroups);
 int svdq_calib_mfma(const void* table, size_t table_bytes, int64_t iters, int64_t workgroups, void* out,
                     size_t out_bytes, void* clocks, size_t clocks_bytes, void* stream);
+int64_t svdq_calib_scaled_flop_per_iteration(int64_t workgroups);
+int svdq_calib_mfma_scaled(const void* table, size_t table_bytes, int64_t iters, int64_t workgroups, int fmt,
+                           void* out, size_t out_bytes, void* clocks, size_t clocks_bytes, void* stream);
 int svdq_calib_copy(const void* src, void* dst, size_t bytes, void* stream);
 int svdq_calib_wall_clock_khz(int* khz);
 

@@ -343,3 +343,25 @@ def test_noalloc_size_limit_and_empty():
                                       None) == 0
     assert L.svdq_linear_w4a4_noalloc(None, None, None, None, 1, None, None, None, None, None, 64, N, 100, R, None,
                                       None) == 2   # K not a multiple of 16
+
+
+@no_gpu_only
+def test_calib_rejections_and_sizes():
+    """The measurement helpers check their arguments on the host: sizes, formats, buffers."""
+    L = _lib.lib()
+    tb = L.svdq_calib_table_bytes()
+    assert tb == 64 * 8 * 64 * 16
+    assert L.svdq_calib_flop_per_iteration(256) == 256 * 8 * 20 * 2 * 32 * 32 * 16
+    assert L.svdq_calib_scaled_flop_per_iteration(256) == 256 * 8 * 20 * 2 * 32 * 32 * 64
+    assert L.svdq_calib_scaled_flop_per_iteration(0) == 0
+    wg = 4
+    out_b, clk_b = wg * 512 * 4, wg * 4 * 8
+    args = (fake(1), tb, 10, wg)
+    assert L.svdq_calib_mfma_scaled(*args, 7, fake(2), out_b, fake(3), clk_b, None) == 3    # format
+    assert L.svdq_calib_mfma_scaled(*args, 4, fake(2), out_b - 4, fake(3), clk_b, None) == 5
+    assert L.svdq_calib_mfma_scaled(fake(1), tb - 16, 10, wg, 0, fake(2), out_b, fake(3), clk_b, None) == 5
+    assert L.svdq_calib_mfma_scaled(fake(1), tb, 0, wg, 4, fake(2), out_b, fake(3), clk_b, None) == 2
+    assert L.svdq_calib_mfma_scaled(None, tb, 10, wg, 4, fake(2), out_b, fake(3), clk_b, None) == 1
+    assert L.svdq_calib_mfma_scaled(*args, 4, fake(1) + 64, out_b, fake(3), clk_b, None) == 6   # overlaps table
+    assert L.svdq_calib_mfma(fake(1), tb, 10, 0, fake(2), out_b, fake(3), clk_b, None) == 2
+    assert L.svdq_calib_copy(fake(1), fake(2), 24, None) == 2
