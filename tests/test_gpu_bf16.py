@@ -56,6 +56,9 @@ def run(gpu_lib, d):
     (1, 16, 1, True),           # smallest problem
     (5, 48, 13, True),
     (40, 3840, 8, True),
+    (130, 128, 200, True),      # two K panels: one pass of the pipelined loop
+    (70, 80, 96, False),        # two panels, the second zero-filled past K
+    (33, 192, 264, True),       # three panels; ragged N
 ])
 def test_bf16_linear_small(gpu_lib, M, K, N, bias):
     d = workloads.make_bf16_linear(M, K, N, kind="dit", seed=M * 7 + N, with_bias=bias)

@@ -121,6 +121,9 @@ def test_gemm_deterministic(gpu_lib):
     dict(M=257, K=1024, N=257, R=0, kind="dit", seed=25),
     dict(M=300, K=512, N=700, R=272, kind="dit", seed=27),
     dict(M=33, K=64, N=40, R=16, kind="dit", seed=28),          # one panel: only the peeled iteration
+    dict(M=70, K=128, N=96, R=16, kind="dit", seed=36),         # two panels: one loop pass, no refill
+    dict(M=290, K=192, N=650, R=32, kind="dit", seed=37),       # three panels; partial column tile
+    dict(M=40, K=80, N=64, R=0, kind="tiny", seed=38),          # two panels, the second K-ragged
 ])
 def test_gemm_packed_activations(gpu_lib, cfg):
     """Packed activations (placed by the oracle's statement of the layout) through the
