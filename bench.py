@@ -483,7 +483,8 @@ def step_percentiles(fn, n_sets, iters, stream):
     """p10 / p50 / p90 of the per-call device time of fn(set_index) over `iters` back-to-back
     calls, from one HIP event recorded between consecutive calls (the calls are all queued
     before the host waits, so the device runs them back to back). A separate pass after the
-    timed region: the events do not touch the headline figure. Microseconds."""
+    timed region, conditioned by time like it and started while the conditioning calls still
+    run: the events do not touch the headline figure. Microseconds."""
     import gc
 
     import numpy as np
@@ -492,9 +493,8 @@ def step_percentiles(fn, n_sets, iters, stream):
     gc.collect()
     gc.disable()
     try:
-        for i in range(min(4, iters)):
-            fn(i % n_sets)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        condition(fn, n_sets, stream, min_ms=10.0)
         evs[0].record(stream)
         for i in range(iters):
             fn(i % n_sets)
