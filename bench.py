@@ -639,8 +639,9 @@ def calibration(dev, stream, quick=False):
     return res
 
 
-def cpu_baseline(d, cfg, repeats=2):
-    """The oracle (untuned NumPy float64) on the same workload, whole layer per call."""
+def cpu_baseline(d, cfg, repeats=5):
+    """The oracle (untuned NumPy float64) on the same workload, whole layer per call: five
+    calls (about 10 s of host work at the headline shape), median."""
     import numpy as np
     from oracle import svdq as S
 
