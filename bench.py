@@ -164,7 +164,8 @@ def run_static(args):
 CALIBS = {"calib": "sustained v_mfma_f32_32x32x16_f16 (8 waves per CU, the GEMM's occupancy and accumulator "
                    "footprint) on exact NVFP4 values, random f16 bits and zeros, and the block-scaled "
                    "v_mfma_scale_f32_32x32x64_f8f6f4 on random fp4 and fp8 operands, with the shader clock read "
-                   "by the kernel; streaming device copy of 1 GiB (HBM) and 64 MiB (cache resident)"}
+                   "by the kernel; streaming device copy of 1 GiB (HBM) and 64 MiB (cache resident); LDS "
+                   "bandwidth of 16-byte reads, writes and a 3:1 mix"}
 
 
 # the oracle's own timing on the host cores (no GPU): the configurations of the pages'
@@ -621,6 +622,25 @@ def calib_copy(dev, stream, nbytes, reps=10):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1), round(ms * 1e3, 2)
 
 
+def calib_lds(dev, stream, mode, workgroups=256):
+    """Chip-wide LDS bandwidth (TB/s of bytes moved) of 16-byte accesses: mode 0 reads, 1
+    writes, 2 three reads to one write."""
+    import torch
+    from bit_w4a4_quantized_quantize_amd import _lib
+    L = _lib.lib()
+    out = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
+    per_iter = L.svdq_calib_lds_bytes_per_iteration(workgroups)
+    iters = 4096
+
+    def launch(i):
+        _lib.check("svdq_calib_lds", L.svdq_calib_lds(iters, workgroups, mode, out.data_ptr(), out.numel() * 4,
+                                                      stream.cuda_stream))
+
+    ms, _ = timed(launch, 1, 10, stream, min_ms=10.0)
+    return {"TBps": round(iters * per_iter / (ms * 1e-3) / 1e12, 1), "ms_per_launch": round(ms, 4),
+            "bytes_per_launch": iters * per_iter}
+
+
 def calibration(dev, stream, quick=False):
     """Sustained f16 MFMA rates and device-copy rates on this device."""
     tables = calib_tables(dev)
@@ -636,6 +656,8 @@ def calibration(dev, stream, quick=False):
     if not quick:
         gbs, us = calib_copy(dev, stream, 64 << 20, reps=50)
         res["copy_64MiB_cache_resident"] = {"GBps": gbs, "us": us}
+        res["lds_16B_accesses"] = {"reads": calib_lds(dev, stream, 0), "writes": calib_lds(dev, stream, 1),
+                                   "three_reads_one_write": calib_lds(dev, stream, 2)}
     return res
 
 

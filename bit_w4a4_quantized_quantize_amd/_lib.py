@@ -80,6 +80,8 @@ SIGNATURES = {
     "svdq_calib_scaled_flop_per_iteration": (_i64, [_i64]),
     "svdq_calib_mfma_scaled": (_int, [_c_void_p, _size, _i64, _i64, _int, _c_void_p, _size, _c_void_p, _size,
                                       _c_void_p]),
+    "svdq_calib_lds_bytes_per_iteration": (_i64, [_i64]),
+    "svdq_calib_lds": (_int, [_i64, _i64, _int, _c_void_p, _size, _c_void_p]),
     "svdq_calib_copy": (_int, [_c_void_p, _c_void_p, _size, _c_void_p]),
     "svdq_calib_wall_clock_khz": (_int, [ctypes.POINTER(_int)]),
 }

@@ -1226,6 +1226,25 @@ int svdq_calib_mfma_scaled(const void* table, size_t table_bytes, int64_t iters,
   return ok();
 }
 
+int64_t svdq_calib_lds_bytes_per_iteration(int64_t workgroups) {
+  if (workgroups <= 0) return 0;
+  return svdq::calib_lds_bytes_per_iteration(workgroups);
+}
+
+int svdq_calib_lds(int64_t iters, int64_t workgroups, int mode, void* out, size_t out_bytes, void* stream) {
+  if (mode < 0 || mode > 2) return fail(SVDQ_ERR_UNSUPPORTED, "mode = %d (0 reads, 1 writes, 2 three to one)", mode);
+  if (iters < 1 || workgroups < 1 || workgroups > (int64_t(1) << 20))
+    return fail(SVDQ_ERR_SHAPE, "iters = %lld and workgroups = %lld must be positive (workgroups <= 2^20)",
+                (long long)iters, (long long)workgroups);
+  if (out == nullptr) return fail(SVDQ_ERR_NULL, "out is NULL");
+  const size_t need = (size_t)workgroups * 64 * svdq::calib_waves_per_workgroup() * 4;
+  if (out_bytes < need) return fail(SVDQ_ERR_WORKSPACE, "out has %zu bytes, %zu needed", out_bytes, need);
+  hipError_t e = svdq::launch_calib_lds(iters, workgroups, mode, static_cast<float*>(out),
+                                        static_cast<hipStream_t>(stream));
+  if (int st_ = launched(e, "calibration", static_cast<hipStream_t>(stream))) return st_;
+  return ok();
+}
+
 int svdq_calib_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes % 16 != 0) return fail(SVDQ_ERR_SHAPE, "bytes = %zu is not a multiple of 16", bytes);
   if (bytes == 0) return ok();

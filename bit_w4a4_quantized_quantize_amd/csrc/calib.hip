@@ -139,6 +139,37 @@ __global__ __launch_bounds__(64 * kCalibWaves) void calib_mfma_scaled_kernel(con
   out[(size_t)blockIdx.x * 64 * kCalibWaves + threadIdx.x] = s;
 }
 
+// LDS bandwidth: 8 waves per workgroup over a 64 KB region, each lane moving 16 bytes per
+// instruction at consecutive 16-byte slots (conflict-free). MODE 0: ds_read_b128 only; 1:
+// ds_write_b128 only; 2: three reads to one write (the GEMM main loop's mix is about 3:1).
+// Each iteration issues 8 instructions per wave; the sums keep the reads live.
+template <int MODE>
+__global__ __launch_bounds__(64 * kCalibWaves) void calib_lds_kernel(int64_t iters, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) u32x4 buf[4096];   // 64 KB
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 4096; i += 64 * kCalibWaves) buf[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  u32x4 acc = zero4();
+  const u32x4 w = {(uint32_t)tid, 7u, 9u, 11u};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int slot = (tid + 512 * k + (int)(it & 7) * 64) & 4095;
+      if (MODE == 0 || (MODE == 2 && (k & 3) != 3)) {
+        const u32x4 v = buf[slot];
+        acc[0] += v[0]; acc[1] ^= v[1]; acc[2] += v[2]; acc[3] ^= v[3];
+      } else {
+        buf[slot] = w + acc;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the iteration's accesses are done
+  }
+  __syncthreads();
+  const u32x4 last = buf[(tid * 7) & 4095];   // the writes are observed
+  out[(size_t)blockIdx.x * 64 * kCalibWaves + tid] =
+      (float)(acc[0] + acc[1] + acc[2] + acc[3] + last[0] + last[1] + last[2] + last[3]);
+}
+
 // Grid-stride copy of 16-byte units, four in flight per thread.
 __global__ __launch_bounds__(256) void calib_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                          int64_t n) {
@@ -179,6 +210,20 @@ hipError_t launch_calib_mfma(const void* table, int64_t iters, int64_t workgroup
                              hipStream_t stream) {
   hipLaunchKernelGGL(calib_mfma_kernel, dim3((unsigned)workgroups), dim3(64 * kCalibWaves), 0, stream,
                      static_cast<const f16x8*>(table), iters, out, clocks);
+  return hipGetLastError();
+}
+
+int64_t calib_lds_bytes_per_iteration(int64_t workgroups) { return workgroups * 64 * kCalibWaves * 8 * 16; }
+
+hipError_t launch_calib_lds(int64_t iters, int64_t workgroups, int mode, float* out, hipStream_t stream) {
+  if (mode == 0)
+    hipLaunchKernelGGL(calib_lds_kernel<0>, dim3((unsigned)workgroups), dim3(64 * kCalibWaves), 0, stream, iters, out);
+  else if (mode == 1)
+    hipLaunchKernelGGL(calib_lds_kernel<1>, dim3((unsigned)workgroups), dim3(64 * kCalibWaves), 0, stream, iters, out);
+  else if (mode == 2)
+    hipLaunchKernelGGL(calib_lds_kernel<2>, dim3((unsigned)workgroups), dim3(64 * kCalibWaves), 0, stream, iters, out);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -151,6 +151,9 @@ hipError_t launch_calib_mfma(const void* table, int64_t iters, int64_t workgroup
 int64_t calib_scaled_flop_per_wave_iteration();
 hipError_t launch_calib_mfma_scaled(const void* table, int64_t iters, int64_t workgroups, int fmt, float* out,
                                     uint64_t* clocks, hipStream_t stream);
+// LDS bandwidth (mode 0: 16-byte reads, 1: writes, 2: three reads to one write)
+int64_t calib_lds_bytes_per_iteration(int64_t workgroups);
+hipError_t launch_calib_lds(int64_t iters, int64_t workgroups, int mode, float* out, hipStream_t stream);
 hipError_t launch_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 }  // namespace svdq

@@ -411,6 +411,11 @@ int svdq_linear_mxfp4(const void* x, const void* smooth, const void* w_codes, co
  *   fp8 e4m3, using 32 bytes) and unit E8M0 scales, operands taken from the same
  *   table's bytes. Work per launch: iters * svdq_calib_scaled_flop_per_iteration(
  *   workgroups) flop. Another fmt returns SVDQ_ERR_UNSUPPORTED.
+ * svdq_calib_lds: LDS bandwidth. `workgroups` workgroups of 8 waves each run
+ *   `iters` iterations of 8 16-byte LDS accesses per lane on conflict-free slots
+ *   of a 64 KB region: mode 0 reads only, 1 writes only, 2 three reads to one
+ *   write. Bytes per launch: iters * svdq_calib_lds_bytes_per_iteration(
+ *   workgroups). out: >= workgroups * 512 floats (keeps the reads live).
  * svdq_calib_copy: dst = src, `bytes` (a multiple of 16) by a streaming
  *   kernel; src and dst must not overlap. The device-copy rate is the
  *   practical HBM ceiling, and its byte counters calibrate the profiler's.
@@ -424,6 +429,8 @@ int svdq_calib_mfma(const void* table, size_t table_bytes, int64_t iters, int64_
 int64_t svdq_calib_scaled_flop_per_iteration(int64_t workgroups);
 int svdq_calib_mfma_scaled(const void* table, size_t table_bytes, int64_t iters, int64_t workgroups, int fmt,
                            void* out, size_t out_bytes, void* clocks, size_t clocks_bytes, void* stream);
+int64_t svdq_calib_lds_bytes_per_iteration(int64_t workgroups);
+int svdq_calib_lds(int64_t iters, int64_t workgroups, int mode, void* out, size_t out_bytes, void* stream);
 int svdq_calib_copy(const void* src, void* dst, size_t bytes, void* stream);
 int svdq_calib_wall_clock_khz(int* khz);
 

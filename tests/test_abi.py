@@ -365,3 +365,8 @@ def test_calib_rejections_and_sizes():
     assert L.svdq_calib_mfma_scaled(*args, 4, fake(1) + 64, out_b, fake(3), clk_b, None) == 6   # overlaps table
     assert L.svdq_calib_mfma(fake(1), tb, 10, 0, fake(2), out_b, fake(3), clk_b, None) == 2
     assert L.svdq_calib_copy(fake(1), fake(2), 24, None) == 2
+    assert L.svdq_calib_lds_bytes_per_iteration(256) == 256 * 512 * 8 * 16
+    assert L.svdq_calib_lds(10, wg, 3, fake(2), out_b, None) == 3
+    assert L.svdq_calib_lds(0, wg, 0, fake(2), out_b, None) == 2
+    assert L.svdq_calib_lds(10, wg, 0, None, out_b, None) == 1
+    assert L.svdq_calib_lds(10, wg, 1, fake(2), out_b - 4, None) == 5
