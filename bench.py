@@ -47,6 +47,12 @@ WORKLOADS = {
     "out_2048": (("LAYERS_2048", "out"), "DiT attention output projection at 2048px"),
     "ffn_w1_2048": (("LAYERS_2048", "w1"), "DiT FFN w1 at 2048px"),
     "ffn_w2_2048": (("LAYERS_2048", "w2"), "DiT FFN w2 at 2048px"),
+    "qkv_1024_tp8": (("SHARDS_TP8_1024", "qkv"), "one GPU's shard of the 1024^2 fused QKV projection at "
+                                                 "8-way tensor parallelism (N = 11520 / 8)"),
+    "ffn_w1_1024_tp8": (("SHARDS_TP8_1024", "w1"), "one GPU's shard of the 1024^2 FFN w1 at 8-way tensor "
+                                                   "parallelism (N = 10240 / 8)"),
+    "ffn_w2_1024_tp8": (("SHARDS_TP8_1024", "w2"), "one GPU's shard of the 1024^2 FFN w2 at 8-way tensor "
+                                                   "parallelism (K = 10240 / 8, row-parallel)"),
 }
 DEFAULT_WORKLOAD = "ffn_w1_1024"
 # the gated FFN block (w1/w3 as one 2F-channel layer with silu(gate) * up, then w2)

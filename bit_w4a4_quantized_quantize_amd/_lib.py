@@ -21,6 +21,7 @@ SIGNATURES = {
     "svdq_status_string": (ctypes.c_char_p, [_int]),
     "svdq_last_error": (ctypes.c_char_p, []),
     "svdq_debug_mode": (_int, []),
+    "svdq_set_gemm_tile": (_int, [_int, ctypes.POINTER(_int)]),
     "svdq_quantize_act_workspace_bytes": (_size, [_i64, _i64, _i64]),
     "svdq_packed_act_bytes": (_size, [_i64, _i64]),
     "svdq_quantize_act": (_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64, _int,

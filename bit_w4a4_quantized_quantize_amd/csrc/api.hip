@@ -219,6 +219,13 @@ const char* svdq_last_error(void) { return g_last_error.c_str(); }
 
 int svdq_debug_mode(void) { return debug_mode() ? 1 : 0; }
 
+int svdq_set_gemm_tile(int tile, int* previous) {
+  if (tile < 0 || tile > 4) return fail(SVDQ_ERR_INVALID, "tile = %d is not 0..4", tile);
+  const int prev = svdq::set_gemm_tile(tile);
+  if (previous != nullptr) *previous = prev;
+  return SVDQ_OK;
+}
+
 size_t svdq_quantize_act_workspace_bytes(int64_t M, int64_t K, int64_t R) {
   if (M <= 0 || K <= 0 || R <= 0) return 0;
   return quant_ws_bytes(M, K, R);

@@ -59,6 +59,14 @@ struct LdsCfg {
   static constexpr int kRest = kChunks - kFull * kWaves;         // waves 0..kRest-1 take one more
   static constexpr int kPerWave = kFull + (kRest ? 1 : 0);
   static constexpr int kStageBytes = kChunks * 4096;
+  // LDS of the output epilogue: the gated exchange region (one f32x16 per lane per
+  // column tile and wave row), then 32 staged bf16 rows of every writing wave
+  static constexpr int epilogue_bytes(bool gated) {
+    return (gated ? WM * TN * 64 * 64 : 0) + (gated ? WM : kWaves) * 32 * (32 * TN) * 2;
+  }
+  static constexpr int lds_bytes(bool gated) {
+    return 2 * kStageBytes > epilogue_bytes(gated) ? 2 * kStageBytes : epilogue_bytes(gated);
+  }
 };
 
 // GATED: the weight holds 2F output channels (a.N = 2F, a.gated_f = F); the
@@ -327,6 +335,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   constexpr int kPieces = kCols / 8;
   constexpr int kXBytes = GATED ? WM * TN * 64 * 64 : 0;   // f32x16 per lane per column tile
   const bool writer = !GATED || wave_n == 0;
+  static_assert(kXBytes + (GATED ? WM : C::kWaves) * 32 * kCols * 2 == C::epilogue_bytes(GATED),
+                "the launch sizes LDS for this epilogue");
   uint16_t* stage_out = reinterpret_cast<uint16_t*>(smem + kXBytes + (GATED ? wave_m : wave) * (32 * kCols * 2));
   f32x16* xchg = reinterpret_cast<f32x16*>(smem) + wave_m * TN * 64;
   const bool vec_ok = (FO % 8) == 0;
@@ -426,7 +436,8 @@ hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
   using C = LdsCfg<WM, WN, TM, TN>;
   const int64_t col_tiles = GATED ? ((a.gated_f + 31) / 32 + TN - 1) / TN : (a.N + C::BN - 1) / C::BN;
   const int64_t tiles = col_tiles * ((a.M + C::BM - 1) / C::BM);
-  const unsigned lds = 2 * C::kStageBytes;
+  const unsigned lds = C::lds_bytes(GATED);
+  static_assert(C::lds_bytes(GATED) <= 160 * 1024, "LDS per workgroup");
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN, GATED, Q2>),
                                     (int)lds, lds_set);
@@ -438,29 +449,52 @@ hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Tile width: 320 columns (5 tiles per wave) or 256 (4 per wave). One
-// workgroup runs per CU, so the kernel takes ceil(tiles / 256) rounds; a
-// 256-wide tile does 80% of the work of a 320-wide one in about 82% of its
-// time. The cheaper estimate wins: e.g. N = 10240 keeps 320 (512 tiles at
-// M = 4096: 2 rounds), N = 11520 takes 256 (720 tiles: 3 rounds of 82%
-// instead of 576 tiles: 3 rounds of 100%). Gated, the same choice is made for
-// the 2F-wide weight (each tile covers half its width in each half).
+static std::atomic<int> g_gemm_tile{0};
+
+// Tile shape. The candidates, with the time of one round of workgroups relative to
+// the 256 x 320 shape's, measured at full occupancy (K = 3840):
+//   1: 256 x 320, 8 waves of 64 x 160, one workgroup per CU       1.0
+//   2: 256 x 256, 8 waves of 64 x 128, one per CU                 0.82
+//   3: 128 x 320, 8 waves of 32 x 160, one per CU                 0.62
+//   4: 128 x 160, 4 waves of 32 x 160, two per CU                 0.66, or 0.49
+//      when no CU has a second one (not gated: that epilogue pairs two wave columns)
+// The estimate is rounds x that factor, the smallest wins (ties to the lower
+// number). The large tiles keep full-size layers on few dequantisations per
+// flop (N = 10240 at M = 4096: 512 tiles of shape 1, two rounds); the small ones
+// keep the CUs busy when the output is small, as for one GPU's share of a layer
+// split 8 ways by columns (N = 1280: 64 tiles of shape 1, 256 of shape 4).
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream) {
   const bool gated = a.gated_f > 0;
-  const int64_t row_blocks = (a.M + 255) / 256;
-  const int64_t width = gated ? 2 * ((a.gated_f + 31) / 32 * 32) : a.N;
-  const int64_t tiles320 = row_blocks * ((width + 319) / 320);
-  const int64_t tiles256 = row_blocks * ((width + 255) / 256);
-  const double cost320 = (double)((tiles320 + 255) / 256);
-  const double cost256 = 0.82 * (double)((tiles256 + 255) / 256);
+  const int64_t FP = gated ? (a.gated_f + 31) / 32 : 0;
+  auto cols = [&](int TN, int WN) -> int64_t {
+    return gated ? (FP + TN - 1) / TN : (a.N + 32 * TN * WN - 1) / (32 * TN * WN);
+  };
+  const int64_t r256 = (a.M + 255) / 256, r128 = (a.M + 127) / 128;
+  const int64_t tiles[4] = {r256 * cols(5, 2), r256 * cols(4, 2), r128 * cols(5, 2), r128 * cols(5, 1)};
+  auto rounds = [](int64_t t, int64_t slots) { return (double)((t + slots - 1) / slots); };
+  const double cost[4] = {rounds(tiles[0], 256), 0.82 * rounds(tiles[1], 256), 0.62 * rounds(tiles[2], 256),
+                          gated ? 1e30 : (tiles[3] <= 256 ? 0.49 : 0.66 * rounds(tiles[3], 512))};
+  int pick = 0;
+  for (int i = 1; i < 4; ++i)
+    if (cost[i] < cost[pick]) pick = i;
+  const int forced = g_gemm_tile.load(std::memory_order_relaxed);
+  if (forced >= 1 && forced <= 4 && !(gated && forced == 4)) pick = forced - 1;
   if (gated) {
     const bool q2 = a.next_qact != nullptr;
-    if (cost256 < cost320)
+    if (pick == 1)
       return q2 ? launch_lds_cfg<4, 2, 2, 4, true, true>(a, stream) : launch_lds_cfg<4, 2, 2, 4, true>(a, stream);
+    if (pick == 2)
+      return q2 ? launch_lds_cfg<4, 2, 1, 5, true, true>(a, stream) : launch_lds_cfg<4, 2, 1, 5, true>(a, stream);
     return q2 ? launch_lds_cfg<4, 2, 2, 5, true, true>(a, stream) : launch_lds_cfg<4, 2, 2, 5, true>(a, stream);
   }
-  if (cost256 < cost320) return launch_lds_cfg<4, 2, 2, 4, false>(a, stream);
-  return launch_lds_cfg<4, 2, 2, 5, false>(a, stream);
+  switch (pick) {
+    case 1: return launch_lds_cfg<4, 2, 2, 4, false>(a, stream);
+    case 2: return launch_lds_cfg<4, 2, 1, 5, false>(a, stream);
+    case 3: return launch_lds_cfg<4, 1, 1, 5, false>(a, stream);
+    default: return launch_lds_cfg<4, 2, 2, 5, false>(a, stream);
+  }
 }
+
+int set_gemm_tile(int tile) { return g_gemm_tile.exchange(tile); }
 
 }  // namespace svdq

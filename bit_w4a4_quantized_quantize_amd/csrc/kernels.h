@@ -76,6 +76,9 @@ hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
 // packed activations (qact holds the packed buffer, ascales unused) and packed
 // weights: each element dequantised once per workgroup into LDS
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream);
+// Process-wide tile shape of launch_gemm_lds: 0 automatic, 1 256 x 320, 2 256 x 256,
+// 3 128 x 320, 4 128 x 160 (not gated: automatic there). Returns the previous value.
+int set_gemm_tile(int tile);
 
 // Linears kept in bf16: y = bf16(x @ w^T + bias), x [M, K], w [N, K], bias [N]
 // or NULL, y [M, N]; K a multiple of 16, M and N below 2^24.

@@ -11,6 +11,7 @@ torch.float8_e4m3fn tensor is accepted and viewed as bytes); wcscales [N];
 wtscale [1]; proj_down [K, R]; proj_up [N, R]; bias [N] or None.
 """
 
+import ctypes
 from dataclasses import dataclass
 from typing import Optional
 
@@ -74,6 +75,15 @@ def _p(t):
 
 def _stream(device=None):
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def set_gemm_tile(tile):
+    """Tile shape of the W4A4 GEMM on packed operands, process-wide (tests and tuning):
+    0 automatic, 1 256 x 320, 2 256 x 256, 3 128 x 320, 4 128 x 160. Returns the previous
+    value. Results are bit-identical for every shape."""
+    prev = ctypes.c_int(0)
+    _lib.check("svdq_set_gemm_tile", _lib.lib().svdq_set_gemm_tile(int(tile), ctypes.byref(prev)))
+    return prev.value
 
 
 def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=None, packed=False,

@@ -101,6 +101,19 @@ const char* svdq_last_error(void);
  * naming the launch, if the device reported an error. */
 int svdq_debug_mode(void);
 
+/* Tile shape of the W4A4 GEMM on packed operands (svdq_gemm_w4a4 with packed
+ * activations, svdq_linear_w4a4 with a packed weight, and the gated and static
+ * variants), for tests and tuning. Process-wide; it applies to launches made
+ * after the call.
+ *   tile 0: automatic (the default): the shape with the fewest estimated rounds
+ *           of workgroups, weighted by each shape's measured time per round;
+ *        1: 256 x 320, 2: 256 x 256, 3: 128 x 320, 4: 128 x 160 outputs per
+ *           workgroup (the gated GEMM cannot take 4 and chooses automatically).
+ * Every shape gives bit-identical results. The previous value goes to *previous
+ * when previous is not NULL. SVDQ_ERR_INVALID (nothing changed) for a tile
+ * outside 0..4. Host only: no device call. */
+int svdq_set_gemm_tile(int tile, int* previous);
+
 /*
  * Activation quantisation quant(x * smooth), and the down-projection of the
  * low-rank branch x @ proj_down (model card, section "What's stored on disk":

@@ -370,3 +370,21 @@ def test_calib_rejections_and_sizes():
     assert L.svdq_calib_lds(0, wg, 0, fake(2), out_b, None) == 2
     assert L.svdq_calib_lds(10, wg, 0, None, out_b, None) == 1
     assert L.svdq_calib_lds(10, wg, 1, fake(2), out_b - 4, None) == 5
+
+
+def test_gemm_tile_override():
+    """svdq_set_gemm_tile is host-only: 0..4 are taken and the previous value comes back;
+    anything else is refused with SVDQ_ERR_INVALID and changes nothing."""
+    L = _lib.lib()
+    prev = ctypes.c_int(-1)
+    assert L.svdq_set_gemm_tile(3, ctypes.byref(prev)) == 0
+    try:
+        assert prev.value == 0
+        for bad in (-1, 5, 99):
+            assert L.svdq_set_gemm_tile(bad, ctypes.byref(prev)) == 8
+            assert "tile" in L.svdq_last_error().decode()
+        assert L.svdq_set_gemm_tile(4, None) == 0
+        assert L.svdq_set_gemm_tile(0, ctypes.byref(prev)) == 0
+        assert prev.value == 4
+    finally:
+        L.svdq_set_gemm_tile(0, None)

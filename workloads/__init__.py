@@ -47,6 +47,13 @@ LAYERS_2048 = {
     "w3": dict(M=M_2048, K=3840, N=10240, R=128, kind="dit", seed=1034),
     "w2": dict(M=M_2048, K=10240, N=3840, R=128, kind="swiglu", seed=1044),
 }
+# One GPU's share of the 1024^2 layers under 8-way tensor parallelism: qkv and w1 split by
+# output columns (N / 8), w2 by input rows (K / 8, 1280 = 80 whole 16-blocks).
+SHARDS_TP8_1024 = {
+    "qkv": dict(M=4096, K=3840, N=11520 // 8, R=128, kind="dit", seed=1052),
+    "w1": dict(M=4096, K=3840, N=10240 // 8, R=128, kind="dit", seed=1053),
+    "w2": dict(M=4096, K=10240 // 8, N=3840, R=128, kind="swiglu", seed=1054),
+}
 
 
 def f32_to_bf16_bits(a):
