@@ -1430,14 +1430,16 @@ def main():
     # ---- per-kernel timings, same stream and rotation, the kernels the step runs ----
     packed = args.layout == "packed"
 
+    # the layer's workspace (at least the quantiser's partial sums) is passed, as the
+    # layer step does, so that no call allocates
     def quant_down(i):
         s = sets[i]
         if packed:
             ops.quantize_act(s["x"], s["layer"].smooth, s["layer"].proj_down, qact=s["qpk"],
-                             lora_act=s["lora"], packed=True)
+                             lora_act=s["lora"], packed=True, workspace=s["ws"])
         else:
             ops.quantize_act(s["x"], s["layer"].smooth, s["layer"].proj_down,
-                             qact=s["qact"], ascales=s["ascales"], lora_act=s["lora"])
+                             qact=s["qact"], ascales=s["ascales"], lora_act=s["lora"], workspace=s["ws"])
 
     for i in range(n_sets):
         quant_down(i)

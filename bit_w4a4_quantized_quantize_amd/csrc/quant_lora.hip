@@ -4,8 +4,10 @@
 // section "What's stored on disk": the activation operand of scaled_mma and
 // the (x @ proj_down) factor of the SVD residual; raw x feeds the residual).
 //
-// Two kernels. With a down-projection, quant_lora_ws_kernel (below) splits each
-// workgroup's waves into quantisers and matrix waves. quant_lora_kernel serves
+// Three kernels. With a down-projection, quant_lora_ws_kernel (below) splits each
+// workgroup's waves into quantisers and matrix waves, with K split across
+// workgroups; for short K, quant_lora_rs_kernel (further below) splits the rank
+// across workgroups instead and needs no partial sums. quant_lora_kernel serves
 // the quantisation alone (R = 0, packed output), the down-projection alone, and
 // the lora_act columns past the first 128.
 //
@@ -613,6 +615,303 @@ int k_splits(int64_t M, int64_t K, int64_t R, bool packed_out) {
   return best;
 }
 
+// Split-free form (R in (64, 128]): no partial sums and no reduction launch. A
+// workgroup owns 32 rows and 64 of the lora_act columns over the whole of K; the
+// two workgroups of a row block are dispatched to the same XCD (blocks 16 g + j and
+// 16 g + 8 + j, j < 8) and quantise alternate 64-K panels between them. Waves 4-7
+// copy x, proj_down and smooth global -> LDS with buffer loads that write LDS
+// directly (the swizzle applied on the source side), in 256-K super-panels, three
+// stages, two ahead, and run the down-projection on v_mfma_f32_16x16x32_bf16: wave
+// 4 + m takes the 64-K sub-panel m of every super-panel, and the four partial sums
+// are added in wave order at the end. Waves 0-3 read their x from LDS and quantise.
+// Only the matrix waves issue loads, so the quantisers' stores never share a vmcnt
+// wait with a load. Every workgroup streams its half of proj_down over all of K, so
+// the L2 traffic grows with K; the launcher uses this form where it is the faster.
+constexpr int kRsCols = 64;
+constexpr int kRsX = 16 * 1024;     // x: 16 blocks (sub-panel i, row group q) of 8 rows x 64 K
+constexpr int kRsPd = 32 * 1024;    // proj_down: 32 blocks of 8 k x 64 columns
+constexpr int kRsSm = 1024;         // smooth: 256 k (512 bytes used)
+constexpr int kRsStage = kRsX + kRsPd + kRsSm;
+constexpr int kRsStages = 3;
+constexpr int kRsLds = kRsStages * kRsStage;
+
+template <int N>
+__device__ __forceinline__ void rs_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void rs_wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// a barrier without the memory fence of __syncthreads (which would wait for the
+// copies of later super-panels); the empty asm keeps LDS accesses on their side
+__device__ __forceinline__ void rs_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+#define RS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// x row r (0..31 of the block), 16-byte piece pc (0..7 of a 64-K sub-panel) at slot
+// pc ^ rs_xswz(r) of its 128-byte LDS row; proj_down row k (0..255 of a super-panel),
+// piece pp (8 columns) at slot pp ^ rs_pswz(k). Both make the fragment reads
+// conflict-free (16-byte reads of 16 rows; transposing 8-byte reads of 8 rows).
+__host__ __device__ constexpr int rs_xswz(int r) { return (r >> 1) & 7; }
+__host__ __device__ constexpr int rs_pswz(int k) { return 4 * ((k >> 3) & 1) + 2 * ((k >> 1) & 1); }
+
+template <bool PACKED, bool STATIC>
+__global__ __launch_bounds__(512) void quant_lora_rs_kernel(QLArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int M = a.M, K = a.K, R = a.R;
+  const int w = (int)blockIdx.x;
+  const int h = (w >> 3) & 1;                  // column half
+  const int b = 8 * (w >> 4) + (w & 7);        // row block
+  const int MP = (M + 31) / 32;
+  if (b >= MP) return;
+  const int m0 = 32 * b;
+  const int r0 = kRsCols * h;
+  const int KP = (K + 63) / 64;
+  const int nsp = (K + 255) / 256;
+  const uint32_t x_bytes = (uint32_t)M * K * 2;
+  const uint32_t pd_bytes = (uint32_t)K * R * 2;
+  const uint32_t code_bytes = (uint32_t)MP * KP * 1024;
+  const uint32_t q_bytes = PACKED ? code_bytes + (uint32_t)MP * KP * 128 : (uint32_t)M * (K / 2);
+  const uint32_t s_bytes = PACKED ? 0u : (uint32_t)(K / 16) * M;
+  auto stage_at = [&](int sp) { return smem + (sp % kRsStages) * kRsStage; };
+
+  if (wave >= 4) {
+    const int mw = wave - 4;
+    const auto rx = make_rsrc(a.x, x_bytes);
+    const auto rpd = make_rsrc(a.proj_down, pd_bytes);
+    const auto rsm = make_rsrc(a.smooth, (uint32_t)K * 2);
+    // copies: x blocks 4 mw + u (u < 4), proj_down blocks 8 mw + u (u < 8), and wave 4
+    // the smooth block; lane l fills slot l of a block (row l / 8, slot l % 8)
+    const int rr = lane >> 3, sl = lane & 7;
+    uint32_t xo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int bi = 4 * mw + u, i = bi >> 2, q = bi & 3;
+      const int r = 8 * q + rr;
+      const int m = m0 + r;
+      xo[u] = m < M ? ((uint32_t)m * K + 64 * i + 8 * (sl ^ rs_xswz(r))) * 2 : x_bytes;
+    }
+    auto issue = [&](int sp) {
+      uint8_t* st = stage_at(sp);
+      const int kb = 256 * sp;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int bi = 4 * mw + u, i = bi >> 2, q = bi & 3;
+        const int pc = sl ^ rs_xswz(8 * q + rr);
+        const bool in = xo[u] < x_bytes && kb + 64 * i + 8 * pc < K;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, RS_LDS(void, st + bi * 1024), 16, in ? xo[u] + kb * 2 : x_bytes,
+                                                 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int beta = 8 * mw + u;
+        const int k = 8 * beta + rr;
+        const int pp = sl ^ rs_pswz(k);
+        const int kg = kb + k, col = r0 + 8 * pp;
+        const uint32_t off = kg < K && col < R ? ((uint32_t)kg * R + col) * 2 : pd_bytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rpd, RS_LDS(void, st + kRsX + beta * 1024), 16, off, 0, 0, 0);
+      }
+      if (mw == 0) {
+        const int k = kb + 8 * lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsm, RS_LDS(void, st + kRsX + kRsPd), 16,
+                                                 lane < 32 && k < K ? k * 2 : K * 2, 0, 0, 0);
+      }
+    };
+
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[t][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // fragments of k-step 2 mw (k-step 2 mw + 1: x pieces 4 further, i.e. slot ^ 4, and
+    // proj_down rows 32 further, 4096 bytes): x rows 16 t + l16 (8 k per lane); transposed
+    // proj_down reads of column tile c (lane (G, jj, qq): row 8 G + jj, columns 16 c + 4 qq,
+    // the rows 4 further 512 bytes on)
+    const int G = lane >> 4, jj = (lane >> 2) & 3, qq = lane & 3, l16 = lane & 15;
+    uint32_t xa[2], pa[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = 16 * t + l16;
+      xa[t] = (mw * 4 + (r >> 3)) * 1024 + (r & 7) * 128 + ((G ^ rs_xswz(r)) << 4);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = 64 * mw + 8 * G + jj;
+      const int pp = 2 * c + (qq >> 1);
+      pa[c] = kRsX + (k >> 3) * 1024 + (k & 7) * 128 + ((pp ^ rs_pswz(k)) << 4) + (qq & 1) * 8;
+    }
+    const uint32_t smem_base = (uint32_t)(uintptr_t)RS_LDS(uint8_t, smem);
+    auto multiply = [&](int stg) {
+      const uint32_t so = smem_base + stg * kRsStage;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 xf[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          xf[t] = *reinterpret_cast<const bf16x8*>(smem + stg * kRsStage + (xa[t] ^ (s << 6)));
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        v2i lo0, hi0, lo1, hi1, lo2, hi2, lo3, hi3;
+        const uint32_t b0 = so + pa[0] + s * 4096, b1 = so + pa[1] + s * 4096;
+        const uint32_t b2 = so + pa[2] + s * 4096, b3 = so + pa[3] + s * 4096;
+        // The eight transposing reads of this k-step, complete when the block ends. As
+        // inline assembly: the builtin carries no alias information, so the compiler
+        // would wait for every direct-to-LDS copy in flight before it.
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %8 offset:512\n\t"
+            "ds_read_b64_tr_b16 %2, %9\n\t"
+            "ds_read_b64_tr_b16 %3, %9 offset:512\n\t"
+            "ds_read_b64_tr_b16 %4, %10\n\t"
+            "ds_read_b64_tr_b16 %5, %10 offset:512\n\t"
+            "ds_read_b64_tr_b16 %6, %11\n\t"
+            "ds_read_b64_tr_b16 %7, %11 offset:512\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(lo0), "=v"(hi0), "=v"(lo1), "=v"(hi1), "=v"(lo2), "=v"(hi2), "=v"(lo3), "=v"(hi3)
+            : "v"(b0), "v"(b1), "v"(b2), "v"(b3)
+            : "memory");
+        bf16x8 pf[4];
+        pf[0] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo0, hi0, 0, 1, 2, 3));
+        pf[1] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo1, hi1, 0, 1, 2, 3));
+        pf[2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3));
+        pf[3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo3, hi3, 0, 1, 2, 3));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[c], xf[t], acc[t][c], 0, 0, 0);
+      }
+    };
+
+    issue(0);
+    if (nsp > 1) issue(1);
+    for (int sp = 0; sp < nsp; ++sp) {
+      // this wave's copies of super-panel sp have landed (those of sp + 1 may not)
+      if (sp + 1 < nsp) {
+        if (mw == 0) rs_wait_vm<13>();
+        else rs_wait_vm<12>();
+      } else {
+        rs_wait_vm<0>();
+      }
+      rs_wait_lgkm0();
+      rs_barrier();   // sp visible to every wave; sp - 1's stage is free
+      if (sp + 2 < nsp) issue(sp + 2);
+      multiply(sp % kRsStages);
+    }
+    rs_wait_lgkm0();
+    rs_barrier();
+    // this wave's partial sums through LDS: row r, 16-byte column slot c4 at c4 ^ (r % 16)
+    float* e = reinterpret_cast<float*>(smem + mw * 8192);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 16 * t + l16;
+        const int c4 = 4 * c + G;
+        *reinterpret_cast<f32x4*>(e + r * 64 + ((c4 ^ (r & 15)) << 2)) = acc[t][c];
+      }
+  } else {
+    const int qw = wave;
+    const int r = 8 * qw + (lane >> 3);
+    const int pc = lane & 7;
+    const int m = m0 + r;
+    const auto rq = make_rsrc(a.qact, q_bytes);
+    const auto rsc = make_rsrc(a.ascales, s_bytes);
+    BlockScale<STATIC> bs;
+    bs.init(a.gscale);
+    auto quantise = [&](const uint8_t* st, int sp, int i) {
+      const int p = 4 * sp + i;
+      const int k = 64 * p + 8 * pc;
+      const u32x4 xv =
+          *reinterpret_cast<const u32x4*>(st + (4 * i + qw) * 1024 + (lane >> 3) * 128 + ((pc ^ rs_xswz(r)) << 4));
+      const u32x4 sv = *reinterpret_cast<const u32x4*>(st + kRsX + kRsPd + (64 * i + 8 * pc) * 2);
+      float v[8];
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = bf16lo_to_f32(xv[e]) * bf16lo_to_f32(sv[e]);
+        v[2 * e + 1] = bf16hi_to_f32(xv[e]) * bf16hi_to_f32(sv[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+      // the other half of the block sits in lane ^ 1
+      amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, false)));
+      const uint32_t sc = bs.code(amax);
+      const float sd = bs.divisor(sc);
+      const float inv = sd > 0.0f ? scale_reciprocal(sd) : 0.0f;
+      uint32_t pk = 0u;
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(v[0] * inv), snap21(v[1] * inv), 1.0f, 0);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(v[2] * inv), snap21(v[3] * inv), 1.0f, 1);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(v[4] * inv), snap21(v[5] * inv), 1.0f, 2);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, snap21(v[6] * inv), snap21(v[7] * inv), 1.0f, 3);
+      const int t4 = pc >> 1, hh = pc & 1;
+      if (PACKED) {
+        // rows of the last 32-row panel beyond M are written (as zeros)
+        const uint32_t chunk = (uint32_t)p * MP + b;
+        __builtin_amdgcn_raw_buffer_store_b32(pk, rq, chunk * 1024 + ((hh * 32 + r) * 4 + t4) * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rq, hh == 0 ? code_bytes + chunk * 128 + r * 4 + t4 : q_bytes,
+                                             0, 0);
+      } else {
+        const bool ok = m < M && k < K;
+        __builtin_amdgcn_raw_buffer_store_b32(pk, rq, ok ? (uint32_t)m * (K / 2) + k / 2 : q_bytes, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rsc, ok && hh == 0 ? (uint32_t)(k >> 4) * M + m : s_bytes, 0,
+                                             0);
+      }
+    };
+    for (int sp = 0; sp < nsp; ++sp) {
+      rs_wait_lgkm0();
+      rs_barrier();
+      const uint8_t* st = stage_at(sp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * sp + i < KP && (i & 1) == h) quantise(st, sp, i);
+    }
+    rs_wait_lgkm0();
+    rs_barrier();
+  }
+  rs_wait_lgkm0();
+  rs_barrier();
+  // lora_act: thread row tid / 16, columns 4 (tid % 16) .. + 3, the four k classes added in order
+  {
+    const int rrow = tid >> 4, c4 = tid & 15;
+    const float* e = reinterpret_cast<const float*>(smem);
+    const int off = rrow * 64 + ((c4 ^ (rrow & 15)) << 2);
+    f32x4 sum = *reinterpret_cast<const f32x4*>(e + off);
+    sum += *reinterpret_cast<const f32x4*>(e + 2048 + off);
+    sum += *reinterpret_cast<const f32x4*>(e + 4096 + off);
+    sum += *reinterpret_cast<const f32x4*>(e + 6144 + off);
+    const int m = m0 + rrow, col = r0 + 4 * c4;
+    if (m < M && col < R) {
+      const u32x2 o = u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+      *reinterpret_cast<u32x2*>(a.lora_act + (size_t)m * R + col) = o;
+    }
+  }
+}
+
+// Which fused form: estimated microseconds, fitted to both kernels over M = 512 ..
+// 16896, K = 1280 .. 10240 at R = 128 on MI355X. The split-free form costs about
+// 1.5 + 0.0047 K per round of 256 workgroups (two per 32 rows), bound by its
+// proj_down traffic from L2; the split form its fitted split model plus ~5 for the
+// partial sums' reduction launch. The split-free form is taken only when it is
+// estimated at least 1 faster (at M = 4096, K = 3840 the two are within a
+// microsecond either way and the split form stays).
+bool use_split_free(int64_t M, int64_t K, int64_t R, bool packed_out) {
+  if (R <= kRsCols || R > 2 * kRsCols) return false;
+  const int64_t wgs = 2 * ((M + 31) / 32);
+  const double rs = 1.5 + (double)((wgs + 255) / 256) * 0.0047 * (double)K;
+  const int ks = k_splits(M, K, R, packed_out);
+  const int64_t row_blocks = (M + kRows - 1) / kRows;
+  const int64_t steps = packed_out ? 2 * ((K + 63) / 64) : (K + 31) / 32;
+  const int64_t rounds = (row_blocks * ks + 255) / 256;
+  const double split = (double)rounds * (double)((steps + ks - 1) / ks) * 0.65 +
+                       (ks > 1 ? (double)ks * (double)M * (double)R * 1.26e-6 : 0.0) + 5.0;
+  return rs + 1.0 < split;
+}
+
 }  // namespace
 
 size_t quant_lora_workspace_bytes(int64_t M, int64_t K, int64_t R) {
@@ -628,6 +927,24 @@ hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const ui
                              const uint16_t* gscale) {
   QLArgs a{x, smooth, proj_down, qact, ascales, lora_act, nullptr, (int)M, (int)K, (int)R, 0, 0, gscale};
   const bool st = gscale != nullptr;
+  if (use_split_free(M, K, R, packed_out)) {
+    const void* fn = packed_out ? (st ? reinterpret_cast<const void*>(&quant_lora_rs_kernel<true, true>)
+                                      : reinterpret_cast<const void*>(&quant_lora_rs_kernel<true, false>))
+                                : (st ? reinterpret_cast<const void*>(&quant_lora_rs_kernel<false, true>)
+                                      : reinterpret_cast<const void*>(&quant_lora_rs_kernel<false, false>));
+    static std::atomic<uint64_t> lds_set[4];
+    hipError_t e = set_lds_limit_once(fn, kRsLds, lds_set[(packed_out ? 2 : 0) + (st ? 1 : 0)]);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)(((M + 31) / 32 + 7) / 8 * 16));
+    if (packed_out) {
+      if (st) hipLaunchKernelGGL((quant_lora_rs_kernel<true, true>), grid, dim3(512), kRsLds, stream, a);
+      else hipLaunchKernelGGL((quant_lora_rs_kernel<true, false>), grid, dim3(512), kRsLds, stream, a);
+    } else {
+      if (st) hipLaunchKernelGGL((quant_lora_rs_kernel<false, true>), grid, dim3(512), kRsLds, stream, a);
+      else hipLaunchKernelGGL((quant_lora_rs_kernel<false, false>), grid, dim3(512), kRsLds, stream, a);
+    }
+    return hipGetLastError();
+  }
   const int ks = k_splits(M, K, R, packed_out);
   const int steps = packed_out ? (int)(2 * ((K + 63) / 64)) : (int)((K + 31) / 32);
   a.split_steps = (steps + ks - 1) / ks;

@@ -74,10 +74,15 @@ def test_linear_full_ffn_shape_sampled_rows(gpu_lib):
     ("qkv_2048px", workloads.LAYERS_2048["qkv"]),
     ("out_2048px", workloads.LAYERS_2048["out"]),
     ("w2_2048px", workloads.LAYERS_2048["w2"]),
+    ("qkv_1024_tp8", workloads.SHARDS_TP8_1024["qkv"]),
+    ("w1_1024_tp8", workloads.SHARDS_TP8_1024["w1"]),
+    ("w2_1024_tp8", workloads.SHARDS_TP8_1024["w2"]),
 ])
 def test_linear_full_size_sampled_rows(gpu_lib, name, cfg):
     """The other full-size layers (fused QKV N = 11520; w2 with K = 10240 on SwiGLU-like
-    inputs; the 2048px token count M = 16896), whole output computed with packed weights
+    inputs; the 2048px token count M = 16896; one GPU's share of the 1024^2 layers under
+    8-way tensor parallelism, whose GEMMs take the 128-row tiles and whose w2 share
+    (K = 1280) takes the split-free quantiser), whole output computed with packed weights
     as the layer runs, 24 sampled rows checked against the oracle."""
     rows = np.sort(np.random.default_rng(cfg["seed"]).choice(cfg["M"], size=24, replace=False))
     rows[0], rows[-1] = 0, cfg["M"] - 1

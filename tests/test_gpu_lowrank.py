@@ -3,8 +3,10 @@ float64 product: each element within bf16 rounding plus fp32 accumulation error.
 
 The down-projection runs inside the fused quantisation kernel: 32 rows per
 workgroup, with K split across workgroups (fp32 partials added in a fixed order
-by a second kernel) when there are few row blocks. Covers split and unsplit K,
-ragged M, R = 16 .. 256, K = 16 and 10240, and determinism.
+by a second kernel) when there are few row blocks, or, for short K, the
+split-free form (each workgroup 32 rows and 64 of the columns over all of K).
+Covers split and unsplit K, the split-free form (ragged M and K, R = 96), ragged
+M, R = 16 .. 256, K = 16 and 10240, and determinism.
 """
 
 import numpy as np
@@ -43,12 +45,18 @@ def check_lora(ops, M, K, R, kind, seed):
     (33, 16, 16, "tiny", 14),           # a single 16-wide K block
     (48, 384, 256, "dit", 15),          # R above one 128-wide chunk
     (300, 3840, 256, "dit", 16),        # K split over 7 workgroups, two R chunks, ragged M
+    (4096, 1280, 128, "swiglu", 17),    # short K: the split-free form (rank split across workgroups)
+    (2049, 1040, 96, "dit", 18),        # split-free, ragged M and K, a half-empty column half
+    (1000, 1040, 128, "dit", 19),       # split-free, a partial last super-panel
 ])
 def test_lora_down(gpu_lib, M, K, R, kind, seed):
     check_lora(gpu_lib, M, K, R, kind, seed)
 
 
-def test_lora_down_deterministic(gpu_lib):
-    a = check_lora(gpu_lib, 4096, 3840, 128, "dit", 1003)
-    b = check_lora(gpu_lib, 4096, 3840, 128, "dit", 1003)
+@pytest.mark.parametrize("K", [3840, 1280])
+def test_lora_down_deterministic(gpu_lib, K):
+    """Both fused forms (K split with ordered partial sums at K = 3840, split-free at
+    K = 1280) give the same bits on every call."""
+    a = check_lora(gpu_lib, 4096, K, 128, "dit", 1003)
+    b = check_lora(gpu_lib, 4096, K, 128, "dit", 1003)
     assert np.array_equal(a, b)

@@ -162,6 +162,9 @@ def _unspecified_rows_mask(M, K):
     (600, 3840, 128, "dit", 52),
     (96, 10240, 128, "swiglu", 53),
     (130, 1024, 0, "dit", 54),       # quantisation alone into the packed layout
+    (4096, 1280, 128, "swiglu", 57), # short K: the split-free fused kernel
+    (2049, 1280, 96, "dit", 58),     # split-free, ragged M, a half-empty second column half
+    (1000, 1040, 128, "dit", 59),    # split-free, K neither a multiple of 64 nor of 256
 ])
 def test_quant_packed_layout_bit_exact(gpu_lib, M, K, R, kind, seed):
     """Packed activation output == the oracle's codes/scales placed by the oracle's
@@ -244,6 +247,8 @@ def test_quant_packed_2048px_sampled_rows(gpu_lib):
     (77, 336, 32, "dit", 55),        # ragged M, K % 64 == 16
     (4096, 3840, 128, "dit", 1003),  # the 1024^2 activation, K split over workgroups
     (40, 10240, 256, "swiglu", 56),  # long K, two 128-wide R chunks
+    (4096, 1280, 128, "swiglu", 60), # short K: the split-free fused kernel
+    (2049, 1040, 96, "dit", 61),     # split-free, ragged M and K
 ])
 def test_quant_canonical_with_down_projection_bit_exact(gpu_lib, M, K, R, kind, seed):
     """Canonical qact/ascales written by the fused quantisation + down-projection

@@ -66,7 +66,7 @@ def _g_for(choice, M, K, kind, seed, sm):
 
 
 @pytest.mark.parametrize("M,K,kind,seed", [(64, 256, "tiny", 1001), (300, 3840, "dit", 61),
-                                           (96, 10240, "swiglu", 62)])
+                                           (96, 10240, "swiglu", 62), (2049, 1040, "dit", 69)])
 @pytest.mark.parametrize("gc", G_CHOICES)
 @pytest.mark.parametrize("R", [0, 128])
 def test_static_quant_canonical_bit_exact(gpu_lib, M, K, kind, seed, gc, R):
@@ -81,7 +81,8 @@ def test_static_quant_canonical_bit_exact(gpu_lib, M, K, kind, seed, gc, R):
         assert np.array_equal(host_u8(q), qd) and np.array_equal(host_u8(s), sd)
 
 
-@pytest.mark.parametrize("M,K,R,seed", [(77, 336, 32, 63), (600, 3840, 128, 64), (130, 1024, 0, 65)])
+@pytest.mark.parametrize("M,K,R,seed", [(77, 336, 32, 63), (600, 3840, 128, 64), (130, 1024, 0, 65),
+                                         (4096, 1280, 128, 68)])   # split-free fused kernel
 @pytest.mark.parametrize("gc", ["calibrated", 3.7e-4])
 def test_static_quant_packed_bit_exact(gpu_lib, M, K, R, seed, gc):
     from tests.test_gpu_quant import _unspecified_rows_mask
