@@ -59,6 +59,10 @@ DEFAULT_WORKLOAD = "ffn_w1_1024"
 FFN_BLOCKS = {
     "ffn_block_1024": (dict(M=4096, K=3840, N=2 * 10240, R=128, kind="dit", seed=1003), "FFN_W2_1024",
                        "DiT FFN block at 1024^2"),
+    # one GPU's share under 8-way tensor parallelism: w1/w3 by columns (F = 1280), w2 by rows
+    "ffn_block_1024_tp8": (dict(M=4096, K=3840, N=2 * 1280, R=128, kind="dit", seed=1053),
+                           ("SHARDS_TP8_1024", "w2"), "one GPU's share of the DiT FFN block at 1024^2 under "
+                           "8-way tensor parallelism (F = 10240 / 8)"),
 }
 
 
@@ -156,7 +160,8 @@ def run_static(args):
         "config": {"workload": f"{desc}: static global activation scale calibrated on another seeded batch "
                                f"(seed {cfg['seed'] + 1000}), per-16 e4m3 block scales relative to it; "
                                f"M={M} K={K} N={N} R={R}",
-                   "cache": "warm" if args.warm else f"cold (rotating {n_sets} sets)"},
+                   "cache": "warm" if args.warm else f"cold (rotating {n_sets} sets)",
+                   **({"gemm_tile_forced": args.gemm_tile} if args.gemm_tile else {})},
         "act_gscale": g_val, "saturated_block_scale_fraction": sat,
         "dynamic_layer_us": round(dyn_ms * 1e3, 2),
         "normwise_static_vs_dynamic": round(dist, 5),
@@ -318,6 +323,9 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="sweep: time eager launches only")
     p.add_argument("--copy-calibration", action="store_true",
                    help="finish with a plain 512 MiB device copy (to calibrate HBM byte counters)")
+    p.add_argument("--gemm-tile", type=int, default=0, choices=[0, 1, 2, 3, 4],
+                   help="force the W4A4 GEMM's tile shape (0 automatic, 1 256x320, 2 256x256, 3 128x320, "
+                        "4 128x160), for comparisons")
     p.add_argument("--condition-ms", type=float, default=30.0,
                    help="minimum untimed device work before timing; conditioning also waits until "
                         "consecutive ~2 ms windows agree within 2%%")
@@ -728,7 +736,8 @@ def run_ffn_block(args):
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     cfg13, w2_name, desc = FFN_BLOCKS[args.workload]
-    cfg2 = dict(getattr(workloads, w2_name))
+    cfg2 = dict(getattr(workloads, w2_name) if isinstance(w2_name, str)
+                else getattr(workloads, w2_name[0])[w2_name[1]])
     M, K, R = cfg13["M"], cfg13["K"], cfg13["R"]
     F_out = cfg13["N"] // 2
     N2 = cfg2["N"]
@@ -837,6 +846,7 @@ def run_ffn_block(args):
             "workload": f"{desc}: gated w1/w3 (one 2F-channel SVDQuant W4A4 layer, h = silu(gate) * up) "
                         f"then w2; M={M} K={K} F={F_out} N2={N2} R={R}",
             "cache": "warm" if args.warm else f"cold (rotating {n_sets} sets)",
+            **({"gemm_tile_forced": args.gemm_tile} if args.gemm_tile else {}),
             "flop_per_step": flops_block,
         },
         "pct_mfma_peak": round(100.0 * tflops / PEAK_F16_MFMA_TFLOPS, 2),
@@ -1301,6 +1311,7 @@ def run_mx(args):
         "config": {"workload": f"{desc}, both operands re-rounded to MXFP4 (E2M1, E8M0 per 32 K); "
                                f"M={M} K={K} N={N} R={R}",
                    "cache": "warm" if args.warm else f"cold (rotating {n_sets} sets)",
+                   **({"gemm_tile_forced": args.gemm_tile} if args.gemm_tile else {}),
                    "flop_per_step": flops_linear},
         "roofline": {
             "kernel": "gemm_mx_kernel (scaled FP4 matrix instruction + low-rank up-projection + epilogue)",
@@ -1345,6 +1356,12 @@ def run_mx(args):
 
 def main():
     args = parse()
+    if args.gemm_tile:
+        from bit_w4a4_quantized_quantize_amd import ops
+        ops.set_gemm_tile(args.gemm_tile)
+        print(f"[bench] W4A4 GEMM tile shape forced to {args.gemm_tile} "
+              f"({ {1: '256x320', 2: '256x256', 3: '128x320', 4: '128x160'}[args.gemm_tile] })",
+              file=sys.stderr, flush=True)
     if args.workload in ORACLE_TIMES:
         return run_oracle_times(args)
     if args.workload in STATIC_VARIANTS:
@@ -1495,6 +1512,7 @@ def main():
             "workload": f"{desc}: SVDQuant W4A4 NVFP4 linear, M={M} K={K} N={N} R={R}",
             "weight_layout": args.layout,
             "cache": "warm" if args.warm else f"cold (rotating {n_sets} sets)",
+            **({"gemm_tile_forced": args.gemm_tile} if args.gemm_tile else {}),
             "flop_per_step": flops_linear,
             "arithmetic": "exact NVFP4 dequant to f16, f16 MFMA with fp32 accumulation; "
                           "low-rank in bf16 MFMA; quantisation in fp32",
