@@ -1447,16 +1447,12 @@ def main():
     # ---- per-kernel timings, same stream and rotation, the kernels the step runs ----
     packed = args.layout == "packed"
 
-    # the layer's workspace (at least the quantiser's partial sums) is passed, as the
-    # layer step does, so that no call allocates
+    # as in the layer step: packed activations (with either weight layout), and the layer's
+    # workspace (at least the quantiser's partial sums) passed so that no call allocates
     def quant_down(i):
         s = sets[i]
-        if packed:
-            ops.quantize_act(s["x"], s["layer"].smooth, s["layer"].proj_down, qact=s["qpk"],
-                             lora_act=s["lora"], packed=True, workspace=s["ws"])
-        else:
-            ops.quantize_act(s["x"], s["layer"].smooth, s["layer"].proj_down,
-                             qact=s["qact"], ascales=s["ascales"], lora_act=s["lora"], workspace=s["ws"])
+        ops.quantize_act(s["x"], s["layer"].smooth, s["layer"].proj_down, qact=s["qpk"],
+                         lora_act=s["lora"], packed=True, workspace=s["ws"])
 
     for i in range(n_sets):
         quant_down(i)
@@ -1464,10 +1460,7 @@ def main():
 
     def gemm(i):
         s = sets[i]
-        if packed:
-            ops.gemm_w4a4(s["qpk"], None, s["lora"], s["layer"], y=s["y"], M=M)
-        else:
-            ops.gemm_w4a4(s["qact"], s["ascales"], s["lora"], s["layer"], y=s["y"])
+        ops.gemm_w4a4(s["qpk"], None, s["lora"], s["layer"], y=s["y"], M=M)
 
     def quant(i):
         s = sets[i]
@@ -1520,8 +1513,7 @@ def main():
         "pct_mfma_peak": round(100.0 * tflops / PEAK_F16_MFMA_TFLOPS, 2),
         "roofline": {
             "kernel": "gemm_lds_kernel (scaled GEMM + low-rank up-projection + epilogue)"
-                      if args.layout == "packed" else
-                      "gemm_w4a4_kernel (scaled GEMM + low-rank up-projection + epilogue)",
+                      + ("" if args.layout == "packed" else ", reading the canonical weight layout"),
             "bound": "mfma",
             "achieved": round(gemm_tflops, 2),
             "peak": PEAK_F16_MFMA_TFLOPS,

@@ -383,8 +383,6 @@ static int validate_gemm(const void* qact, const void* ascales, int act_layout, 
     if (act_layout == SVDQ_ACT_PACKED) {
       if (ascales != nullptr)
         return fail(SVDQ_ERR_INVALID, "ascales must be NULL with packed activations");
-      if (weight_layout != SVDQ_WEIGHT_PACKED)
-        return fail(SVDQ_ERR_INVALID, "packed activations need the packed weight layout");
       const char* names[] = {"qact"};
       const void* ptrs[] = {qact};
       if ((st = check_ptrs(names, ptrs, 1))) return st;
@@ -524,15 +522,14 @@ static int linear_impl(const void* x, const void* smooth, const void* gscale, co
 
   char* w = static_cast<char*>(workspace);
   const bool packed = weight_layout == SVDQ_WEIGHT_PACKED;
+  // activations always go to the packed layout; the GEMM reads either weight layout
   void* qact = w + ws.act;
-  void* ascales = packed ? nullptr : (void*)(w + ws.ascales);
   void* lora = R > 0 ? (void*)(w + ws.lora) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   void* scratch = ws.total > ws.partial ? (void*)(w + ws.partial) : nullptr;
-  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora, scratch, packed, s, gscale))) return st;
+  if ((st = run_quantize(x, smooth, M, K, proj_down, R, qact, nullptr, lora, scratch, true, s, gscale))) return st;
   svdq::GemmArgs a{};
   a.qact = static_cast<const uint8_t*>(qact);
-  a.ascales = static_cast<const uint8_t*>(ascales);
   a.lora_act = static_cast<const uint16_t*>(lora);
   a.weight = static_cast<const uint8_t*>(weight);
   a.wscales = static_cast<const uint8_t*>(wscales);
@@ -544,7 +541,7 @@ static int linear_impl(const void* x, const void* smooth, const void* gscale, co
   a.M = M; a.N = N; a.K = K; a.R = R;
   a.packed = packed;
   a.act_gscale = static_cast<const uint16_t*>(gscale);
-  hipError_t e = packed ? svdq::launch_gemm_lds(a, s) : svdq::launch_gemm_w4a4(a, s);
+  hipError_t e = svdq::launch_gemm_lds(a, s);
   if (int st_ = launched(e, "gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }

@@ -73,8 +73,8 @@ struct GemmArgs {
 };
 // canonical activations (LDS-staged), canonical or packed weights
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
-// packed activations (qact holds the packed buffer, ascales unused) and packed
-// weights: each element dequantised once per workgroup into LDS
+// packed activations (qact holds the packed buffer, ascales unused) and the weight
+// packed or canonical (`packed`): each element dequantised once per workgroup into LDS
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream);
 // Process-wide tile shape of launch_gemm_lds: 0 automatic, 1 256 x 320, 2 256 x 256,
 // 3 128 x 320, 4 128 x 160 (not gated: automatic there). Returns the previous value.

@@ -283,7 +283,7 @@ def gemm_w4a4(qact, ascales, lora_act, w: SVDQLinearWeights, y=None, M=None):
 
     Canonical activations: qact [M, K/2], ascales [K/16, M]. Packed activations
     (from quantize_act(..., packed=True)): qact is the packed buffer, ascales
-    None, and M must be given; the layer's weight must be packed too.
+    None, and M must be given. Either weight layout goes with either.
     """
     dev = _check_layer(w)
     K = w.K
@@ -292,8 +292,6 @@ def gemm_w4a4(qact, ascales, lora_act, w: SVDQLinearWeights, y=None, M=None):
     if act_packed:
         if M is None:
             raise ValueError("M is required with packed activations")
-        if w.layout != WEIGHT_PACKED:
-            raise ValueError("packed activations need the packed weight layout (use .packed())")
         _need(qact, "qact (packed)", torch.uint8, 1, min_numel=L.svdq_packed_act_bytes(M, K))
     else:
         _need(qact, "qact", torch.uint8, 2)

@@ -171,8 +171,8 @@ int svdq_unpack_weight(const void* packed, size_t packed_bytes, int64_t N, int64
  *             + lora_act @ proj_up^T + bias[n] )
  *
  *   qact [M, K/2] u8 + ascales [K/16, M] u8 (act_layout SVDQ_ACT_CANONICAL), or
- *     a packed activation buffer with ascales NULL (SVDQ_ACT_PACKED; needs
- *     SVDQ_WEIGHT_PACKED weights); lora_act [M, R] bf16 (R > 0)
+ *     a packed activation buffer with ascales NULL (SVDQ_ACT_PACKED), with either
+ *     weight layout; lora_act [M, R] bf16 (R > 0)
  *   weight: qweight [N, K/2] (SVDQ_WEIGHT_CANONICAL, wscales [K/16, N] given)
  *           or a packed buffer (SVDQ_WEIGHT_PACKED, wscales NULL)
  *   wcscales [N] bf16, wtscale [1] bf16, proj_up [N, R] bf16 (R > 0), bias [N] bf16 or NULL
@@ -188,8 +188,8 @@ int svdq_gemm_w4a4(const void* qact, const void* ascales, int act_layout, const 
                    void* y, void* stream);
 
 /*
- * The whole layer: svdq_quantize_act into the workspace, then svdq_gemm_w4a4
- * (activations packed in the workspace when the weight is packed).
+ * The whole layer: svdq_quantize_act into the workspace (packed activations),
+ * then svdq_gemm_w4a4 on them with the weight in either layout.
  *   x [M, K] bf16, smooth [K] bf16, weight/wscales/weight_layout as above,
  *   wcscales, wtscale, proj_down [K, R], proj_up [N, R], bias (or NULL),
  *   y [M, N] bf16; workspace of at least svdq_linear_workspace_bytes(M, N, K, R)

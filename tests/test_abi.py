@@ -139,7 +139,6 @@ def gemm(**kw):
     (dict(lora=None), 1), (dict(bias=fake(9) + 2), 4), (dict(weight=fake(4) + 1), 4),
     (dict(y=fake(1)), 6), (dict(y=fake(6) - 64), 6),
     (dict(act_layout=3), 8), (dict(act_layout=1), 8),                         # ascales must be NULL
-    (dict(act_layout=1, ascales=None), 8),                                     # needs packed weights
     (dict(act_layout=1, ascales=None, layout=1, wscales=None, qact=None), 1),
     (dict(act_layout=1, ascales=None, layout=1, wscales=None, M=1 << 20, K=1 << 12), 3),   # packed act > 2 GiB
     (dict(act_layout=1, ascales=None, layout=1, wscales=None, N=1 << 20, K=1 << 12), 3),   # packed weight > 2 GiB

@@ -144,6 +144,29 @@ def test_gemm_packed_activations(gpu_lib, cfg):
     assert S.normwise_rel_err(F.bf16_to_f64(a), y64) <= TOL
 
 
+@pytest.mark.parametrize("cfg", [
+    dict(M=77, K=336, N=200, R=32, kind="dit", seed=41),        # K % 64 == 16: the last canonical row segment is half past K
+    dict(M=300, K=1040, N=650, R=16, kind="dit", seed=42),
+    dict(M=33, K=16, N=40, R=0, kind="tiny", seed=43),          # one 16-K block
+])
+def test_gemm_packed_activations_canonical_weight(gpu_lib, cfg):
+    """Packed activations with the weight in its on-disk layout (read by the kernel without
+    the load-time repack): bit-identical to the packed weight, and within the oracle's gate."""
+    from oracle import repack as P
+    d, layer, qact, ascales, lora_bits = _oracle_inputs(cfg, True, False)
+    R = d["R"]
+    qpk = dev_u8(P.repack(qact, ascales))
+    lora = dev_bf16(lora_bits) if R > 0 else None
+    y_c = gpu_lib.gemm_w4a4(qpk, None, lora, layer, M=d["M"])
+    y_p = gpu_lib.gemm_w4a4(qpk, None, lora, layer.packed(), M=d["M"])
+    torch.cuda.synchronize()
+    a, b = host_bits(y_c), host_bits(y_p)
+    assert np.array_equal(a, b)
+    y64 = S.gemm_w4a4(qact, ascales, F.bf16_to_f64(lora_bits) if R > 0 else None, d["qweight"],
+                      d["wscales"], d["wcscales"], d["wtscale"], d["proj_up"] if R > 0 else None, d["bias"])
+    assert S.normwise_rel_err(F.bf16_to_f64(a), y64) <= TOL
+
+
 def test_gemm_packed_full_ffn_shape_sampled_rows(gpu_lib):
     from oracle import repack as P
     cfg = workloads.FFN_W1_1024

@@ -8,8 +8,10 @@ tiling bug (a wrong row or column offset, a missed ragged edge, a chunk dealt to
 wrong wave). The gated GEMM has no 128 x 160 shape: forcing 4 there falls back to the
 automatic choice, which must still give the same result.
 
-Cases: ragged M and N over several tiles of every shape, K not a multiple of the 64-wide
-panel, R = 0, a rank in three residual passes, one GPU's share of the 1024^2 FFN w1
+Each case also runs the canonical (on-disk) weight layout, which the kernel reads without a
+repack, and requires the same bits. Cases: ragged M and N over several tiles of every shape,
+K not a multiple of the 64-wide panel (so K not a multiple of 32 inside a canonical row), R = 0,
+a rank in three residual passes, one GPU's share of the 1024^2 FFN w1
 under 8-way tensor parallelism (N = 1280, where the automatic choice is 128 x 160) on
 sampled rows, and the gated step with and without w2's quantisation in its epilogue.
 """
@@ -36,6 +38,8 @@ def tile_reset(gpu_lib):
 
 
 def _gemm_all_tiles(ops, d, layer, qact, ascales, lora_bits):
+    """Packed activations with the packed weight under every tile shape; the same with the
+    canonical (on-disk) weight, read by the kernel without a repack, must agree bit for bit."""
     R = d["R"]
     qpk = dev_u8(P.repack(qact, ascales))
     lora = dev_bf16(lora_bits) if R > 0 else None
@@ -44,8 +48,10 @@ def _gemm_all_tiles(ops, d, layer, qact, ascales, lora_bits):
     for t in TILES:
         ops.set_gemm_tile(t)
         y = ops.gemm_w4a4(qpk, None, lora, pl, M=d["M"])
+        yc = ops.gemm_w4a4(qpk, None, lora, layer, M=d["M"])
         torch.cuda.synchronize()
         out[t] = host_bits(y)
+        assert np.array_equal(host_bits(yc), out[t]), f"tile {t}: canonical weight differs from packed"
     ops.set_gemm_tile(0)
     return out
 
