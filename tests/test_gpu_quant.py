@@ -107,6 +107,58 @@ def test_quant_exact_ties_signed_zeros_and_special_blocks(gpu_lib):
     assert_exact(gpu_lib, x, sm)
 
 
+def _special_blocks(M, K, seed):
+    """x [M, K] (bf16 bits) whose 16-blocks cycle through six kinds: exact E2M1 midpoints
+    times a normal e4m3 scale with amax = 6 s (ties), all zero with negative zeros, values
+    whose scale underflows to 0 (signs kept), subnormal scales, saturating (amax/6 > 448), and
+    ordinary normal values."""
+    rng = np.random.default_rng(seed)
+    nb = K // 16
+    mi, bi = np.meshgrid(np.arange(M), np.arange(nb), indexing="ij")
+    kind = (mi + bi) % 6
+    sc = F.e4m3_decode(rng.integers(0x08, 0x70, size=(M, nb)).astype(np.uint8))
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    blk = np.zeros((M, nb, 16))
+    k0 = (kind == 0)[..., None]
+    signs = np.where(rng.random((M, nb, 7)) < 0.5, 1.0, -1.0)
+    blk[..., 0:1] = np.where(k0, 6 * sc[..., None], 0.0)
+    blk[..., 1:8] = np.where(k0, mids * sc[..., None] * signs, 0.0)
+    blk[..., 8:15] = np.where(k0, mids[::-1] * sc[..., None], 0.0)
+    noise = rng.standard_normal((M, nb, 16))
+    for k, factor in ((2, 2.0 ** -24), (3, 2.0 ** -7), (4, 5000.0), (5, 1.0)):
+        blk = np.where((kind == k)[..., None], noise * factor, blk)
+    x = F.f64_to_bf16(blk.reshape(M, K))
+    neg0 = np.zeros((M, nb, 16), dtype=bool)
+    neg0[..., 0::3] = True
+    x[(neg0 & (kind == 1)[..., None]).reshape(M, K)] = 0x8000
+    return x
+
+
+@pytest.mark.parametrize("K", [1280, 3840])
+@pytest.mark.parametrize("packed", [True, False])
+def test_fused_quant_special_blocks_bit_exact(gpu_lib, K, packed):
+    """The special blocks above through the fused quantise + down-projection kernels (R = 128,
+    M = 2048): the split-free form at K = 1280 and the K-split form at K = 3840, in both
+    output layouts. Codes and scales equal the oracle's bit for bit; each fused kernel has its
+    own copy of the quantisation, so the tie, zero and saturation rules are pinned in each."""
+    from oracle import repack as P
+    M, R = 2048, 128
+    x = _special_blocks(M, K, 31 + K)
+    sm = F.f64_to_bf16(np.where(np.arange(K) % 3 == 0, 0.5, 1.0))
+    pd = F.f64_to_bf16(np.random.default_rng(32).standard_normal((K, R)) * 0.02)
+    q_ref, s_ref = S.quantize_act(x, sm)
+    if packed:
+        buf, _, _ = gpu_lib.quantize_act(dev_bf16(x), dev_bf16(sm), dev_bf16(pd), packed=True)
+        torch.cuda.synchronize()
+        q, s = P.unpack(host_u8(buf), M, K)
+    else:
+        qt, st, _ = gpu_lib.quantize_act(dev_bf16(x), dev_bf16(sm), dev_bf16(pd))
+        torch.cuda.synchronize()
+        q, s = host_u8(qt), host_u8(st)
+    assert np.array_equal(s, s_ref), f"scales differ at {np.argwhere(s != s_ref)[:4].tolist()}"
+    assert np.array_equal(q, q_ref), f"codes differ at {np.argwhere(q != q_ref)[:4].tolist()}"
+
+
 def test_quant_random_bit_patterns(gpu_lib):
     """Arbitrary finite bf16 bit patterns (wide exponent range) times a random smooth."""
     rng = np.random.default_rng(23)
