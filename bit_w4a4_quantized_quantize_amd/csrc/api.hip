@@ -446,8 +446,10 @@ int svdq_gemm_w4a4(const void* qact, const void* ascales, int act_layout, const 
   a.y = static_cast<uint16_t*>(y);
   a.M = M; a.N = N; a.K = K; a.R = R;
   a.packed = weight_layout == SVDQ_WEIGHT_PACKED;
-  hipError_t e = act_packed ? svdq::launch_gemm_lds(a, static_cast<hipStream_t>(stream))
-                            : svdq::launch_gemm_w4a4(a, static_cast<hipStream_t>(stream));
+  // the LDS-dequantising kernel unless both operands are canonical
+  a.act_canonical = act_packed ? 0 : 1;
+  hipError_t e = act_packed || a.packed ? svdq::launch_gemm_lds(a, static_cast<hipStream_t>(stream))
+                                        : svdq::launch_gemm_w4a4(a, static_cast<hipStream_t>(stream));
   if (int st_ = launched(e, "gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }

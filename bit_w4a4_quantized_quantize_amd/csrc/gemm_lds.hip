@@ -81,14 +81,15 @@ struct LdsCfg {
 // 16-block is two 8-column pieces held by an even lane and the next one in the
 // store loop below, so the block maximum takes one lane swap; an output tile
 // holds whole blocks (its width is a multiple of 32 columns).
-// CW: the weight in the canonical on-disk layout (qweight [N, K/2], low nibble first;
-// wscales [K/16, N]) rather than the packed buffer, for callers that skip the load-time
-// repack. A lane then loads 16 bytes of one weight row (row l % 32, k from 32 (l / 32) in
-// the panel) and one v_permlane32_swap per pair of dwords regroups them into the packed
-// layout's per-lane order (lane (h, c): the four 8-code runs at k = 16 t + 8 h); the four
-// block scales come from byte loads. From there on the kernel is the same, so both layouts
-// give identical results.
-template <int WM, int WN, int TM, int TN, bool GATED, bool Q2 = false, bool CW = false>
+// CA / CW: the activations / the weight in the canonical layout (codes [rows, K/2], low
+// nibble first; e4m3 scales [K/16, rows]) rather than the packed buffer, for callers that
+// skip the load-time repack or hold canonical activations (not both at once: that
+// combination takes the older canonical kernel). A lane then loads 16 bytes of one row
+// (row l % 32, k from 32 (l / 32) in the panel) and one v_permlane32_swap per pair of dwords
+// regroups them into the packed layout's per-lane order (lane (h, c): the four 8-code runs at
+// k = 16 t + 8 h); the four block scales come from byte loads. From there on the kernel is
+// the same, so both layouts give identical results.
+template <int WM, int WN, int TM, int TN, bool GATED, bool Q2 = false, bool CA = false, bool CW = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   using C = LdsCfg<WM, WN, TM, TN>;
   static_assert(!GATED || WN == 2, "the gated epilogue pairs the two wave columns");
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   // bytes of each operand buffer (codes, and the canonical scales); the buffer resources are
   // built after choosing the operand, since a select between two resources is lowered
   // through a private-memory array
-  const uint32_t qa_bytes = a_code_bytes + (uint32_t)KP * MP * 128;
+  const uint32_t qa_bytes = CA ? (uint32_t)M * (uint32_t)(K / 2) : a_code_bytes + (uint32_t)KP * MP * 128;
   const uint32_t qb_bytes = CW ? (uint32_t)N * (uint32_t)(K / 2) : b_code_bytes + (uint32_t)KP * NP * 128;
 
   // chunk c = wave + kWaves * s; A chunks first. Out-of-range panels read as zero.
@@ -147,13 +148,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
     const bool is_a = c < C::kChunksA;
     const bool in = is_a ? mp0 + c < MP : b_panel_in(c - C::kChunksA);
     const int row = is_a ? mp0 + c : b_panel(c - C::kChunksA);
-    if (CW && !is_a) {   // uniform per wave: every lane takes part in the swaps
-      const int rows_total = N;
+    if ((CA && is_a) || (CW && !is_a)) {   // uniform per wave: every lane takes part in the swaps
+      const int rows_total = is_a ? M : N;
       const int r = 32 * row + l32;
       const int kb = 64 * kp + 32 * h;       // k of this lane's first code
       const bool rin = in && r < rows_total;
-      const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.weight, qb_bytes);
-      const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.wscales, (uint32_t)(K / 16) * rows_total);
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(is_a ? a.qact : a.weight, is_a ? qa_bytes : qb_bytes);
+      const __amdgpu_buffer_rsrc_t rsc = make_rsrc(is_a ? a.ascales : a.wscales, (uint32_t)(K / 16) * rows_total);
       u32x4 v = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, rin && kb < K ? (uint32_t)r * (K / 2) + kb / 2 : 0x80000000u,
                                                        0, 0));
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs a) {
   }
 }
 
-template <int WM, int WN, int TM, int TN, bool GATED, bool Q2 = false, bool CW = false>
+template <int WM, int WN, int TM, int TN, bool GATED, bool Q2 = false, bool CA = false, bool CW = false>
 hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
   using C = LdsCfg<WM, WN, TM, TN>;
   const int64_t col_tiles = GATED ? ((a.gated_f + 31) / 32 + TN - 1) / TN : (a.N + C::BN - 1) / C::BN;
@@ -478,11 +479,11 @@ hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
   const unsigned lds = C::lds_bytes(GATED);
   static_assert(C::lds_bytes(GATED) <= 160 * 1024, "LDS per workgroup");
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN, GATED, Q2, CW>),
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_lds_kernel<WM, WN, TM, TN, GATED, Q2, CA, CW>),
                                     (int)lds, lds_set);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((gemm_lds_kernel<WM, WN, TM, TN, GATED, Q2, CW>), grid, dim3(C::kThreads), lds, stream, a);
+  hipLaunchKernelGGL((gemm_lds_kernel<WM, WN, TM, TN, GATED, Q2, CA, CW>), grid, dim3(C::kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -490,13 +491,14 @@ hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t stream) {
 
 static std::atomic<int> g_gemm_tile{0};
 
-template <bool CW>
+template <bool CA, bool CW>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream, int pick) {
+  static_assert(!(CA && CW), "canonical activations and weights together take the older kernel");
   switch (pick) {
-    case 1: return launch_lds_cfg<4, 2, 2, 4, false, false, CW>(a, stream);
-    case 2: return launch_lds_cfg<4, 2, 1, 5, false, false, CW>(a, stream);
-    case 3: return launch_lds_cfg<4, 1, 1, 5, false, false, CW>(a, stream);
-    default: return launch_lds_cfg<4, 2, 2, 5, false, false, CW>(a, stream);
+    case 1: return launch_lds_cfg<4, 2, 2, 4, false, false, CA, CW>(a, stream);
+    case 2: return launch_lds_cfg<4, 2, 1, 5, false, false, CA, CW>(a, stream);
+    case 3: return launch_lds_cfg<4, 1, 1, 5, false, false, CA, CW>(a, stream);
+    default: return launch_lds_cfg<4, 2, 2, 5, false, false, CA, CW>(a, stream);
   }
 }
 
@@ -536,7 +538,11 @@ hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream) {
       return q2 ? launch_lds_cfg<4, 2, 1, 5, true, true>(a, stream) : launch_lds_cfg<4, 2, 1, 5, true>(a, stream);
     return q2 ? launch_lds_cfg<4, 2, 2, 5, true, true>(a, stream) : launch_lds_cfg<4, 2, 2, 5, true>(a, stream);
   }
-  return a.packed ? launch_tile<false>(a, stream, pick) : launch_tile<true>(a, stream, pick);
+  if (a.act_canonical) {
+    if (!a.packed) return hipErrorInvalidValue;   // both canonical: not this kernel
+    return launch_tile<true, false>(a, stream, pick);
+  }
+  return a.packed ? launch_tile<false, false>(a, stream, pick) : launch_tile<false, true>(a, stream, pick);
 }
 
 int set_gemm_tile(int tile) { return g_gemm_tile.exchange(tile); }

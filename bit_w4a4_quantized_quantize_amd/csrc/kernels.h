@@ -70,11 +70,16 @@ struct GemmArgs {
   // into next_qact, the packed activation layout of [M, F] (F % 64 == 0), or NULL
   const uint16_t* next_smooth = nullptr;
   uint8_t* next_qact = nullptr;
+  // launch_gemm_lds: activations in the canonical layout (qact [M, K/2], ascales [K/16, M])
+  // instead of the packed buffer; only with the packed weight (canonical activations with
+  // the canonical weight go to launch_gemm_w4a4)
+  int act_canonical = 0;
 };
 // canonical activations (LDS-staged), canonical or packed weights
 hipError_t launch_gemm_w4a4(const GemmArgs& a, hipStream_t stream);
-// packed activations (qact holds the packed buffer, ascales unused) and the weight
-// packed or canonical (`packed`): each element dequantised once per workgroup into LDS
+// activations packed (qact holds the packed buffer) or canonical (act_canonical) and the
+// weight packed or canonical (`packed`), not both canonical: each element dequantised once
+// per workgroup into LDS
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t stream);
 // Process-wide tile shape of launch_gemm_lds: 0 automatic, 1 256 x 320, 2 256 x 256,
 // 3 128 x 320, 4 128 x 160 (not gated: automatic there). Returns the previous value.

@@ -9,7 +9,7 @@ wrong wave). The gated GEMM has no 128 x 160 shape: forcing 4 there falls back t
 automatic choice, which must still give the same result.
 
 Each case also runs the canonical (on-disk) weight layout, which the kernel reads without a
-repack, and requires the same bits. Cases: ragged M and N over several tiles of every shape,
+repack, and canonical activations with the packed weight, and requires the same bits. Cases: ragged M and N over several tiles of every shape,
 K not a multiple of the 64-wide panel (so K not a multiple of 32 inside a canonical row), R = 0,
 a rank in three residual passes, one GPU's share of the 1024^2 FFN w1
 under 8-way tensor parallelism (N = 1280, where the automatic choice is 128 x 160) on
@@ -39,19 +39,23 @@ def tile_reset(gpu_lib):
 
 def _gemm_all_tiles(ops, d, layer, qact, ascales, lora_bits):
     """Packed activations with the packed weight under every tile shape; the same with the
-    canonical (on-disk) weight, read by the kernel without a repack, must agree bit for bit."""
+    canonical (on-disk) weight read without a repack, and canonical activations with the
+    packed weight, must agree bit for bit."""
     R = d["R"]
     qpk = dev_u8(P.repack(qact, ascales))
     lora = dev_bf16(lora_bits) if R > 0 else None
     pl = layer.packed()
+    qc, sc = dev_u8(qact), dev_u8(ascales)
     out = {}
     for t in TILES:
         ops.set_gemm_tile(t)
         y = ops.gemm_w4a4(qpk, None, lora, pl, M=d["M"])
         yc = ops.gemm_w4a4(qpk, None, lora, layer, M=d["M"])
+        ya = ops.gemm_w4a4(qc, sc, lora, pl)
         torch.cuda.synchronize()
         out[t] = host_bits(y)
         assert np.array_equal(host_bits(yc), out[t]), f"tile {t}: canonical weight differs from packed"
+        assert np.array_equal(host_bits(ya), out[t]), f"tile {t}: canonical activations differ from packed"
     ops.set_gemm_tile(0)
     return out
 
