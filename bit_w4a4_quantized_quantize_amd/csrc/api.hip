@@ -881,8 +881,8 @@ static int check_mx(int64_t rows, int64_t K, int64_t R) {
   if (st) return st;
   if (K % 128 != 0)
     return fail(SVDQ_ERR_UNSUPPORTED, "K = %lld: the MXFP4 variant needs K a multiple of 128", (long long)K);
-  if ((int64_t)svdq::mx_codes_bytes(rows, K) >= (int64_t(1) << 31))
-    return fail(SVDQ_ERR_UNSUPPORTED, "MXFP4 operand of %lld rows exceeds 2 GiB", (long long)rows);
+  if ((int64_t)svdq::mx_codes_bytes(rows, K) >= (int64_t(1) << 31) || rows * R * 2 >= (int64_t(1) << 31))
+    return fail(SVDQ_ERR_UNSUPPORTED, "MXFP4 operand or low-rank factor of %lld rows exceeds 2 GiB", (long long)rows);
   return SVDQ_OK;
 }
 

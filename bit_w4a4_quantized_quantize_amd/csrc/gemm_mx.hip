@@ -128,11 +128,15 @@ __global__ void reround_mx_kernel(const uint8_t* __restrict__ qweight, const uin
 
 // ---------------------------------------------------------------------------
 // GEMM: 8 waves (4 x 2), tile 256 x (32 TN 2), 128-K panels (two matrix-
-// instruction K steps) in S LDS stages, all copied by direct global-to-LDS
-// loads: per chunk and panel two 1 KB code blocks and its 128 scale bytes (4
-// blocks x 32 rows, one 4-byte piece per lane of half a wave), so every panel
-// costs each wave the same number of copies and one vmcnt wait per panel covers
-// it. Epilogue as in gemm_lds.hip.
+// instruction K steps) in S LDS stages, all copied buffer-to-LDS: per chunk and
+// panel two 1 KB code blocks and its 128 scale bytes (4 blocks x 32 rows, one
+// 4-byte piece per lane of half a wave). The rank-R residual follows as further
+// panels of the same stage ring (two 16-wide R steps each, lora_act and proj_up
+// rows in the code blocks' places), so its copies are issued while the last
+// matrix panels multiply. Every panel, matrix or residual, costs each wave the
+// same number of copies, so one vmcnt count per panel holds throughout. The
+// tile's alpha = wtscale * wcscales and bias are staged in LDS at the start.
+// Output staging as in gemm_lds.hip.
 // ---------------------------------------------------------------------------
 
 constexpr int kGroupM = 4;
@@ -149,6 +153,17 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
+// Buffer-to-LDS copies of 16 and 4 bytes per lane. Device functions rather than
+// calls inside the kernel's lambdas: the host compilation pass of a lambda rejects
+// the 16-byte form (a gfx950 feature) without a diagnostic and then emits no
+// launch stub for the kernel.
+__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(lds), 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf_to_lds4(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(lds), 4, voff, soff, 0, 0);
+}
+
 template <int WM, int WN, int TM, int TN, int S>
 struct MxCfg {
   static constexpr int kWaves = WM * WN;
@@ -163,16 +178,18 @@ struct MxCfg {
   static constexpr int kPerWave = kFull + (kRest ? 1 : 0);
   static constexpr int kCodeBytes = kChunks * 2048;                 // two 1 KB K steps per chunk
   static constexpr int kStageBytes = kCodeBytes + kChunks * 128;     // + 4 scale blocks x 32 rows
-  static constexpr int kLdsBytes = S * kStageBytes;
-  static constexpr int kResSteps = kLdsBytes / (kChunks * 1024);    // R/16 steps per residual pass
+  static constexpr int kAlphaOff = S * kStageBytes;                  // f32 alpha [BN], then f32 bias [BN]
+  static constexpr int kLdsBytes = kAlphaOff + 8 * BN;
   static constexpr int kOutBytes = kWaves * 32 * (32 * TN) * 2;
-  static_assert(kOutBytes <= kLdsBytes, "output staging fits");
+  static_assert(kOutBytes <= kAlphaOff, "output staging fits below the column factors");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+  static_assert(S >= 2 && S <= 4, "panel waits cover up to S - 2 = 2 later panels");
+  static_assert((S - 2) * kPerWave * 3 < 64, "vmcnt range");
 };
 
 template <int WM, int WN, int TM, int TN, int S>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxGemmArgs a) {
   using C = MxCfg<WM, WN, TM, TN, S>;
-  static_assert((S - 2) * C::kPerWave * 3 < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -183,8 +200,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxGemmArgs a) {
   const int wave_m = wave % WM;
   const int wave_n = wave / WM;
 
-  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K, R = (int)a.R;
   const int KP = K / 128;
+  const int r_steps = R / 16;
+  const int RP = (r_steps + 1) / 2;   // residual panels
+  const int TP = KP + RP;
   const int MP = (M + 31) / 32;
   const int NP = (N + 31) / 32;
   const int NBX = (N + C::BN - 1) / C::BN;
@@ -201,35 +221,58 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxGemmArgs a) {
   const int mp0 = by * (C::BM / 32);
   const int np0 = bx * (C::BN / 32);
 
-  // this wave's chunks: c = wave + kWaves * s (A chunks first); panels past the
-  // tensor read the last panel (their results are never stored)
-  const uint8_t* src[C::kPerWave];
-  const uint8_t* ssrc[C::kPerWave];   // this lane's 4 scale bytes (lanes 0..31): block l/8, rows 4(l%8)..
-  int rows_of[C::kPerWave];
+  // this wave's chunks c = wave + kWaves * s (A chunks first) as row-panel indices;
+  // panels past the tensor read the last panel (their results are never stored)
+  int pan[C::kPerWave];
 #pragma unroll
   for (int s = 0; s < C::kPerWave; ++s) {
     const int c = min(wave + C::kWaves * s, C::kChunks - 1);
-    const bool is_a = c < C::kChunksA;
-    const int p = is_a ? min(mp0 + c, MP - 1) : min(np0 + c - C::kChunksA, NP - 1);
-    rows_of[s] = is_a ? MP : NP;
-    src[s] = (is_a ? a.act_codes : a.w_codes) + (size_t)p * 1024 + lane * 16;
-    ssrc[s] = (is_a ? a.act_scales : a.w_scales) + (size_t)((lane >> 3) & 3) * rows_of[s] * 32 + p * 32 +
-              4 * (lane & 7);
+    pan[s] = c < C::kChunksA ? min(mp0 + c, MP - 1) : min(np0 + c - C::kChunksA, NP - 1);
   }
+  const uint32_t a_code_bytes = (uint32_t)MP * 32 * (uint32_t)(K / 2);
+  const uint32_t w_code_bytes = (uint32_t)NP * 32 * (uint32_t)(K / 2);
   const bool extra = C::kRest && wave < C::kRest;
+
+  // column factors, loaded before the panels so that the first panel wait covers them
+  float* lds_alpha = reinterpret_cast<float*>(smem + C::kAlphaOff);
+  float* lds_bias = lds_alpha + C::BN;
+  uint32_t wc_raw = 0, b_raw = 0;
+  if (tid < C::BN) {
+    const int col = np0 * 32 + tid;
+    if (col < N) {
+      wc_raw = a.wcscales[col];
+      if (a.bias != nullptr) b_raw = a.bias[col];
+    }
+  }
 
   auto stage_at = [&](int kp) { return smem + (kp % S) * C::kStageBytes; };
   auto copy_chunk = [&](int s, int kp) {
     const int c = wave + C::kWaves * s;
+    const bool is_a = c < C::kChunksA;
     uint8_t* st = stage_at(kp);
+    if (kp < KP) {
+      const int rows = is_a ? MP : NP;
+      const auto rc = make_rsrc(is_a ? a.act_codes : a.w_codes, is_a ? a_code_bytes : w_code_bytes);
+      const auto rsc = make_rsrc(is_a ? a.act_scales : a.w_scales, (uint32_t)(K / 32) * rows * 32);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint8_t* g = src[s] + (size_t)(2 * kp + u) * rows_of[s] * 1024;
-      __builtin_amdgcn_global_load_lds(g, LDS_PTR(st + (c * 2 + u) * 1024), 16, 0, 0);
-    }
-    if (lane < 32) {   // blocks 4 kp .. 4 kp + 3 of the chunk's 32 rows
-      const uint8_t* g = ssrc[s] + (size_t)(4 * kp) * rows_of[s] * 32;
-      __builtin_amdgcn_global_load_lds(g, LDS_PTR(st + C::kCodeBytes + c * 128), 4, 0, 0);
+      for (int u = 0; u < 2; ++u)
+        buf_to_lds16(rc, st + (c * 2 + u) * 1024, lane * 16, ((2 * kp + u) * rows + pan[s]) * 1024);
+      if (lane < 32)   // blocks 4 kp .. 4 kp + 3 of the chunk's 32 rows
+        buf_to_lds4(rsc, st + C::kCodeBytes + c * 128, ((lane >> 3) & 3) * rows * 32 + 4 * (lane & 7),
+                    4 * kp * rows * 32 + pan[s] * 32);
+    } else {
+      // residual panel q: R steps 2q and 2q + 1 of 32 lora_act (A) or proj_up (B) rows,
+      // lane (h, l32) holding 8 values of row l32 as the bf16 instruction's operand
+      const int q = kp - KP;
+      const int g = is_a ? c : c - C::kChunksA;
+      const int row = is_a ? min(mp0 * 32 + 32 * g + l32, M - 1) : min(np0 * 32 + 32 * g + l32, N - 1);
+      const auto rr = make_rsrc(is_a ? a.lora_act : a.proj_up, (uint32_t)(is_a ? M : N) * (uint32_t)R * 2);
+      const int vo = row * R * 2 + 16 * h;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)   // an odd last step is copied twice; the second copy is not multiplied
+        buf_to_lds16(rr, st + (c * 2 + u) * 1024, vo, 32 * min(2 * q + u, r_steps - 1));
+      if (lane < 32)   // keeps the per-panel copy count; these bytes are not read
+        buf_to_lds4(rr, st + C::kCodeBytes + c * 128, vo, 64 * q);
     }
   };
   auto load_panel = [&](int kp) {
@@ -237,14 +280,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxGemmArgs a) {
     for (int s = 0; s < C::kFull; ++s) copy_chunk(s, kp);
     if (extra) copy_chunk(C::kFull, kp);
   };
+  // panel kp landed: copies of panels issued after it may stay in flight
   auto wait_panel = [&](int kp) {
-    const int later = min(kp + S - 2, KP - 1) - kp;
-    if (S == 2 || later <= 0) {
-      wait_vm<0>();
-    } else if (S == 3 || later == 1) {
+    const int later = min(kp + S - 2, TP - 1) - kp;
+    if (later >= 2) {
+      if (extra) wait_vm<(S >= 4 ? 2 : 0) * C::kPerWave * 3>(); else wait_vm<(S >= 4 ? 2 : 0) * C::kFull * 3>();
+    } else if (later == 1) {
       if (extra) wait_vm<C::kPerWave * 3>(); else wait_vm<C::kFull * 3>();
     } else {
-      if (extra) wait_vm<(S >= 4 ? 2 : 0) * C::kPerWave * 3>(); else wait_vm<(S >= 4 ? 2 : 0) * C::kFull * 3>();
+      wait_vm<0>();
     }
   };
 
@@ -258,12 +302,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxGemmArgs a) {
 
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
-    if (p < KP) load_panel(p);
+    if (p < TP) load_panel(p);
+  if (tid < C::BN) {
+    lds_alpha[tid] = bf16lo_to_f32(a.wtscale[0]) * bf16lo_to_f32(wc_raw);
+    lds_bias[tid] = bf16lo_to_f32(b_raw);
+  }
 
   for (int kp = 0; kp < KP; ++kp) {
     wait_panel(kp);
     barrier_no_fence();
-    if (kp + S - 1 < KP) load_panel(kp + S - 1);
+    if (kp + S - 1 < TP) load_panel(kp + S - 1);
     const uint8_t* cur = stage_at(kp);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -294,69 +342,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxGemmArgs a) {
   }
 
   // ---- epilogue: * wtscale * wcscales[n], + lora_act @ proj_up^T, + bias, bf16 ----
-  const int m_w = (mp0 + wave_m * TM) * 32;
-  const int n_w = (np0 + wave_n * TN) * 32;
-  float alpha[TN], bias_v[TN];
   {
-    const float wt = bf16lo_to_f32(a.wtscale[0]);
+    float al[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n_w + 32 * j + l32;
-      const bool in = col < N;
-      alpha[j] = in ? wt * bf16lo_to_f32(a.wcscales[col]) : 0.0f;
-      bias_v[j] = (in && a.bias != nullptr) ? bf16lo_to_f32(a.bias[col]) : 0.0f;
-    }
+    for (int j = 0; j < TN; ++j) al[j] = lds_alpha[(wave_n * TN + j) * 32 + l32];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] *= al[j];
   }
+  for (int q = 0; q < RP; ++q) {
+    const int kp = KP + q;
+    wait_panel(kp);
+    barrier_no_fence();
+    if (kp + S - 1 < TP) load_panel(kp + S - 1);
+    const uint8_t* cur = stage_at(kp);
+    const int nu = 2 * q + 1 < r_steps ? 2 : 1;
+    for (int u = 0; u < nu; ++u) {
+      bf16x8 la[TM], pu[TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
+        la[i] = *reinterpret_cast<const bf16x8*>(cur + ((wave_m * TM + i) * 2 + u) * 1024 + lane * 16);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
+        pu[j] = *reinterpret_cast<const bf16x8*>(cur + ((C::kChunksA + wave_n * TN + j) * 2 + u) * 1024 + lane * 16);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] *= alpha[j];
-
-  const int R = (int)a.R;
-  const int r_steps = R / 16;
-  {
-    const int m_wg = mp0 * 32;
-    for (int r0 = 0; r0 < r_steps; r0 += C::kResSteps) {
-      const int SR = min(C::kResSteps, r_steps - r0);
-      const int blocks = C::kChunks * SR;
-      __syncthreads();   // LDS free (main loop or the previous pass is done)
-      for (int b = wave; b < blocks; b += C::kWaves) {
-        const bool is_a = b < C::kChunksA * SR;
-        const int bb = is_a ? b : b - C::kChunksA * SR;
-        const int g = bb / SR, rs = bb % SR;
-        const int col = 16 * (r0 + rs) + 8 * h;
-        const uint16_t* srcp;
-        if (is_a) {
-          const int m = min(m_wg + 32 * g + l32, M - 1);
-          srcp = a.lora_act + (size_t)m * R + col;
-        } else {
-          const int n = min((np0 + g) * 32 + l32, N - 1);
-          srcp = a.proj_up + (size_t)n * R + col;
-        }
-        __builtin_amdgcn_global_load_lds(srcp, LDS_PTR(smem + b * 1024), 16, 0, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-      __syncthreads();
-      for (int rs = 0; rs < SR; ++rs) {
-        bf16x8 la[TM], pu[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          la[i] = *reinterpret_cast<const bf16x8*>(smem + ((wave_m * TM + i) * SR + rs) * 1024 + lane * 16);
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          pu[j] = *reinterpret_cast<const bf16x8*>(smem + (C::kChunksA * SR + (wave_n * TN + j) * SR + rs) * 1024 + lane * 16);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], pu[j], acc[i][j], 0, 0, 0);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], pu[j], acc[i][j], 0, 0, 0);
     }
   }
 
-  __syncthreads();
+  const int m_w = (mp0 + wave_m * TM) * 32;
+  const int n_w = (np0 + wave_n * TN) * 32;
+  float bias_v[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bias_v[j] = lds_bias[(wave_n * TN + j) * 32 + l32];
+  __syncthreads();   // every wave is done with the stages
   constexpr int kCols = 32 * TN;
   constexpr int kPieces = kCols / 8;
   uint16_t* stage_out = reinterpret_cast<uint16_t*>(smem + wave * (32 * kCols * 2));

@@ -95,6 +95,9 @@ def check_layer(gpu_lib, cfg, rows=None, with_bias=True):
     (dict(M=300, K=384, N=200, R=32, kind="dit", seed=2), True),     # ragged M and N
     (dict(M=77, K=128, N=72, R=0, kind="dit", seed=3), False),       # one panel, no residual, no bias
     (dict(M=513, K=1024, N=640, R=128, kind="swiglu", seed=4), True),
+    (dict(M=96, K=128, N=330, R=48, kind="dit", seed=5), True),      # odd R steps; residual panels in the prologue
+    (dict(M=200, K=512, N=256, R=80, kind="dit", seed=6), True),     # odd R steps over three residual panels
+    (dict(M=64, K=128, N=320, R=128, kind="dit", seed=7), False),    # one matrix panel, four residual panels
 ])
 def test_variant_layer_matches_oracle(gpu_lib, cfg, bias):
     dist = check_layer(gpu_lib, cfg, with_bias=bias)
