@@ -96,6 +96,7 @@ WEIGHT_CANONICAL = 0
 WEIGHT_PACKED = 1
 ACT_CANONICAL = 0
 ACT_PACKED = 1
+ACT_MXFP4 = 2
 
 _lib = None
 

@@ -262,9 +262,13 @@ static int quantize_act_impl(const void* x, const void* smooth, const void* gsca
   int st = check_mk(M, K, R);
   if (st) return st;
   if ((st = check_rsrc_sizes(M, K, R))) return st;
-  if (act_layout != SVDQ_ACT_CANONICAL && act_layout != SVDQ_ACT_PACKED)
+  if (act_layout != SVDQ_ACT_CANONICAL && act_layout != SVDQ_ACT_PACKED && act_layout != SVDQ_ACT_MXFP4)
     return fail(SVDQ_ERR_INVALID, "act_layout %d is not a known layout", act_layout);
   const bool packed = act_layout == SVDQ_ACT_PACKED;
+  const bool mx = act_layout == SVDQ_ACT_MXFP4;
+  if (mx && K % 128 != 0)
+    return fail(SVDQ_ERR_UNSUPPORTED, "K = %lld: the MXFP4 layout needs K a multiple of 128", (long long)K);
+  if (mx && gscale != nullptr) return fail(SVDQ_ERR_UNSUPPORTED, "the MXFP4 layout has no static-scale form");
   if (packed && ascales != nullptr)
     return fail(SVDQ_ERR_INVALID, "ascales must be NULL with the packed layout (the buffer holds them)");
   if (M == 0) return ok();
@@ -292,15 +296,25 @@ static int quantize_act_impl(const void* x, const void* smooth, const void* gsca
     if ((st = check_ptrs(names, ptrs, 1))) return st;
   }
   if (gscale != nullptr && !aligned16(gscale)) return fail(SVDQ_ERR_ALIGN, "act_gscale is not 16-byte aligned");
-  const size_t qbytes = packed ? svdq::packed_weight_bytes(M, K) : (size_t)M * (K / 2);
+  const size_t qbytes = mx ? svdq::mx_codes_bytes(M, K) : packed ? svdq::packed_weight_bytes(M, K) : (size_t)M * (K / 2);
+  const size_t sbytes = mx ? (size_t)((M + 31) / 32) * 32 * (size_t)(K / 32) : (size_t)(K / 16) * M;
   const Range in[] = {range("x", x, (size_t)M * K * 2), range("smooth", smooth, (size_t)K * 2),
                       range("proj_down", R > 0 ? proj_down : nullptr, (size_t)K * R * 2),
                       range("act_gscale", gscale, 2)};
   const Range out[] = {range("qact", qact, qbytes),
-                       range("ascales", packed ? nullptr : ascales, (size_t)(K / 16) * M),
+                       range("ascales", packed ? nullptr : ascales, sbytes),
                        range("lora_act", R > 0 ? lora_act : nullptr, (size_t)M * R * 2),
                        range("workspace", ws_need > 0 ? workspace : nullptr, ws_need)};
   if ((st = check_alias(in, 4, out, 4))) return st;
+  if (mx) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = svdq::launch_quant_lora_mx(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth), static_cast<const uint16_t*>(proj_down),
+        static_cast<uint8_t*>(qact), static_cast<uint8_t*>(ascales), static_cast<uint16_t*>(lora_act),
+        static_cast<float*>(ws_need > 0 ? workspace : nullptr), M, K, R, s);
+    if (int st_ = launched(e, "MX quantisation", s)) return st_;
+    return ok();
+  }
   return run_quantize(x, smooth, M, K, proj_down, R, qact, ascales, lora_act,
                       ws_need > 0 ? workspace : nullptr, packed, static_cast<hipStream_t>(stream), gscale);
 }
@@ -1058,15 +1072,12 @@ int svdq_linear_mxfp4(const void* x, const void* smooth, const void* w_codes, co
   if ((st = check_alias(in, 9, out, 2))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  hipError_t e = svdq::launch_quant_act_mx(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
-                                           ws + w.codes, ws + w.scales, M, K, s);
-  if (int st_ = launched(e, "MX quantisation", s)) return st_;
   uint16_t* lora = reinterpret_cast<uint16_t*>(ws + w.lora);
-  if (R > 0) {
-    e = svdq::launch_lowrank_down(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(proj_down), lora,
-                                  reinterpret_cast<float*>(ws + w.partial), M, K, R, s);
-    if (int st_ = launched(e, "down-projection", s)) return st_;
-  }
+  // one pass over x: MX codes and scales, and lora_act when R > 0
+  hipError_t e = svdq::launch_quant_lora_mx(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(smooth),
+                                            static_cast<const uint16_t*>(proj_down), ws + w.codes, ws + w.scales,
+                                            lora, reinterpret_cast<float*>(ws + w.partial), M, K, R, s);
+  if (int st_ = launched(e, "MX quantisation and down-projection", s)) return st_;
   const svdq::MxGemmArgs a = mx_args(ws + w.codes, ws + w.scales, lora, w_codes, w_scales, wcscales, wtscale,
                                      proj_up, bias, M, N, K, R, y);
   e = svdq::launch_gemm_mx(a, s);

@@ -7,9 +7,10 @@
 // with FP4 operands (on random data it sustains ~3.9x the f16 instruction's
 // rate). The epilogue, low-rank branch and bias are the NVFP4 layer's.
 //
-// MX quantisation of a 32-block (OCP MX rule for E2M1): X = floor(log2 amax) - 2
-// clamped to [-127, 127], byte X + 127; codes = E2M1 nearest-even of v * 2^-X
-// (exact scaling), saturating at 6, sign of v kept; all-zero block: X = -127.
+// MX quantisation of a 32-block (OCP MX rule for E2M1, mx_format.h): X =
+// floor(log2 amax) - 2 clamped to [-127, 127], byte X + 127; codes = E2M1
+// nearest-even of v * 2^-X (exact scaling), saturating at 6, sign of v kept;
+// all-zero block: X = -127.
 //
 // MX operand layout (rows = tokens or output channels, padded to 32-row panels):
 //   codes: per 64-K step s and row panel p a 1 KB chunk at 1024 * (s * P + p);
@@ -20,6 +21,7 @@
 //          32 scales of a block are 4-byte aligned; padding rows hold 0).
 #include "common.h"
 #include "kernels.h"
+#include "mx_format.h"
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -29,31 +31,11 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int mx_exponent(float amax) {
-  if (!(amax > 0.0f)) return -127;
-  int e;
-  frexpf(amax, &e);   // amax = m 2^e, m in [0.5, 1): floor(log2 amax) = e - 1
-  return min(127, max(-127, e - 1 - 2));
-}
-
 // 32 values -> 16 bytes of E2M1 codes (value 2i in the low nibble of byte i)
 __device__ __forceinline__ u32x4 mx_codes(const float (&v)[32], int X) {
   u32x4 out;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t p = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float t0 = ldexpf(v[8 * w + 2 * b], -X), t1 = ldexpf(v[8 * w + 2 * b + 1], -X);
-      switch (b) {
-        case 0: p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, t0, t1, 1.0f, 0); break;
-        case 1: p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, t0, t1, 1.0f, 1); break;
-        case 2: p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, t0, t1, 1.0f, 2); break;
-        default: p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, t0, t1, 1.0f, 3); break;
-      }
-    }
-    out[w] = p;
-  }
+  for (int w = 0; w < 4; ++w) out[w] = mx_codes8(v + 8 * w, X);
   return out;
 }
 

@@ -132,6 +132,12 @@ struct MxGemmArgs {
   int64_t M, N, K, R;
 };
 hipError_t launch_gemm_mx(const MxGemmArgs& a, hipStream_t stream);
+// The variant's fused step: MX codes and scales of x * smooth (the layout above)
+// and lora_act = bf16(x @ proj_down) in one pass over x (R = 0: the quantisation
+// alone); partial as for launch_quant_lora. K % 128 == 0.
+hipError_t launch_quant_lora_mx(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down, uint8_t* codes,
+                                uint8_t* scales, uint16_t* lora_act, float* partial, int64_t M, int64_t K, int64_t R,
+                                hipStream_t stream);
 // lora_act = bf16(x @ proj_down) alone (the quantiser's down-projection without
 // the quantisation); partial as for launch_quant_lora
 hipError_t launch_lowrank_down(const uint16_t* x, const uint16_t* proj_down, uint16_t* lora_act, float* partial,

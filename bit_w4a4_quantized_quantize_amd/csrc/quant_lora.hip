@@ -46,6 +46,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "mx_format.h"
 
 namespace svdq {
 
@@ -293,8 +294,13 @@ constexpr int kWsStage = kWsX + 64 * 256;    // + proj_down of one panel (64 k x
 typedef short v4s __attribute__((ext_vector_type(4)));
 #define WS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-template <bool PACKED, bool STATIC = false>
+// MXO: the quantisers write the MXFP4 variant's operand instead (gemm_mx.hip's
+// layout and the rule of mx_format.h: a 32-block is the four lanes of a DPP quad,
+// whose maximum two quad swaps gather); qact and ascales are then the MX code and
+// scale buffers, K % 128 == 0, and PACKED and STATIC are false.
+template <bool PACKED, bool STATIC = false, bool MXO = false>
 __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
+  static_assert(!MXO || (!PACKED && !STATIC), "the MX output has its own layout and dynamic scales");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kWsStage];
 
   const int tid = threadIdx.x;
@@ -313,8 +319,9 @@ __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
   const uint32_t code_bytes = (uint32_t)MP * KP * 1024;
   const uint32_t x_bytes = (uint32_t)M * K * 2;
   const uint32_t pd_bytes = (uint32_t)K * R * 2;
-  const uint32_t q_bytes = PACKED ? code_bytes + (uint32_t)MP * KP * 128 : (uint32_t)M * (K / 2);
-  const uint32_t s_bytes = PACKED ? 0u : (uint32_t)(K / 16) * M;
+  const uint32_t q_bytes = MXO ? (uint32_t)MP * 32 * (uint32_t)(K / 2)
+                               : PACKED ? code_bytes + (uint32_t)MP * KP * 128 : (uint32_t)M * (K / 2);
+  const uint32_t s_bytes = MXO ? (uint32_t)(K / 32) * MP * 32 : PACKED ? 0u : (uint32_t)(K / 16) * M;
   const auto rx = make_rsrc(a.x, x_bytes);
   const auto rsm = make_rsrc(a.smooth, (uint32_t)K * 2);
   const auto rpd = make_rsrc(a.proj_down, pd_bytes);
@@ -403,6 +410,24 @@ __global__ __launch_bounds__(512) void quant_lora_ws_kernel(QLArgs a) {
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
       // the other half of the block sits in lane ^ 1 (a DPP lane swap, no LDS round trip)
       amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, false)));
+      if constexpr (MXO) {
+        // the rest of the 32-block sits in lane ^ 2 and lane ^ 3
+        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0x4E, 0xF, 0xF, false)));
+        const int X = mx_exponent(amax);
+        const uint32_t pk = mx_codes8(v, X);
+        // chunk (panel p, row panel q): lane 32 hb + r of the matrix instruction holds
+        // 32-block hb of the panel, 4 bytes per pc % 4; rows of the last 32-row panel
+        // beyond M are written (zero codes, scale byte 0)
+        const int q = m0 >> 5, hb = pc >> 2, jq = pc & 3;
+        const bool ok = j < n && q < MP;
+        const uint32_t chunk = (uint32_t)p * MP + q;
+        __builtin_amdgcn_raw_buffer_store_b32(pk, rq, ok ? chunk * 1024 + (32 * hb + r) * 16 + 4 * jq : q_bytes, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(X + 127), rsc,
+                                             ok && jq == 0 ? (uint32_t)(2 * p + hb) * (MP * 32) + (uint32_t)(m0 + r)
+                                                           : s_bytes,
+                                             0, 0);
+        continue;
+      }
       const uint32_t sc = bs.code(amax);
       const float sd = bs.divisor(sc);
       const float inv = sd > 0.0f ? scale_reciprocal(sd) : 0.0f;
@@ -996,6 +1021,33 @@ hipError_t launch_quant_lora(const uint16_t* x, const uint16_t* smooth, const ui
     launch(false, true);
   }
   if (R > 0 && ks > 1) {
+    const int64_t groups = M * (R / 8);
+    hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const float*>(partial), lora_act, (int)M, (int)R, ks);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_lora_mx(const uint16_t* x, const uint16_t* smooth, const uint16_t* proj_down, uint8_t* codes,
+                                uint8_t* scales, uint16_t* lora_act, float* partial, int64_t M, int64_t K, int64_t R,
+                                hipStream_t stream) {
+  if (R <= 0) return launch_quant_act_mx(x, smooth, codes, scales, M, K, stream);
+  QLArgs a{x, smooth, proj_down, codes, scales, lora_act, nullptr, (int)M, (int)K, (int)R, 0, 0, nullptr};
+  // the canonical layout's split count, so that lora_act has the bits of the
+  // canonical quantisation's down-projection by the same kernel
+  const int ks = k_splits(M, K, R, false);
+  a.partial = ks > 1 ? partial : nullptr;
+  QLArgs w = a;
+  w.split_steps = (int)((K / 64 + ks - 1) / ks);
+  hipLaunchKernelGGL((quant_lora_ws_kernel<false, false, true>),
+                     dim3((unsigned)((M + kWsRows - 1) / kWsRows), (unsigned)ks), dim3(512), 0, stream, w);
+  a.split_steps = (int)((K / 32 + ks - 1) / ks);
+  const dim3 grid((unsigned)((M + kRows - 1) / kRows), (unsigned)ks);
+  for (int64_t r0 = kRChunk; r0 < R; r0 += kRChunk) {   // lora_act columns past the first 128
+    a.r_base = (int)r0;
+    hipLaunchKernelGGL((quant_lora_kernel<kRowTiles, false, false, true>), grid, dim3(64 * kWaves), 0, stream, a);
+  }
+  if (ks > 1) {
     const int64_t groups = M * (R / 8);
     hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float*>(partial), lora_act, (int)M, (int)R, ks);

@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import ACT_CANONICAL, ACT_PACKED, WEIGHT_CANONICAL, WEIGHT_PACKED, SvdqError  # noqa: F401
+from ._lib import ACT_CANONICAL, ACT_MXFP4, ACT_PACKED, WEIGHT_CANONICAL, WEIGHT_PACKED, SvdqError  # noqa: F401
 
 
 def _bytes(t):
@@ -87,16 +87,19 @@ def set_gemm_tile(tile):
 
 
 def quantize_act(x, smooth, proj_down=None, qact=None, ascales=None, lora_act=None, packed=False,
-                 workspace=None):
+                 workspace=None, mx=False):
     """quant(x * smooth) and, with proj_down, lora_act = x @ proj_down.
 
     Returns (qact, ascales, lora_act): canonical qact uint8 [M, K/2] and ascales
     uint8 [K/16, M]; or, with packed=True, one packed uint8 buffer (the packed
-    weight layout with rows = tokens) and ascales None. lora_act bf16 [M, R] or None.
-    workspace: optional uint8 device tensor of at least
-    quantize_act_workspace_bytes(M, K, R) bytes (allocated here when None).
+    weight layout with rows = tokens) and ascales None; or, with mx=True, the
+    MXFP4 variant's code and scale buffers (as quantize_act_mxfp4 gives them).
+    lora_act bf16 [M, R] or None. workspace: optional uint8 device tensor of at
+    least quantize_act_workspace_bytes(M, K, R) bytes (allocated here when None).
     """
-    return _quantize_act(x, smooth, None, proj_down, qact, ascales, lora_act, packed, workspace)
+    if mx and packed:
+        raise ValueError("packed and mx are two different layouts")
+    return _quantize_act(x, smooth, None, proj_down, qact, ascales, lora_act, packed, workspace, mx)
 
 
 def quantize_act_static(x, smooth, act_gscale, proj_down=None, qact=None, ascales=None, lora_act=None,
@@ -129,7 +132,7 @@ def calibrate_act_gscale(x, smooth, act_gscale=None, workspace=None):
     return act_gscale
 
 
-def _quantize_act(x, smooth, act_gscale, proj_down, qact, ascales, lora_act, packed, workspace):
+def _quantize_act(x, smooth, act_gscale, proj_down, qact, ascales, lora_act, packed, workspace, mx=False):
     _need(x, "x", torch.bfloat16, 2)
     M, K = x.shape
     _k_ok(K)
@@ -141,7 +144,15 @@ def _quantize_act(x, smooth, act_gscale, proj_down, qact, ascales, lora_act, pac
         R = proj_down.shape[1]
         _need(proj_down, "proj_down", torch.bfloat16, shape=(K, R))
     L = _lib.lib()
-    if packed:
+    if mx:
+        if K % 128 != 0:
+            raise ValueError(f"K={K}: the MXFP4 layout needs K a multiple of 128")
+        if qact is None or ascales is None:
+            c, sc = mx_buffers(M, K, dev)
+            qact = c if qact is None else qact
+            ascales = sc if ascales is None else ascales
+        _check_mx_operands(qact, ascales, M, K, "act")
+    elif packed:
         nbytes = L.svdq_packed_act_bytes(M, K)
         if qact is None:
             qact = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -167,7 +178,7 @@ def _quantize_act(x, smooth, act_gscale, proj_down, qact, ascales, lora_act, pac
         ws_bytes = _need(workspace, "workspace", torch.uint8, 1, min_numel=ws_need).numel()
     _devices(x=x, smooth=smooth, act_gscale=act_gscale, proj_down=proj_down, qact=qact, ascales=ascales,
              lora_act=lora_act, workspace=workspace)
-    layout = ACT_PACKED if packed else ACT_CANONICAL
+    layout = ACT_MXFP4 if mx else ACT_PACKED if packed else ACT_CANONICAL
     rest = (_p(proj_down), R, layout, _p(qact), _p(_bytes(ascales)) if ascales is not None else None,
             _p(lora_act) if R > 0 else None, _p(workspace), ws_bytes, _stream(dev))
     if act_gscale is None:

@@ -82,10 +82,15 @@ enum {
 /* Layouts of quantised activations (codes + scales).                                     */
 enum {
   SVDQ_ACT_CANONICAL = 0,    /* qact [M, K/2] + ascales [K/16, M]                            */
-  SVDQ_ACT_PACKED = 1        /* one buffer of svdq_packed_act_bytes(M, K) in the packed
+  SVDQ_ACT_PACKED = 1,       /* one buffer of svdq_packed_act_bytes(M, K) in the packed
                                 weight layout with rows = tokens; ascales must be NULL.
                                 Rows beyond M in the last 32-row panel are unspecified;
                                 positions beyond K are zero.                               */
+  SVDQ_ACT_MXFP4 = 2         /* the MXFP4 variant's operand instead of NVFP4 (see the
+                                MXFP4 section below): qact = MX codes
+                                (svdq_mx_codes_bytes(M, K)), ascales = MX scales
+                                (svdq_mx_scales_bytes(M, K)); K % 128 == 0, dynamic
+                                scales only (svdq_quantize_act).                          */
 };
 
 #define SVDQ_ABI_VERSION 1
@@ -123,6 +128,10 @@ int svdq_set_gemm_tile(int tile, int* previous);
  *   act_layout SVDQ_ACT_CANONICAL: qact [M, K/2] u8, ascales [K/16, M] u8;
  *              SVDQ_ACT_PACKED: qact = packed buffer (svdq_packed_act_bytes(M, K)
  *              bytes), ascales NULL. Outputs follow the rule in the file header.
+ *              SVDQ_ACT_MXFP4: qact, ascales = the MXFP4 variant's code and scale
+ *              buffers, as svdq_quantize_act_mxfp4 writes them (bit for bit), with
+ *              the down-projection in the same pass; K % 128 == 0 and
+ *              svdq_quantize_act_static rejects it (SVDQ_ERR_UNSUPPORTED).
  *   proj_down [K, R] bf16, lora_act [M, R] bf16: used when R > 0 (both
  *     required then); lora_act = bf16(x @ proj_down) with fp32 accumulation.
  *   workspace: device scratch of at least svdq_quantize_act_workspace_bytes(M, K, R)
@@ -383,10 +392,13 @@ int svdq_prepare_residual(const void* weight, const void* smooth, const void* pr
  *   Padding rows hold zero codes and scale byte 0.
  * K must be a multiple of 128 (SVDQ_ERR_UNSUPPORTED otherwise).
  * svdq_reround_weight_mxfp4: canonical qweight/wscales -> MX codes/scales (load time).
- * svdq_quantize_act_mxfp4: x [M, K], smooth [K] -> MX codes/scales.
+ * svdq_quantize_act_mxfp4: x [M, K], smooth [K] -> MX codes/scales. The same
+ *   codes and scales with lora_act in one pass: svdq_quantize_act with
+ *   act_layout SVDQ_ACT_MXFP4.
  * svdq_gemm_mxfp4: MX operands + lora_act [M, R] -> y [M, N] bf16.
- * svdq_linear_mxfp4: the whole variant layer from x, with a workspace of
- *   svdq_linear_mxfp4_workspace_bytes(M, K, R) bytes.
+ * svdq_linear_mxfp4: the whole variant layer from x (that one-pass quantisation,
+ *   then the GEMM), with a workspace of svdq_linear_mxfp4_workspace_bytes(M, K, R)
+ *   bytes.
  */
 size_t svdq_mx_codes_bytes(int64_t rows, int64_t K);
 size_t svdq_mx_scales_bytes(int64_t rows, int64_t K);

@@ -84,7 +84,9 @@ def q(**kw):
     (dict(proj_down=None), 1), (dict(lora_act=None), 1),
     (dict(x=fake(1) + 8), 4), (dict(ascales=fake(5) + 4), 4),
     (dict(qact=fake(1) + 64), 6), (dict(lora_act=fake(3)), 6), (dict(ascales=fake(4)), 6),
-    (dict(layout=2), 8), (dict(layout=1), 8),           # packed needs ascales NULL
+    (dict(layout=3), 8), (dict(layout=1), 8),           # packed needs ascales NULL
+    (dict(layout=2, K=192), 3),                         # the MXFP4 layout needs K % 128 == 0
+    (dict(layout=2, ascales=None), 1), (dict(layout=2, ascales=fake(4) + 32 * 64), 6),
     (dict(layout=1, ascales=None, qact=fake(2) - 1024 * 4), 6),
 ])
 def test_quantize_act_rejections(kw, code):
@@ -289,6 +291,14 @@ def test_prepare_empty_and_rank_zero_pointers():
     assert prep(R=0, omega=None, pd=None, pu=None, ws_bytes=0) == 5
     assert L.svdq_prepare_workspace_bytes(10240, 3840, 128) >= 10240 * 3840 * 2
     assert L.svdq_prepare_workspace_bytes(0, 3840, 128) == 0
+
+
+@no_gpu_only
+def test_quantize_act_static_rejects_mx_layout():
+    L = _lib.lib()
+    assert L.svdq_quantize_act_static(fake(1), fake(2), fake(8), 64, 256, fake(3), 16, 2, fake(4), fake(5),
+                                      fake(6), fake(7), 1 << 30, None) == 3
+    assert "static" in L.svdq_last_error().decode()
 
 
 @no_gpu_only

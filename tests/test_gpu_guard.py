@@ -153,6 +153,29 @@ def test_quantize_writes_exactly_outputs(gpu_lib, M, K, R, packed):
     _run_guarded(f"quantize_act[packed={packed}]", specs, call, ref)
 
 
+@pytest.mark.parametrize("M,K,R", [(130, 384, 32), (64, 3840, 128)])
+def test_quantize_mx_writes_exactly_outputs(gpu_lib, M, K, R):
+    """The MXFP4 layout of svdq_quantize_act: codes and scales of the padded rows, lora_act."""
+    ops = gpu_lib
+    x, sm = workloads.make_activation(M, K, kind="dit", seed=M + K)
+    pd = dev_bf16(F.f64_to_bf16(np.random.default_rng(K).standard_normal((K, R)) * 0.05))
+    xd, smd = dev_bf16(x), dev_bf16(sm)
+    c_ref, s_ref, l_ref = ops.quantize_act(xd, smd, pd, mx=True)
+    torch.cuda.synchronize()
+    L = ops._lib.lib()
+    specs = {"qact": ((L.svdq_mx_codes_bytes(M, K),), torch.uint8, True),
+             "ascales": ((L.svdq_mx_scales_bytes(M, K),), torch.uint8, True),
+             "lora_act": ((M, R), torch.bfloat16, True)}
+    ws_bytes = ops.quantize_act_workspace_bytes(M, K, R)
+    if ws_bytes > 0:
+        specs["workspace"] = ((ws_bytes,), torch.uint8, False)
+
+    def call(qact, ascales, lora_act, workspace=None):
+        ops.quantize_act(xd, smd, pd, qact=qact, ascales=ascales, lora_act=lora_act, workspace=workspace, mx=True)
+
+    _run_guarded("quantize_act[mx]", specs, call, {"qact": c_ref, "ascales": s_ref, "lora_act": l_ref})
+
+
 def test_lowrank_down_writes_exactly_lora(gpu_lib):
     ops = gpu_lib
     M, K, R = 77, 3840, 128

@@ -110,6 +110,35 @@ def test_variant_layer_full_size_sampled(gpu_lib):
     assert dist < 0.2
 
 
+def _lora_within_bound(got_bits, x_bits, pd_bits, K):
+    got = F.bf16_to_f64(got_bits)
+    ref = S.lowrank_down(x_bits, pd_bits)
+    scale = np.abs(F.bf16_to_f64(x_bits)) @ np.abs(F.bf16_to_f64(pd_bits))
+    tol = np.abs(ref) * 2.0 ** -8 + scale * K * 2.0 ** -23 + 1e-30
+    assert not np.any(np.abs(got - ref) > tol)
+
+
+@pytest.mark.parametrize("M,K,R", [
+    (64, 128, 16), (300, 256, 32), (1, 384, 128), (130, 1024, 256),   # R above one 128-wide chunk
+    (2049, 1280, 128), (4096, 3840, 128),
+])
+def test_fused_quant_down_mx(gpu_lib, M, K, R):
+    """svdq_quantize_act with the MXFP4 layout: codes and scales bit for bit those of the
+    standalone MX quantiser (padding rows included) and of the oracle, and lora_act within
+    the down-projection's bound, from one pass over x."""
+    d = workloads.make_linear(M, K, 16, R, kind="dit", seed=M + K + R, with_bias=False)
+    x, sm, pd = dev_bf16(d["x"]), dev_bf16(d["smooth"]), dev_bf16(d["proj_down"])
+    codes, scales, lora = gpu_lib.quantize_act(x, sm, pd, mx=True)
+    c1, s1 = gpu_lib.quantize_act_mxfp4(x, sm)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(codes), host_u8(c1))
+    assert np.array_equal(host_u8(scales), host_u8(s1))
+    ca, sa = X.quantize_act_mx(d["x"], d["smooth"])
+    assert np.array_equal(unpack_mx_scales(host_u8(scales), M, K), sa)
+    assert np.array_equal(unpack_mx_codes(host_u8(codes), M, K), ca)
+    _lora_within_bound(host_bits(lora), d["x"], d["proj_down"], K)
+
+
 def test_gemm_entry_matches_linear(gpu_lib):
     d, layer = make_layer(dict(M=128, K=256, N=96, R=16, kind="dit", seed=9))
     wc, ws = gpu_lib.reround_weight_mxfp4(layer)
@@ -117,6 +146,18 @@ def test_gemm_entry_matches_linear(gpu_lib):
     ac, asc = gpu_lib.quantize_act_mxfp4(x, layer.smooth)
     _, _, lora = gpu_lib.quantize_act(x, layer.smooth, layer.proj_down)
     y1 = gpu_lib.gemm_mxfp4(ac, asc, lora, wc, ws, layer, 128)
+    y2 = gpu_lib.linear_mxfp4(x, layer, wc, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_gemm_entry_on_fused_operands_matches_linear(gpu_lib):
+    """The layer equals the GEMM entry point on the one-pass quantiser's operands, bit for bit."""
+    d, layer = make_layer(dict(M=300, K=1024, N=200, R=128, kind="dit", seed=10))
+    wc, ws = gpu_lib.reround_weight_mxfp4(layer)
+    x = dev_bf16(d["x"])
+    ac, asc, lora = gpu_lib.quantize_act(x, layer.smooth, layer.proj_down, mx=True)
+    y1 = gpu_lib.gemm_mxfp4(ac, asc, lora, wc, ws, layer, 300)
     y2 = gpu_lib.linear_mxfp4(x, layer, wc, ws)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
