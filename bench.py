@@ -1216,8 +1216,8 @@ def run_prep(args):
         "config": {"workload": cfg["desc"], "cache": "warm" if args.warm else f"rotating {n_sets} weights"},
         "roofline": {
             "kernel": "residual stage (svdq_prepare_residual: residual_kernel, fp64, then the quantiser); "
-                      "the preparation's time splits about evenly between it, the fp32 products and the "
-                      "Cholesky QR (profiles/prep_ffn_w1_1024_kernel_stats.txt)",
+                      "most of the preparation's time is the Cholesky QR, then this stage and the fp32 "
+                      "matrix-instruction products (profiles/prep_ffn_w1_1024_kernel_stats.txt)",
             "bound": "alu",
             "achieved": round(res_tflops, 2),
             "peak": PEAK_FP64_TFLOPS,

@@ -32,75 +32,109 @@ namespace {
 constexpr int kRMax = 128;   // fp64 Gram / Cholesky of R x R sit in LDS
 
 // ---------------------------------------------------------------------------
-// Tall-skinny products with Ws = W / smooth (fp32), 64 x R per workgroup
+// Tall-skinny products with Ws = W / smooth (fp32) on the fp32 matrix instruction
+// v_mfma_f32_32x32x2_f32: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32] of
+// a 32 x 2 by 2 x 32 product; accumulator element i of lane l is row
+// 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32. A workgroup of 4 waves owns a
+// 64 x 128 output tile: wave (wm, wn) rows 32 wm .. + 31 and columns 64 wn .. + 63
+// (two 32 x 32 blocks; columns past R multiply zeros and are not stored, which keeps
+// the loop free of branches so the accumulators stay in place). The reduction walks 32-wide
+// chunks through two LDS stages, the next chunk's global loads in registers while
+// the current one multiplies.
 // ---------------------------------------------------------------------------
 
-// Y[n, r] = sum_k Ws[n, k] B[k, r]; 256 threads, 32 rows per workgroup (enough
-// workgroups to fill the chip at N = 10240), thread (rg, cg) owns rows
-// 2rg, 2rg+1 and columns 8cg..8cg+7.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 8 consecutive bf16 of W and the matching 8 of smooth (past the bounds W = 0 and
+// smooth = 1; the division waits until the chunk's matrix instructions are issued)
+struct Ws8 {
+  u32x4 w, s;
+};
+__device__ __forceinline__ Ws8 ws8_load(const uint16_t* __restrict__ W, const uint16_t* __restrict__ smooth,
+                                        int64_t n, int k, bool in, int K) {
+  Ws8 r;
+  r.w = in ? *reinterpret_cast<const u32x4*>(W + n * K + k) : u32x4{0u, 0u, 0u, 0u};
+  r.s = in ? *reinterpret_cast<const u32x4*>(smooth + k) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  return r;
+}
+__device__ __forceinline__ float ws8_value(const Ws8& r, int e) {
+  const uint32_t wb = (r.w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+  const uint32_t sb = (r.s[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+  return bf16lo_to_f32(wb) / bf16lo_to_f32(sb);
+}
+
+// Y[n, r] = sum_k Ws[n, k] B[k, r] (B [K, R] fp32): 64 rows per workgroup.
+// K % 16 == 0, so a thread's 8 k are all inside K or all past it.
 __global__ __launch_bounds__(256) void tsmm_nn_kernel(const uint16_t* __restrict__ W,
                                                       const uint16_t* __restrict__ smooth,
                                                       const float* __restrict__ B, float* __restrict__ Y,
                                                       int N, int K, int R) {
-  __shared__ float As[32][32 + 4];    // [k][row]
-  __shared__ float Bs[32][kRMax];     // [k][r]
+  __shared__ __attribute__((aligned(16))) float As[2][32][64 + 4];   // [stage][k][row]
+  __shared__ __attribute__((aligned(16))) float Bs[2][32][kRMax];    // [stage][k][r]
   const int t = threadIdx.x;
-  const int n0 = blockIdx.x * 32;
-  const int rg = t & 15, cg = t >> 4;
-  float acc[2][8];
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int n0 = blockIdx.x * 64;
+  // loads: A row t / 4, k (t % 4) * 8 .. + 7 of the chunk; B pieces t + 256 u (u < 4): k = piece / 32,
+  // r = 4 (piece % 32)
+  const int ar = t >> 2, ak = (t & 3) * 8;
+  Ws8 av;
+  f32x4_t bv[4];
+  auto load = [&](int k0) {
+    av = ws8_load(W, smooth, n0 + ar, k0 + ak, n0 + ar < N && k0 + ak < K, K);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    {   // A: row t / 8, 4 k from (t % 8) * 4 (K % 16 == 0: all 4 in or all past K)
-      const int row = t >> 3, kk = (t & 7) * 4;
-      const int n = n0 + row, k = k0 + kk;
-      float v[4];
-      if (n < N && k < K) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(W + (size_t)n * K + k);
-        const u32x2 sv = *reinterpret_cast<const u32x2*>(smooth + k);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t wb = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          const uint32_t sb = (sv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          v[e] = bf16lo_to_f32(wb) / bf16lo_to_f32(sb);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = 0.0f;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) As[kk + e][row] = v[e];
+    for (int u = 0; u < 4; ++u) {
+      const int pc = t + 256 * u, kk = pc >> 5, r = 4 * (pc & 31);
+      bv[u] = (k0 + kk < K && r < R) ? *reinterpret_cast<const f32x4_t*>(B + (size_t)(k0 + kk) * R + r)
+                                     : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    for (int idx = t; idx < 32 * R; idx += 256) {
-      const int kk = idx / R, r = idx % R;
-      Bs[kk][r] = (k0 + kk < K) ? B[(size_t)(k0 + kk) * R + r] : 0.0f;
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) As[st][ak + e][ar] = ws8_value(av, e);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = t + 256 * u;
+      *reinterpret_cast<f32x4_t*>(&Bs[st][pc >> 5][4 * (pc & 31)]) = bv[u];
     }
-    __syncthreads();
-    if (8 * cg < R) {
-#pragma unroll 8
-      for (int kk = 0; kk < 32; ++kk) {
-        float a[2], b[8];
+  };
+  f32x16_t acc[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = As[kk][2 * rg + i];
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b[j] = Bs[kk][8 * cg + j];
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
+  const int nk = (K + 31) / 32;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int st = kc & 1;
+    if (kc + 1 < nk) load(32 * (kc + 1));
+    float fa[16], fb0[16], fb1[16];   // the chunk's operands, read before its matrix instructions
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-      }
+    for (int s2 = 0; s2 < 16; ++s2) {
+      fa[s2] = As[st][2 * s2 + h][32 * wm + l32];
+      fb0[s2] = Bs[st][2 * s2 + h][64 * wn + l32];
+      fb1[s2] = Bs[st][2 * s2 + h][64 * wn + 32 + l32];
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s2], fb0[s2], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s2], fb1[s2], acc[1], 0, 0, 0);
+    }
+    if (kc + 1 < nk) store(st ^ 1);
     __syncthreads();
   }
-  if (8 * cg < R) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int n = n0 + 2 * rg + i;
-      if (n < N)
+  for (int c = 0; c < 2; ++c) {
+    const int col = 64 * wn + 32 * c + l32;
+    if (col >= R) continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) Y[(size_t)n * R + 8 * cg + j] = acc[i][j];
+    for (int i = 0; i < 16; ++i) {
+      const int n = n0 + 32 * wm + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (n < N) Y[(size_t)n * R + col] = acc[c][i];
     }
   }
 }
@@ -111,66 +145,76 @@ __global__ __launch_bounds__(256) void tsmm_tn_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ smooth,
                                                       const float* __restrict__ Q, float* __restrict__ Zp,
                                                       int N, int K, int R, int rows_per) {
-  __shared__ float As[32][64 + 4];    // [n][k]
-  __shared__ float Qs[32][kRMax];     // [n][r]
+  __shared__ __attribute__((aligned(16))) float As[2][32][64 + 4];   // [stage][n][k]
+  __shared__ __attribute__((aligned(16))) float Qs[2][32][kRMax];    // [stage][n][r]
   const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;
   const int k0 = blockIdx.x * 64;
-  const int s = blockIdx.y;
-  const int nb = s * rows_per, ne = min(N, nb + rows_per);
-  const int kg = t & 15, cg = t >> 4;
-  float acc[4][8];
+  const int sp = blockIdx.y;
+  const int nb = sp * rows_per, ne = min(N, nb + rows_per);
+  // loads: A row t / 8 of the chunk, k (t % 8) * 8 .. + 7; Q pieces as B above
+  const int ar = t >> 3, ak = (t & 7) * 8;
+  Ws8 av;
+  f32x4_t qv[4];
+  auto load = [&](int n0) {
+    av = ws8_load(W, smooth, n0 + ar, k0 + ak, n0 + ar < ne && k0 + ak < K, K);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
-  for (int n0 = nb; n0 < ne; n0 += 32) {
-    {   // A: row t / 8, 8 k from (t % 8) * 8
-      const int row = t >> 3, kk = (t & 7) * 8;
-      const int n = n0 + row, k = k0 + kk;
-      float v[8];
-      if (n < ne && k < K) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(W + (size_t)n * K + k);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wb = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          const uint16_t sb = smooth[k + e];
-          v[e] = bf16lo_to_f32(wb) / bf16lo_to_f32(sb);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) As[row][kk + e] = v[e];
+    for (int u = 0; u < 4; ++u) {
+      const int pc = t + 256 * u, nn = pc >> 5, r = 4 * (pc & 31);
+      qv[u] = (n0 + nn < ne && r < R) ? *reinterpret_cast<const f32x4_t*>(Q + (size_t)(n0 + nn) * R + r)
+                                      : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    for (int idx = t; idx < 32 * R; idx += 256) {
-      const int nn = idx / R, r = idx % R;
-      Qs[nn][r] = (n0 + nn < ne) ? Q[(size_t)(n0 + nn) * R + r] : 0.0f;
+  };
+  auto store = [&](int st) {
+    *reinterpret_cast<f32x4_t*>(&As[st][ar][ak]) =
+        f32x4_t{ws8_value(av, 0), ws8_value(av, 1), ws8_value(av, 2), ws8_value(av, 3)};
+    *reinterpret_cast<f32x4_t*>(&As[st][ar][ak + 4]) =
+        f32x4_t{ws8_value(av, 4), ws8_value(av, 5), ws8_value(av, 6), ws8_value(av, 7)};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = t + 256 * u;
+      *reinterpret_cast<f32x4_t*>(&Qs[st][pc >> 5][4 * (pc & 31)]) = qv[u];
     }
-    __syncthreads();
-    if (8 * cg < R) {
-#pragma unroll 4
-      for (int nn = 0; nn < 32; ++nn) {
-        float a[4], b[8];
+  };
+  f32x16_t acc[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = As[nn][4 * kg + i];
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b[j] = Qs[nn][8 * cg + j];
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
+  const int nc = (ne - nb + 31) / 32;
+  if (nc > 0) {
+    load(nb);
+    store(0);
+  }
+  __syncthreads();
+  for (int ic = 0; ic < nc; ++ic) {
+    const int st = ic & 1;
+    if (ic + 1 < nc) load(nb + 32 * (ic + 1));
+    float fa[16], fb0[16], fb1[16];   // the chunk's operands, read before its matrix instructions
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-      }
+    for (int s2 = 0; s2 < 16; ++s2) {
+      fa[s2] = As[st][2 * s2 + h][32 * wm + l32];
+      fb0[s2] = Qs[st][2 * s2 + h][64 * wn + l32];
+      fb1[s2] = Qs[st][2 * s2 + h][64 * wn + 32 + l32];
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s2], fb0[s2], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s2], fb1[s2], acc[1], 0, 0, 0);
+    }
+    if (ic + 1 < nc) store(st ^ 1);
     __syncthreads();
   }
-  if (8 * cg < R) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + 4 * kg + i;
-      if (k < K)
+  for (int c = 0; c < 2; ++c) {
+    const int col = 64 * wn + 32 * c + l32;
+    if (col >= R) continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) Zp[((size_t)s * K + k) * R + 8 * cg + j] = acc[i][j];
+    for (int i = 0; i < 16; ++i) {
+      const int k = k0 + 32 * wm + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (k < K) Zp[((size_t)sp * K + k) * R + col] = acc[c][i];
     }
   }
 }
@@ -527,7 +571,7 @@ hipError_t launch_prepare_lowrank(const uint16_t* W, const uint16_t* smooth, con
   float* z2 = reinterpret_cast<float*>(ws + w.z2);
   float* zp = reinterpret_cast<float*>(ws + w.zp);
   const int n = (int)N, k = (int)K, r = (int)R;
-  const dim3 g_nn((n + 31) / 32), g_tn((k + 63) / 64, w.splits);
+  const dim3 g_nn((n + 63) / 64), g_tn((k + 63) / 64, w.splits);
   const int64_t kr = (int64_t)K * R;
   auto tn = [&](const float* qq, float* out) {
     hipLaunchKernelGGL(tsmm_tn_kernel, g_tn, dim3(256), 0, s, W, smooth, qq, zp, n, k, r, w.rows_per);
