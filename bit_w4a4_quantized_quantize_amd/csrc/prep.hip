@@ -430,11 +430,17 @@ __device__ __forceinline__ void residual_col(const uint16_t* __restrict__ W, con
                                              int k, double (&E)[NR]) {
 #pragma unroll
   for (int i = 0; i < NR; ++i) E[i] = i < nrows ? (double)bf16lo_to_f32(W[(size_t)(n0 + i) * K + k]) : 0.0;
-  const uint16_t* p = pd + (size_t)k * R;
-  for (int r = 0; r < R; ++r) {
-    const double d = (double)bf16lo_to_f32(p[r]);
+  // this column's proj_down row, 8 values per 16-byte load (R % 16 == 0)
+  const u32x4* p = reinterpret_cast<const u32x4*>(pd + (size_t)k * R);
+  for (int r8 = 0; r8 < R / 8; ++r8) {
+    const u32x4 v = p[r8];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) E[i] = fma(-pus[i * kRMax + r], d, E[i]);
+    for (int e = 0; e < 8; ++e) {
+      const int r = 8 * r8 + e;
+      const double d = (double)bf16lo_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) E[i] = fma(-pus[i * kRMax + r], d, E[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i) E[i] = E[i] / sm;
