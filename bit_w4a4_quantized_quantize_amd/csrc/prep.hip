@@ -282,21 +282,32 @@ __global__ void gram_sum_kernel(const double* __restrict__ Gp, double* __restric
   G[i] = v;
 }
 
-// One workgroup: right-looking Cholesky of G in LDS (a pivot that is not
-// positive makes its column zero), then X = L^-1 right-looking (row j of X is
-// divided by L[j][j], then X[i][:] -= L[i][j] X[j][:] for i > j). One barrier
-// per step: step j updates with the still unscaled column (row) j times
-// 1/pivot, and column (row) j itself is scaled during step j+1, which does not
-// touch it otherwise. X is lower triangular like L: its off-diagonal entry
-// (i, c) is kept at the mirrored slot (c, i) of the same R x R array, its
-// diagonal aside. Output T = L^-T = X^T (fp32, upper triangular). 1024 threads
-// as 32 x 32 (ty, tx). Dynamic LDS: R*(R+1) + 2R doubles.
-__global__ __launch_bounds__(1024) void chol_inv_kernel(const double* __restrict__ G, int R, float* __restrict__ T) {
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Cholesky QR's factorisation, in two kernels. G = L L^T right-looking in one
+// workgroup (a pivot that is not positive makes its column zero), one barrier per
+// step: step j updates with the still unscaled column j times 1/pivot, and column j
+// itself is scaled during step j+1, which does not touch it otherwise. Then
+// X = L^-1, one column per wave: column c of X is the forward substitution of e_c,
+// right-looking (row j of X is divided by L[j][j], then X[i][c] -= L[i][j] X[j][c]
+// for i > j), so each element sees the same operations in the same order as in a
+// right-looking inversion of the whole matrix. Output T = L^-T = X^T (fp32, upper
+// triangular).
+
+// 1024 threads as 32 x 32 (ty, tx). Lout [R, R] (lower triangle and diagonal; the
+// upper triangle is not written), ld_out [R] = the diagonal. Dynamic LDS:
+// R*(R+1) + R doubles.
+__global__ __launch_bounds__(1024) void chol_kernel(const double* G, int R, double* Lout,   // Lout may be G
+                                                   double* __restrict__ ld_out) {
   extern __shared__ double lds_d[];
   const int S_ = R + 1;   // padded row stride: column walks hit distinct banks
   double* L = lds_d;
-  double* xd = lds_d + R * S_;  // diagonal of X
-  double* ld = xd + R;          // diagonal of L
+  double* ld = lds_d + R * S_;  // diagonal of L
   const int t = threadIdx.x;
   const int tx = t & 31, ty = t >> 5;
   for (int idx = t; idx < R * R; idx += 1024) L[(idx / R) * S_ + idx % R] = G[idx];
@@ -320,35 +331,54 @@ __global__ __launch_bounds__(1024) void chol_inv_kernel(const double* __restrict
     __syncthreads();
   }
   __syncthreads();
-  // X = I: clear the upper triangle (X's off-diagonal slots), diagonal 1
-  for (int a = ty; a < R; a += 32)
-    for (int b = a + 1 + tx; b < R; b += 32) L[a * S_ + b] = 0.0;
-  for (int i = t; i < R; i += 1024) xd[i] = 1.0;
-  __syncthreads();
-  for (int j = 0; j <= R; ++j) {
-    if (j > 0) {   // scale row j-1 of X: (j-1, c) at slot (c, j-1), c < j-1; diagonal xd[j-1]
-      const double lp = ld[j - 1];
-      for (int c = t; c < j; c += 1024) {
-        if (c < j - 1) L[c * S_ + j - 1] = lp > 0.0 ? L[c * S_ + j - 1] / lp : 0.0;
-        else xd[j - 1] = lp > 0.0 ? xd[j - 1] / lp : 0.0;
-      }
-    }
-    if (j == R) break;
-    const double lj = ld[j];
-    const double inv_l = lj > 0.0 ? 1.0 / lj : 0.0;
-    for (int i = j + 1 + ty; i < R; i += 32) {
-      const double lij = L[i * S_ + j] * inv_l;
-      for (int c = tx; c <= j; c += 32) {
-        const double xjc = c < j ? L[c * S_ + j] : xd[j];   // row j of X, not yet scaled
-        L[c * S_ + i] -= lij * xjc;   // X(i, c) at slot (c, i); c <= j < i
-      }
-    }
-    __syncthreads();
+  // L (scaled, diagonal = roots of the pivots) and its diagonal out
+  for (int idx = t; idx < R * R; idx += 1024) {
+    const int i = idx / R, j = idx % R;
+    if (j < i) Lout[idx] = L[i * S_ + j];
+    else if (j == i) Lout[idx] = ld[i];
+  }
+  for (int i = t; i < R; i += 1024) ld_out[i] = ld[i];
+}
+
+// T[c, :] = column c of X = L^-1, divided row by row by L[i][i]; wave w of workgroup
+// b takes c = 4 b + w. Lane l holds rows l and l + 64 of the column; the pivot row's
+// value comes from its lane. Dynamic LDS: R*(R+1) + R doubles (L, 1 / L[j][j]).
+__global__ __launch_bounds__(256) void inv_kernel(const double* __restrict__ Lg, const double* __restrict__ ldg,
+                                                  int R, float* __restrict__ T) {
+  extern __shared__ double lds_d[];
+  const int S_ = R + 1;
+  double* L = lds_d;
+  double* il = lds_d + R * S_;
+  const int t = threadIdx.x;
+  for (int idx = t; idx < R * R; idx += 256) {
+    const int i = idx / R, j = idx % R;
+    if (j < i) L[i * S_ + j] = Lg[idx];
+  }
+  for (int j = t; j < R; j += 256) {
+    const double lj = ldg[j];
+    il[j] = lj > 0.0 ? 1.0 / lj : 0.0;
   }
   __syncthreads();
-  for (int idx = t; idx < R * R; idx += 1024) {
-    const int a = idx / R, b = idx % R;
-    T[idx] = b > a ? (float)L[a * S_ + b] : (b == a ? (float)xd[a] : 0.0f);
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int c = 4 * (int)blockIdx.x + wave;
+  if (c >= R) return;
+  const int r0 = lane, r1 = lane + 64;
+  double x0 = r0 == c ? 1.0 : 0.0, x1 = r1 == c ? 1.0 : 0.0;   // X(r, c), rows not yet divided
+  for (int j = c; j < R - 1; ++j) {
+    const double xj = readlane_f64(j < 64 ? x0 : x1, j & 63);
+    const double inv_l = il[j];
+    const double l0 = L[min(r0, R - 1) * S_ + j] * inv_l, l1 = L[min(r1, R - 1) * S_ + j] * inv_l;
+    const double u0 = x0 - l0 * xj, u1 = x1 - l1 * xj;
+    x0 = r0 > j && r0 < R ? u0 : x0;
+    x1 = r1 > j && r1 < R ? u1 : x1;
+  }
+  if (r0 < R) {
+    const double l = ldg[r0];
+    T[c * R + r0] = r0 >= c ? (float)(l > 0.0 ? x0 / l : 0.0) : 0.0f;
+  }
+  if (r1 < R) {
+    const double l = ldg[r1];
+    T[c * R + r1] = r1 >= c ? (float)(l > 0.0 ? x1 / l : 0.0) : 0.0f;
   }
 }
 
@@ -505,7 +535,7 @@ __global__ void fill_u16_kernel(uint16_t* __restrict__ p, uint16_t v, int64_t n)
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct PrepWs {
-  size_t wp, ones, y, q, z, z2, zp, gp, g, tm, total;
+  size_t wp, ones, y, q, z, z2, zp, gp, g, ldv, tm, total;
   int splits, rows_per;
 };
 
@@ -531,6 +561,7 @@ PrepWs prep_ws(int64_t N, int64_t K, int64_t R) {
     w.zp = o; o = al(o + (size_t)S * K * R * 4);
     w.gp = o; o = al(o + (size_t)((big + kGramRows - 1) / kGramRows) * R * R * 8);
     w.g = o; o = al(o + (size_t)R * R * 8);
+    w.ldv = o; o = al(o + (size_t)R * 8);
     w.tm = o; o = al(o + (size_t)R * R * 4);
   }
   w.total = o;
@@ -545,13 +576,16 @@ size_t prep_workspace_bytes(int64_t N, int64_t K, int64_t R) { return prep_ws(N,
 static hipError_t orth(float* a, float* b, int rows, int R, const PrepWs& w, uint8_t* ws, hipStream_t s) {
   double* gp = reinterpret_cast<double*>(ws + w.gp);
   double* g = reinterpret_cast<double*>(ws + w.g);
+  double* ldv = reinterpret_cast<double*>(ws + w.ldv);
   float* tm = reinterpret_cast<float*>(ws + w.tm);
   const int chunks = (rows + kGramRows - 1) / kGramRows;
-  const int lds_chol = (R * (R + 1) + 2 * R) * 8;
+  const int lds_chol = (R * (R + 1) + R) * 8;   // chol_kernel and inv_kernel alike
   const int lds_mul = (R * R + 64 * (R + 4)) * 4;
-  static std::atomic<uint64_t> chol_set{0}, mul_set{0};
-  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&chol_inv_kernel), (kRMax * (kRMax + 1) + 2 * kRMax) * 8,
+  static std::atomic<uint64_t> chol_set{0}, inv_set{0}, mul_set{0};
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&chol_kernel), (kRMax * (kRMax + 1) + kRMax) * 8,
                                     chol_set);
+  if (e != hipSuccess) return e;
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&inv_kernel), (kRMax * (kRMax + 1) + kRMax) * 8, inv_set);
   if (e != hipSuccess) return e;
   e = set_lds_limit_once(reinterpret_cast<const void*>(&right_mul_kernel), (kRMax * kRMax + 64 * (kRMax + 4)) * 4,
                          mul_set);
@@ -561,7 +595,8 @@ static hipError_t orth(float* a, float* b, int rows, int R, const PrepWs& w, uin
     float* out = pass == 0 ? b : a;
     hipLaunchKernelGGL(gram_kernel, dim3(chunks), dim3(256), 0, s, in, gp, rows, R);
     hipLaunchKernelGGL(gram_sum_kernel, dim3((R * R + 255) / 256), dim3(256), 0, s, gp, g, chunks, R * R);
-    hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(1024), lds_chol, s, g, R, tm);
+    hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(1024), lds_chol, s, g, R, g, ldv);   // L over G
+    hipLaunchKernelGGL(inv_kernel, dim3((R + 3) / 4), dim3(256), lds_chol, s, g, ldv, R, tm);
     hipLaunchKernelGGL(right_mul_kernel, dim3((rows + 63) / 64), dim3(256), lds_mul, s, in, tm, out, rows, R);
   }
   return hipGetLastError();
