@@ -54,7 +54,8 @@ def test_residual_stage_bit_exact(gpu_lib, N, K, R):
     check_residual(gpu_lib, W, sm, pu, pd)
 
 
-@pytest.mark.parametrize("N,K,R,iters,strong", [(512, 384, 32, 2, 8), (640, 768, 64, 1, 0), (257, 160, 16, 0, 4)])
+@pytest.mark.parametrize("N,K,R,iters,strong", [(512, 384, 32, 2, 8), (640, 768, 64, 1, 0), (257, 160, 16, 0, 4),
+                                                  (400, 256, 96, 1, 6)])   # R above 64, not a power of two
 def test_randomized_split_matches_oracle(gpu_lib, N, K, R, iters, strong):
     W, sm, _ = workloads.make_prep_weight(N, K, seed=3 * N + K, strong=strong)
     omega = workloads.make_omega(K, R, seed=R + iters)
