@@ -64,30 +64,34 @@ __device__ __forceinline__ float ws8_value(const Ws8& r, int e) {
   return bf16lo_to_f32(wb) / bf16lo_to_f32(sb);
 }
 
-// Y[n, r] = sum_k Ws[n, k] B[k, r] (B [K, R] fp32): 64 rows per workgroup.
-// K % 16 == 0, so a thread's 8 k are all inside K or all past it.
+// Y[n, r] = sum_k Ws[n, k] B[k, r] (B [K, R] fp32): 64 rows per workgroup; the
+// reduction may be split (blockIdx.y = split s over k in [s kper, (s+1) kper), kper a
+// multiple of 32, partial sums to Y + s N R, added in split order by sum_splits_kernel).
+// K % 16 == 0, so a thread's 8 k are all inside the range or all past it.
 __global__ __launch_bounds__(256) void tsmm_nn_kernel(const uint16_t* __restrict__ W,
                                                       const uint16_t* __restrict__ smooth,
                                                       const float* __restrict__ B, float* __restrict__ Y,
-                                                      int N, int K, int R) {
+                                                      int N, int K, int R, int kper) {
   __shared__ __attribute__((aligned(16))) float As[2][32][64 + 4];   // [stage][k][row]
   __shared__ __attribute__((aligned(16))) float Bs[2][32][kRMax];    // [stage][k][r]
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int wm = wave & 1, wn = wave >> 1;
   const int n0 = blockIdx.x * 64;
+  const int kb = (int)blockIdx.y * kper, ke = min(K, kb + kper);
+  Y += (size_t)blockIdx.y * N * R;
   // loads: A row t / 4, k (t % 4) * 8 .. + 7 of the chunk; B pieces t + 256 u (u < 4): k = piece / 32,
   // r = 4 (piece % 32)
   const int ar = t >> 2, ak = (t & 3) * 8;
   Ws8 av;
   f32x4_t bv[4];
   auto load = [&](int k0) {
-    av = ws8_load(W, smooth, n0 + ar, k0 + ak, n0 + ar < N && k0 + ak < K, K);
+    av = ws8_load(W, smooth, n0 + ar, k0 + ak, n0 + ar < N && k0 + ak < ke, K);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int pc = t + 256 * u, kk = pc >> 5, r = 4 * (pc & 31);
-      bv[u] = (k0 + kk < K && r < R) ? *reinterpret_cast<const f32x4_t*>(B + (size_t)(k0 + kk) * R + r)
-                                     : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      bv[u] = (k0 + kk < ke && r < R) ? *reinterpret_cast<const f32x4_t*>(B + (size_t)(k0 + kk) * R + r)
+                                      : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
   auto store = [&](int st) {
@@ -104,13 +108,15 @@ __global__ __launch_bounds__(256) void tsmm_nn_kernel(const uint16_t* __restrict
   for (int c = 0; c < 2; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
-  const int nk = (K + 31) / 32;
-  load(0);
-  store(0);
+  const int nk = (ke - kb + 31) / 32;
+  if (nk > 0) {
+    load(kb);
+    store(0);
+  }
   __syncthreads();
   for (int kc = 0; kc < nk; ++kc) {
     const int st = kc & 1;
-    if (kc + 1 < nk) load(32 * (kc + 1));
+    if (kc + 1 < nk) load(kb + 32 * (kc + 1));
     float fa[16], fb0[16], fb1[16];   // the chunk's operands, read before its matrix instructions
 #pragma unroll
     for (int s2 = 0; s2 < 16; ++s2) {
@@ -536,7 +542,8 @@ size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct PrepWs {
   size_t wp, ones, y, q, z, z2, zp, gp, g, ldv, tm, total;
-  int splits, rows_per;
+  int splits, rows_per;   // Ws^T Q: row splits
+  int nn_splits, nn_kper;   // Ws B: reduction splits
 };
 
 PrepWs prep_ws(int64_t N, int64_t K, int64_t R) {
@@ -546,19 +553,29 @@ PrepWs prep_ws(int64_t N, int64_t K, int64_t R) {
   w.ones = o; o = al(o + (size_t)K * 2);
   if (R > 0) {
     const int64_t kb = (K + 63) / 64;
-    int S = (int)((256 + kb - 1) / kb);
+    int S = (int)(512 / kb);   // about two workgroups per CU
     S = S < 1 ? 1 : (S > 16 ? 16 : S);
     int64_t rp = (N + S - 1) / S;
     rp = (rp + 31) / 32 * 32;
     S = (int)((N + rp - 1) / rp);
     w.splits = S;
     w.rows_per = (int)rp;
+    // Ws B: 64-row workgroups, the reduction split so that about two workgroups run per CU
+    const int64_t nb = (N + 63) / 64;
+    const int64_t nk32 = (K + 31) / 32;
+    int64_t Sn = 512 / nb;
+    Sn = Sn < 1 ? 1 : (Sn > 16 ? 16 : Sn);
+    Sn = Sn > nk32 ? nk32 : Sn;
+    const int64_t kper = (nk32 + Sn - 1) / Sn * 32;
+    w.nn_kper = (int)kper;
+    w.nn_splits = (int)((K + kper - 1) / kper);
     const int64_t big = N > K ? N : K;
     w.y = o; o = al(o + (size_t)N * R * 4);
     w.q = o; o = al(o + (size_t)N * R * 4);
     w.z = o; o = al(o + (size_t)K * R * 4);
     w.z2 = o; o = al(o + (size_t)K * R * 4);
-    w.zp = o; o = al(o + (size_t)S * K * R * 4);
+    const size_t zp_tn = (size_t)S * K * R * 4, zp_nn = w.nn_splits > 1 ? (size_t)w.nn_splits * N * R * 4 : 0;
+    w.zp = o; o = al(o + (zp_tn > zp_nn ? zp_tn : zp_nn));
     w.gp = o; o = al(o + (size_t)((big + kGramRows - 1) / kGramRows) * R * R * 8);
     w.g = o; o = al(o + (size_t)R * R * 8);
     w.ldv = o; o = al(o + (size_t)R * 8);
@@ -612,7 +629,16 @@ hipError_t launch_prepare_lowrank(const uint16_t* W, const uint16_t* smooth, con
   float* z2 = reinterpret_cast<float*>(ws + w.z2);
   float* zp = reinterpret_cast<float*>(ws + w.zp);
   const int n = (int)N, k = (int)K, r = (int)R;
-  const dim3 g_nn((n + 63) / 64), g_tn((k + 63) / 64, w.splits);
+  const dim3 g_nn((n + 63) / 64, w.nn_splits), g_tn((k + 63) / 64, w.splits);
+  const int64_t nr = (int64_t)N * R;
+  // y = Ws b, through the split partial sums when the reduction is split
+  auto nn = [&](const float* b) {
+    float* dst = w.nn_splits > 1 ? zp : y;
+    hipLaunchKernelGGL(tsmm_nn_kernel, g_nn, dim3(256), 0, s, W, smooth, b, dst, n, k, r, w.nn_kper);
+    if (w.nn_splits > 1)
+      hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, s, zp, y, nr,
+                         w.nn_splits);
+  };
   const int64_t kr = (int64_t)K * R;
   auto tn = [&](const float* qq, float* out) {
     hipLaunchKernelGGL(tsmm_tn_kernel, g_tn, dim3(256), 0, s, W, smooth, qq, zp, n, k, r, w.rows_per);
@@ -620,12 +646,12 @@ hipError_t launch_prepare_lowrank(const uint16_t* W, const uint16_t* smooth, con
                        w.splits);
   };
   hipError_t e;
-  hipLaunchKernelGGL(tsmm_nn_kernel, g_nn, dim3(256), 0, s, W, smooth, omega, y, n, k, r);
+  nn(omega);
   for (int it = 0; it < iters; ++it) {
     if ((e = orth(y, q, n, r, w, ws, s)) != hipSuccess) return e;
     tn(y, z);
     if ((e = orth(z, z2, k, r, w, ws, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(tsmm_nn_kernel, g_nn, dim3(256), 0, s, W, smooth, z, y, n, k, r);
+    nn(z);
   }
   if ((e = orth(y, q, n, r, w, ws, s)) != hipSuccess) return e;
   tn(y, z);
