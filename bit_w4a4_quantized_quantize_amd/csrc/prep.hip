@@ -240,43 +240,48 @@ __global__ void sum_splits_kernel(const float* __restrict__ Zp, float* __restric
 
 constexpr int kGramRows = 128;
 
-// Gp[c] = Y[rows of chunk c]^T Y[rows of chunk c], fp64, thread (bi, bj) owns the
-// 8 x 8 block (8bi.., 8bj..).
+// Gp[c] = Y[rows of chunk c]^T Y[rows of chunk c], fp64; each chunk is split over
+// four workgroups by quadrant of G (R % 8 == 0), so that the chip has work for
+// 4 x (rows / 128) workgroups.
 __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ Y, double* __restrict__ Gp,
                                                    int rows, int R) {
+  // workgroup (chunk, quadrant): quadrant q of G, rows (q / 2) R/2 .., columns (q % 2) R/2 ..;
+  // thread (bi, bj) of 16 x 16 owns its 4 x 4 elements (4 bi.., 4 bj.. within the quadrant)
   __shared__ float Ys[kGramRows][kRMax];
   const int t = threadIdx.x;
   const int r0 = blockIdx.x * kGramRows;
   const int nr = min(kGramRows, rows - r0);
+  const int half = R / 2;
+  const int q = blockIdx.y, gi0 = (q >> 1) * half, gj0 = (q & 1) * half;
   for (int idx = t; idx < kGramRows * R; idx += 256) {
     const int rr = idx / R, c = idx % R;
     Ys[rr][c] = rr < nr ? Y[(size_t)(r0 + rr) * R + c] : 0.0f;
   }
   __syncthreads();
-  const int nb = R / 8;
-  const int bi = t / 16, bj = t % 16;
-  if (bi >= nb || bj >= nb) return;
-  double acc[8][8];
+  const int bi = t >> 4, bj = t & 15;
+  if (4 * bi >= half || 4 * bj >= half) return;
+  const int i0 = gi0 + 4 * bi, j0 = gj0 + 4 * bj;
+  double acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
-  for (int rr = 0; rr < nr; ++rr) {
-    double a[8], b[8];
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int rr = 0; rr < nr; ++rr) {   // the chunk's rows in order, as a whole-G loop would take them
+    double a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = (double)Ys[rr][8 * bi + i];
+    for (int i = 0; i < 4; ++i) a[i] = (double)Ys[rr][i0 + i];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = (double)Ys[rr][8 * bj + j];
+    for (int j = 0; j < 4; ++j) b[j] = (double)Ys[rr][j0 + j];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
   }
   double* g = Gp + (size_t)blockIdx.x * R * R;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) g[(8 * bi + i) * R + 8 * bj + j] = acc[i][j];
+    for (int j = 0; j < 4; ++j) g[(i0 + i) * R + j0 + j] = acc[i][j];
 }
 
 // G = sum of the chunk Grams, chunks added in order (one thread per entry).
@@ -388,45 +393,76 @@ __global__ __launch_bounds__(256) void inv_kernel(const double* __restrict__ Lg,
   }
 }
 
-// Dynamic LDS: R*R + 64*(R+4) floats.
+// O[n, r] = sum_k A[n, k] T[k, r] (A [rows, R], T [R, R], fp32) on the fp32 matrix
+// instruction, with the tiles and two-stage chunks of tsmm_nn_kernel.
 __global__ __launch_bounds__(256) void right_mul_kernel(const float* __restrict__ A, const float* __restrict__ T,
                                                         float* __restrict__ O, int rows, int R) {
-  extern __shared__ float lds_f[];
-  float* Ts = lds_f;
-  float* As = lds_f + R * R;   // [64][R + 4]
-  const int ld = R + 4;
+  __shared__ __attribute__((aligned(16))) float As[2][32][64 + 4];   // [stage][k][row]
+  __shared__ __attribute__((aligned(16))) float Bs[2][32][kRMax];    // [stage][k][r]
   const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;
   const int n0 = blockIdx.x * 64;
-  for (int idx = t; idx < R * R; idx += 256) Ts[idx] = T[idx];
-  for (int idx = t; idx < 64 * R; idx += 256) {
-    const int rr = idx / R, c = idx % R;
-    As[rr * ld + c] = (n0 + rr < rows) ? A[(size_t)(n0 + rr) * R + c] : 0.0f;
-  }
-  __syncthreads();
-  const int rg = t & 15, cg = t >> 4;
-  if (8 * cg >= R) return;
-  float acc[4][8];
+  const int ar = t >> 2, ak = (t & 3) * 8;   // A row t / 4, k (t % 4) * 8 .. + 7 of the chunk
+  f32x4_t av[2], bv[4];
+  auto load = [&](int k0) {
+    const bool in = n0 + ar < rows && k0 + ak < R;   // R % 16 == 0: all 8 in or all out
+    const float* src = A + (size_t)(in ? n0 + ar : 0) * R + (in ? k0 + ak : 0);
+    av[0] = in ? *reinterpret_cast<const f32x4_t*>(src) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    av[1] = in ? *reinterpret_cast<const f32x4_t*>(src + 4) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
-  for (int k = 0; k < R; ++k) {
-    float b[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = Ts[k * R + 8 * cg + j];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = As[(4 * rg + i) * ld + k];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a, b[j], acc[i][j]);
+    for (int u = 0; u < 4; ++u) {
+      const int pc = t + 256 * u, kk = pc >> 5, r = 4 * (pc & 31);
+      bv[u] = (k0 + kk < R && r < R) ? *reinterpret_cast<const f32x4_t*>(T + (size_t)(k0 + kk) * R + r)
+                                     : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) As[st][ak + e][ar] = av[e >> 2][e & 3];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = t + 256 * u;
+      *reinterpret_cast<f32x4_t*>(&Bs[st][pc >> 5][4 * (pc & 31)]) = bv[u];
+    }
+  };
+  f32x16_t acc[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
+  const int nk = (R + 31) / 32;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int st = kc & 1;
+    if (kc + 1 < nk) load(32 * (kc + 1));
+    float fa[16], fb0[16], fb1[16];
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      fa[s2] = As[st][2 * s2 + h][32 * wm + l32];
+      fb0[s2] = Bs[st][2 * s2 + h][64 * wn + l32];
+      fb1[s2] = Bs[st][2 * s2 + h][64 * wn + 32 + l32];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s2], fb0[s2], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s2], fb1[s2], acc[1], 0, 0, 0);
+    }
+    if (kc + 1 < nk) store(st ^ 1);
+    __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + 4 * rg + i;
-    if (n < rows)
+  for (int c = 0; c < 2; ++c) {
+    const int col = 64 * wn + 32 * c + l32;
+    if (col >= R) continue;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) O[(size_t)n * R + 8 * cg + j] = acc[i][j];
+    for (int i = 0; i < 16; ++i) {
+      const int n = n0 + 32 * wm + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (n < rows) O[(size_t)n * R + col] = acc[c][i];
+    }
   }
 }
 
@@ -597,24 +633,20 @@ static hipError_t orth(float* a, float* b, int rows, int R, const PrepWs& w, uin
   float* tm = reinterpret_cast<float*>(ws + w.tm);
   const int chunks = (rows + kGramRows - 1) / kGramRows;
   const int lds_chol = (R * (R + 1) + R) * 8;   // chol_kernel and inv_kernel alike
-  const int lds_mul = (R * R + 64 * (R + 4)) * 4;
-  static std::atomic<uint64_t> chol_set{0}, inv_set{0}, mul_set{0};
+  static std::atomic<uint64_t> chol_set{0}, inv_set{0};
   hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&chol_kernel), (kRMax * (kRMax + 1) + kRMax) * 8,
                                     chol_set);
   if (e != hipSuccess) return e;
   e = set_lds_limit_once(reinterpret_cast<const void*>(&inv_kernel), (kRMax * (kRMax + 1) + kRMax) * 8, inv_set);
   if (e != hipSuccess) return e;
-  e = set_lds_limit_once(reinterpret_cast<const void*>(&right_mul_kernel), (kRMax * kRMax + 64 * (kRMax + 4)) * 4,
-                         mul_set);
-  if (e != hipSuccess) return e;
   for (int pass = 0; pass < 2; ++pass) {
     float* in = pass == 0 ? a : b;
     float* out = pass == 0 ? b : a;
-    hipLaunchKernelGGL(gram_kernel, dim3(chunks), dim3(256), 0, s, in, gp, rows, R);
+    hipLaunchKernelGGL(gram_kernel, dim3(chunks, 4), dim3(256), 0, s, in, gp, rows, R);
     hipLaunchKernelGGL(gram_sum_kernel, dim3((R * R + 255) / 256), dim3(256), 0, s, gp, g, chunks, R * R);
     hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(1024), lds_chol, s, g, R, g, ldv);   // L over G
     hipLaunchKernelGGL(inv_kernel, dim3((R + 3) / 4), dim3(256), lds_chol, s, g, ldv, R, tm);
-    hipLaunchKernelGGL(right_mul_kernel, dim3((rows + 63) / 64), dim3(256), lds_mul, s, in, tm, out, rows, R);
+    hipLaunchKernelGGL(right_mul_kernel, dim3((rows + 63) / 64), dim3(256), 0, s, in, tm, out, rows, R);
   }
   return hipGetLastError();
 }
