@@ -110,6 +110,15 @@ def test_variant_layer_full_size_sampled(gpu_lib):
     assert dist < 0.2
 
 
+def test_variant_layer_wide_tile_ragged_sampled(gpu_lib):
+    # M = 4000, N = 4200: 208 tiles of 256 x 320 (one round on 256 CUs) against 272 of
+    # 256 x 256, so the launcher takes the 320-wide tile; both edges are ragged
+    # (4000 = 15 x 256 + 160 rows, 4200 = 13 x 320 + 40 columns)
+    rows = np.array([0, 255, 256, 3839, 3840, 3999])
+    dist = check_layer(gpu_lib, dict(M=4000, K=256, N=4200, R=32, kind="dit", seed=8), with_bias=True, rows=rows)
+    assert dist < 0.2
+
+
 def _lora_within_bound(got_bits, x_bits, pd_bits, K):
     got = F.bf16_to_f64(got_bits)
     ref = S.lowrank_down(x_bits, pd_bits)
