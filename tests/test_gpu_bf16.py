@@ -87,6 +87,18 @@ def test_bf16_linear_2048px_sampled(gpu_lib):
     check_rows(d, y_bits, rows)
 
 
+def test_bf16_linear_wide_tile_ragged_sampled(gpu_lib):
+    """M = 4000, N = 4200, K = 336: 224 tiles of 256 x 320 (one round on 256 CUs) against
+    272 of 256 x 256, so the launcher takes the 320-wide tile with its plain loop; both
+    edges are ragged (160 rows, 40 columns past the last full tile) and the last K
+    panel is zero-filled past K."""
+    M, K, N = 4000, 336, 4200
+    d = workloads.make_bf16_linear(M, K, N, kind="dit", seed=4242)
+    y_bits = run(gpu_lib, d)
+    rows = np.array([0, 255, 256, 3839, 3840, 3998, 3999])
+    check_rows(d, y_bits, rows)
+
+
 def test_bf16_linear_into_given_output_is_deterministic(gpu_lib):
     d = workloads.make_bf16_linear(256, 512, 384, kind="dit", seed=3)
     x, w, b = dev_bf16(d["x"]), dev_bf16(d["W"]), dev_bf16(d["bias"])
