@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libsvdq.so")
 
 SOURCES = ["api.hip", "quant_act.hip", "quant_lora.hip", "gemm_w4a4.hip", "gemm_lds.hip", "gemm_bf16.hip",
-           "repack.hip", "prep.hip", "gemm_mx.hip", "calib.hip"]
+           "repack.hip", "prep.hip", "gemm_mx.hip", "calib.hip", "gemm_bf16_blaslt.hip"]
 HEADERS = ["common.h", "kernels.h"]
 
 
@@ -61,7 +61,8 @@ def build(verbose=False):
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-L/opt/rocm/lib", "-lhipblaslt",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

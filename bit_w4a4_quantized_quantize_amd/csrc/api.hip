@@ -748,6 +748,19 @@ int svdq_linear_w4a4_gated(const void* x, const void* smooth, const void* weight
   return ok();
 }
 
+// Which product runs a bf16 linear. SVDQ_BF16_GEMM=hip or =blaslt forces one
+// (read on every call); otherwise hipBLASLt takes the large products whose
+// 256 x 320 tile grid leaves a partial last round on 256 CUs (M = 4096: qkv,
+// out and w2 of the 1024^2 DiT), where the hand-written kernel measured slower,
+// and the hand-written kernel keeps the rest (w1/w3 fill two whole rounds).
+static bool use_blaslt_bf16(int64_t M, int64_t N, int64_t K) {
+  const char* v = getenv("SVDQ_BF16_GEMM");
+  if (v != nullptr && strcmp(v, "hip") == 0) return false;
+  if (v != nullptr && strcmp(v, "blaslt") == 0) return true;
+  const int64_t tiles320 = ((M + 255) / 256) * ((N + 319) / 320);
+  return (double)M * (double)N * (double)K >= 1.6e10 && tiles320 % 256 != 0;
+}
+
 int svdq_linear_bf16(const void* x, const void* weight, const void* bias, int64_t M, int64_t N,
                      int64_t K, void* y, void* stream) {
   int st = check_mk(M, K, 0);
@@ -775,7 +788,10 @@ int svdq_linear_bf16(const void* x, const void* weight, const void* bias, int64_
   a.M = M;
   a.N = N;
   a.K = K;
-  hipError_t e = svdq::launch_gemm_bf16(a, static_cast<hipStream_t>(stream));
+  hipError_t e = hipSuccess;
+  bool done = false;
+  if (use_blaslt_bf16(M, N, K)) e = svdq::blaslt_linear_bf16(a, static_cast<hipStream_t>(stream), &done);
+  if (e == hipSuccess && !done) e = svdq::launch_gemm_bf16(a, static_cast<hipStream_t>(stream));
   if (int st_ = launched(e, "bf16 gemm", static_cast<hipStream_t>(stream))) return st_;
   return ok();
 }

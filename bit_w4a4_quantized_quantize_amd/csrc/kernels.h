@@ -96,6 +96,9 @@ struct Bf16GemmArgs {
 };
 int64_t gemm_bf16_tiles(int64_t M, int64_t N);
 hipError_t launch_gemm_bf16(const Bf16GemmArgs& a, hipStream_t stream);
+// The same product through hipBLASLt (no workspace); *done stays false when no
+// plan exists for the shape (first seen under stream capture) and nothing ran.
+hipError_t blaslt_linear_bf16(const Bf16GemmArgs& a, hipStream_t stream, bool* done);
 
 // Load-time SVDQuant weight preparation: the rank-R split of W / smooth by the
 // randomized range finder (omega [K, R] fp32 from the caller; writes proj_down

@@ -66,10 +66,14 @@ def test_bf16_linear_small(gpu_lib, M, K, N, bias):
     check_rows(d, y_bits, np.arange(M))
 
 
+@pytest.mark.parametrize("backend", ["hip", "blaslt", "auto"])
 @pytest.mark.parametrize("K,N", [(3840, 11520), (3840, 3840), (3840, 10240), (10240, 3840)])
-def test_bf16_linear_dit_shapes_sampled(gpu_lib, K, N):
+def test_bf16_linear_dit_shapes_sampled(gpu_lib, K, N, backend, monkeypatch):
     """The sweep's bf16 layer shapes at M = 4096 (qkv, out, w1/w3, w2): sampled rows
-    from every row block, including tile edges and the last row."""
+    from every row block, including tile edges and the last row; with the
+    hand-written kernel forced, hipBLASLt forced, and the library's own choice."""
+    if backend != "auto":
+        monkeypatch.setenv("SVDQ_BF16_GEMM", backend)
     M = 4096
     d = workloads.make_bf16_linear(M, K, N, kind="dit", seed=5000 + K + N)
     y_bits = run(gpu_lib, d)
@@ -131,3 +135,44 @@ def test_bf16_linear_rounding_bit_exact(gpu_lib):
     ties = np.sum(np.abs(y64 / ulp_bf16(y64) % 1 - 0.5) < 1e-12)
     assert ties > 50, ties
     assert np.array_equal(run(gpu_lib, d), yb)
+
+
+@pytest.mark.parametrize("M,K,N,bias", [(300, 336, 200, True), (257, 64, 321, False), (1, 16, 1, True)])
+def test_bf16_linear_blaslt_small(gpu_lib, M, K, N, bias, monkeypatch):
+    """hipBLASLt forced on ragged shapes, with and without bias: the operand
+    transposition and the bias epilogue give the same checks as the kernel."""
+    monkeypatch.setenv("SVDQ_BF16_GEMM", "blaslt")
+    d = workloads.make_bf16_linear(M, K, N, kind="dit", seed=M * 11 + N, with_bias=bias)
+    y_bits = run(gpu_lib, d)
+    check_rows(d, y_bits, np.arange(M))
+
+
+def test_bf16_linear_blaslt_graph_replays(gpu_lib, monkeypatch):
+    """hipBLASLt's product captured in a graph after an eager call made its plan:
+    every replay (with other eager work between) equals the eager output bit for
+    bit, and a shape first seen under capture falls back to the kernel and is
+    still within the parity checks."""
+    monkeypatch.setenv("SVDQ_BF16_GEMM", "blaslt")
+    d = workloads.make_bf16_linear(300, 256, 200, kind="dit", seed=17)
+    d2 = workloads.make_bf16_linear(96, 128, 72, kind="dit", seed=18)
+    x, w, b = dev_bf16(d["x"]), dev_bf16(d["W"]), dev_bf16(d["bias"])
+    x2, w2, b2 = dev_bf16(d2["x"]), dev_bf16(d2["W"]), dev_bf16(d2["bias"])
+    y = torch.empty((300, 200), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((96, 72), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.linear_bf16(x, w, b, y=y)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gpu_lib.linear_bf16(x, w, b, y=y)
+        gpu_lib.linear_bf16(x2, w2, b2, y=y2)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.zero_()
+        y2.zero_()
+        gpu_lib.linear_bf16(x2, w2, None, y=torch.empty_like(y2))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+        check_rows(d2, host_bits(y2), np.arange(96))
