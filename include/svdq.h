@@ -333,6 +333,12 @@ int svdq_lowrank_down(const void* x, const void* proj_down, int64_t M, int64_t K
  *   checkpoint), bias [N] bf16 or NULL, y [M, N] bf16 (round to nearest even);
  *   y must not overlap any input. Products are exact and accumulate in fp32
  *   on the matrix cores. K: a positive multiple of 16; M, N up to 2^24.
+ *   Backend: the library's own kernel, or hipBLASLt (no workspace) for large
+ *   products (M*N*K >= 1.6e10) whose grid of 256 x 320 output tiles is not a
+ *   whole number of 256-workgroup rounds; a shape first seen while the stream
+ *   is capturing takes the library's kernel. The environment variable
+ *   SVDQ_BF16_GEMM=hip or =blaslt (read on every call) forces one of the two.
+ *   Both meet the same bound: one bf16 rounding of an fp32 accumulation.
  */
 int svdq_linear_bf16(const void* x, const void* weight, const void* bias, int64_t M, int64_t N,
                      int64_t K, void* y, void* stream);
